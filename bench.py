@@ -1,0 +1,231 @@
+"""Throughput of the packed-bitmask apply on one MI355X.
+
+One step = one in-place apply of a packed int32 allow-mask to bf16 logits
+[256, 128256] with vocab_size 128000 and 128 random unique row indices
+(batch 256 x 128k vocab is the shape the logits-processor page benchmarks;
+the vocab/padding and index rules are XGrammar "Bitmask Operations").
+
+Metric: effective HBM bandwidth = algorithmic bytes per step / time per step,
+algorithmic bytes = mask words of the processed rows (R * ceil(V/32) * 4)
++ one write pass over their logits (R * V * 2).
+
+Timing: inputs sit in HBM; the timed region rotates over enough independent
+buffer sets (> 2 x the 256 MB Infinity Cache) that no step finds its data in
+a cache.  The K launches are captured once in a HIP graph and replayed, so
+the host's launch rate does not pace the GPU; HIP events on the launch
+stream bracket the replay.  A warm figure (one buffer set, cache-resident,
+not HBM) is reported beside it.  The CPU baseline is the oracle's plain C
+loop on one host core over repeated passes of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "effective HBM GB/s (% of MI355X peak) for bitmask apply, B=256 V=128000 bf16"
+PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+INFINITY_CACHE = 256 << 20  # bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--variant", default="auto", choices=["auto", "scalar", "vec", "wronly"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work for the oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip the warm, per-variant and ceiling figures")
+    return ap.parse_args()
+
+
+def effective_bytes(rows: int, vocab: int, esize: int, out_of_place: bool = False) -> int:
+    words = (vocab + 31) // 32
+    return rows * words * 4 + rows * vocab * esize * (2 if out_of_place else 1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the apply has no cross-GPU step, and this build runs on a "
+              "single GPU only (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import packed_logit_bitmask_amd as mb
+    from packed_logit_bitmask_amd import workloads
+
+    mb.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = workloads.mixed_bf16()
+    R, V = len(wl.indices), wl.vocab_size
+    eff = effective_bytes(R, V, 2)
+    set_bytes = wl.logits.nbytes + wl.mask.nbytes
+    nsets = max(2, math.ceil(2 * INFINITY_CACHE / set_bytes))
+
+    host_logits = torch.from_numpy(wl.logits.view(np.int16))
+    sets = []
+    for _ in range(nsets):
+        x = host_logits.to(dev).view(torch.bfloat16)
+        m = torch.from_numpy(wl.mask).to(dev)
+        i = torch.from_numpy(wl.indices).to(dev)
+        sets.append((x, m, i))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def timed(variant, steps, warmup, rotate=True):
+        use = sets if rotate else sets[:1]
+
+        def one(k):
+            x, m, i = use[k % len(use)]
+            mb.mi_apply_bitmask_inplace(x, m, V, i, -math.inf, variant=variant)
+
+        with torch.cuda.stream(stream):
+            for k in range(warmup):
+                one(k)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(steps):
+                one(k)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()  # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        del g
+        return ms / steps
+
+    ms_step = timed(args.variant, args.steps, args.warmup, rotate=True)
+    gbps = eff / (ms_step * 1e-3) / 1e9
+
+    extras = {}
+    if not args.no_extras:
+        warm = timed(args.variant, args.steps, 10, rotate=False)
+        extras["warm_cache_resident"] = {
+            "note": "one buffer set reused every step: logits and mask stay in the 256 MB Infinity Cache; "
+                    "not an HBM figure",
+            "ms_per_step": warm, "GBps": eff / (warm * 1e-3) / 1e9}
+        per = {}
+        for var in ("scalar", "vec", "wronly"):
+            t = timed(var, args.steps, 10, rotate=True)
+            per[var] = {"ms_per_step": t, "GBps": eff / (t * 1e-3) / 1e9}
+        extras["variants_cold"] = per
+        extras["ceiling_cold"] = ceilings(torch, dev, eff, nsets, args.steps, stream)
+
+    cpu = cpu_baseline(wl, eff, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {
+            "workload": "mixed_bf16: in-place apply, bf16 logits [256,128256] N(0,2), vocab_size=128000, "
+                        "mask int32 [256,4008] with per-row density U[0.001,0.5] and garbage padding words, "
+                        "128 unique random row indices",
+            "logits_dtype": "bfloat16",
+            "rows_processed": R, "vocab_size": V, "variant": args.variant,
+            "protocol": f"cold: {nsets} rotating buffer sets of {set_bytes / 1e6:.1f} MB "
+                        f"({nsets * set_bytes / 1e6:.0f} MB > 2 x 256 MB Infinity Cache); {args.steps} "
+                        "launches captured in one HIP graph, timed by HIP events on the launch stream",
+            "effective_bytes_per_step": eff,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+def ceilings(torch, dev, eff, nsets, steps, stream):
+    """Plain fill and copy over the same byte count, same rotation."""
+    n = eff // 2
+    nsets = max(2, math.ceil(2 * INFINITY_CACHE / eff))
+    bufs = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(nsets)]
+    half = [torch.empty(n // 2, dtype=torch.int16, device=dev) for _ in range(2 * nsets)]
+    torch.cuda.synchronize()
+    out = {}
+    for name, fn in (("fill", lambda k: bufs[k % nsets].fill_(-128)),
+                     ("copy", lambda k: half[(2 * k) % (2 * nsets)].copy_(half[(2 * k + 1) % (2 * nsets)]))):
+        with torch.cuda.stream(stream):
+            for k in range(10):
+                fn(k)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(steps):
+                fn(k)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        with torch.cuda.stream(stream):
+            g.replay()
+        e.record(stream)
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / steps
+        out[name] = {"bytes_per_step": eff, "ms_per_step": ms, "GBps": eff / (ms * 1e-3) / 1e9}
+        del g
+    return out
+
+
+def cpu_baseline(wl, eff, seconds):
+    """The oracle's C loop, one core, repeated full passes until `seconds` pass."""
+    import oracle
+
+    x = wl.logits.copy()
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.apply_inplace(x, wl.mask, wl.dtype, wl.vocab_size, list(wl.indices), wl.fill_value)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(eff * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} full passes of the same workload (128 indexed rows x 128000 tokens) "
+                      f"in {el:.1f} s on one host core"}
+
+
+if __name__ == "__main__":
+    main()

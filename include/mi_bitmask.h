@@ -1,0 +1,169 @@
+/*
+ * mi_bitmask.h -- C ABI of the packed-bitmask apply for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (XGrammar "Bitmask Operations", apply_token_bitmask_inplace;
+ * Modular MAX "apply_packed_bitmask"):
+ *
+ *   for every processed row r and every token v < V:
+ *       word = (uint32) mask[r, v / 32]
+ *       if bit (v % 32) of word is 0:  logits[r, v] = fill
+ *
+ * A set bit keeps the token, a clear bit masks it.  Words are int32 in
+ * memory (kept as int32 because old PyTorch had no uint32, XGrammar
+ * allocate_token_bitmask) and are read as uint32.
+ *
+ * Shared conventions of every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer except the ``out`` parameters of the host helpers
+ * is DEVICE memory, borrowed from the caller, and must stay valid until the
+ * work enqueued on ``stream`` has finished.  The library allocates nothing,
+ * keeps no state between calls and never synchronises: each call validates
+ * on the host, enqueues its kernel(s) on ``stream`` (0 = the null stream)
+ * and returns.  Calls are therefore legal under HIP graph capture.
+ *
+ * Layout.  logits is [rows, cols] of ``dtype`` with a contiguous last
+ * dimension and a row pitch of ``logits_row_stride`` ELEMENTS
+ * (>= cols).  mask is int32 [mask_rows, mask_cols] with a pitch of
+ * ``mask_row_stride`` WORDS (>= mask_cols).  logits must be aligned to its
+ * element size, mask and indices to 4 bytes.  Row pitches may break
+ * 16-byte alignment; the kernels handle any row start.
+ *
+ * Vocab size (XGrammar "Bitmask Operations", Notes: Padding).  vocab_size
+ * = -1 selects the default V = min(cols, 32 * mask_cols).  An explicit V
+ * must satisfy 0 <= V <= min(cols, 32 * mask_cols).  Only columns [0, V)
+ * and words [0, ceil(V/32)) are touched; bits past V in the last word and
+ * later words are never used (Modular MAX "apply_packed_bitmask": padding
+ * bits are never read).  Columns >= V of a processed row are never written
+ * in place.
+ *
+ * Rows (XGrammar "Bitmask Operations", Notes: Indices).  indices == NULL
+ * processes rows 0..rows-1 and needs mask_rows >= rows (extra mask rows are
+ * ignored) and num_indices == 0.  Otherwise indices is a device int32 array
+ * of num_indices row numbers; each r selects logits row r AND mask row r.
+ * They should be unique (duplicates only repeat identical writes) and lie
+ * in [0, min(rows, mask_rows)); the host cannot see device memory, so an
+ * out-of-range value is skipped by the kernel (that slot writes nothing).
+ * num_indices == 0 with a non-NULL pointer processes no row.
+ *
+ * Fill.  fill_value is rounded once, to nearest-even, into the dtype
+ * (overflow gives +-inf; NaN gives a quiet NaN with the input's sign).
+ * Kept elements are never rewritten with a different bit pattern: NaN
+ * payloads, -0.0 and subnormals survive exactly.
+ *
+ * Errors.  Every entry point returns a status and never throws or aborts.
+ * All argument checks run on the host before any HIP call, so a failing
+ * call enqueues nothing.  MI_ERR_HIP reports a launch failure; the HIP
+ * error text is then in mi_last_error_message().  The message is
+ * thread-local and valid until the thread's next call into the library.
+ */
+#ifndef MI_BITMASK_H
+#define MI_BITMASK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mi_dtype {
+    MI_DTYPE_F32 = 0,   /* IEEE binary32 */
+    MI_DTYPE_F16 = 1,   /* IEEE binary16 */
+    MI_DTYPE_BF16 = 2   /* bfloat16 */
+} mi_dtype_t;
+
+typedef enum mi_status {
+    MI_OK = 0,
+    MI_ERR_NULL_POINTER = 1,   /* a required pointer is NULL */
+    MI_ERR_BAD_DTYPE = 2,      /* dtype is not one of mi_dtype_t */
+    MI_ERR_BAD_SHAPE = 3,      /* negative size, pitch < width, too few mask rows, size limits */
+    MI_ERR_BAD_VOCAB = 4,      /* vocab_size < -1 or above min(cols, 32 * mask_cols) */
+    MI_ERR_BAD_INDICES = 5,    /* num_indices < 0 or too large */
+    MI_ERR_ALIAS = 6,          /* an output overlaps an input it must not overlap */
+    MI_ERR_MISALIGNED = 7,     /* a pointer is not aligned to its element size */
+    MI_ERR_BAD_VARIANT = 8,    /* unknown variant, or one the operation does not have */
+    MI_ERR_HIP = 9             /* the HIP runtime refused the launch */
+} mi_status_t;
+
+/* Kernel variants (the *_ex entry points).  All give bit-identical results. */
+typedef enum mi_variant {
+    MI_VARIANT_AUTO = 0,    /* the library's choice for the dtype and operation */
+    MI_VARIANT_SCALAR = 1,  /* one thread per element */
+    MI_VARIANT_VEC = 2,     /* 16-byte vectors: all-masked vectors are stored without a
+                               read, mixed ones read-select-write, all-kept ones skipped */
+    MI_VARIANT_WRONLY = 3   /* in place only: one lane per element, the store of the fill
+                               predicated by the mask bit; logits are never read */
+} mi_variant_t;
+
+/*
+ * In-place apply: logits[r, v] = fill for every processed row r and v < V
+ * whose mask bit is 0 (XGrammar "Bitmask Operations",
+ * apply_token_bitmask_inplace, with fill_value = -INFINITY for that page's
+ * semantics).  mask may not overlap logits; indices may not overlap logits.
+ * No work is enqueued when V == 0 or no row is processed.
+ */
+mi_status_t mi_apply_bitmask_inplace(
+    void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const int32_t *indices, int64_t num_indices,
+    double fill_value, hipStream_t stream);
+
+/*
+ * Out-of-place apply (Modular MAX "apply_packed_bitmask": one fused pass,
+ * output = logit where the bit is set, else fill_value).  out is [rows, cols]
+ * of the same dtype with pitch out_row_stride elements (>= cols).  Every
+ * element of out's [rows, cols] window is written: processed rows get the
+ * masked copy over [0, V) and a plain copy over [V, cols); rows outside an
+ * index list are plain copies.  out == logits with equal pitch is the
+ * in-place apply; any other overlap of out with logits, mask or indices is
+ * MI_ERR_ALIAS.  With an index list the call runs two kernels (copy, then
+ * the in-place apply on out).
+ */
+mi_status_t mi_apply_bitmask_out(
+    void *out, int64_t out_row_stride,
+    const void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const int32_t *indices, int64_t num_indices,
+    double fill_value, hipStream_t stream);
+
+/* As above, with an explicit kernel variant (MI_VARIANT_WRONLY: in place only). */
+mi_status_t mi_apply_bitmask_inplace_ex(
+    void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const int32_t *indices, int64_t num_indices,
+    double fill_value, mi_variant_t variant, hipStream_t stream);
+
+mi_status_t mi_apply_bitmask_out_ex(
+    void *out, int64_t out_row_stride,
+    const void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const int32_t *indices, int64_t num_indices,
+    double fill_value, mi_variant_t variant, hipStream_t stream);
+
+/*
+ * Host helpers (no device access, usable without a GPU).
+ *
+ * mi_resolve_vocab_size: the V the apply calls use (XGrammar "Bitmask
+ * Operations", Notes: Padding); *vocab_out receives it.  MI_ERR_BAD_VOCAB
+ * or MI_ERR_BAD_SHAPE as for the apply calls.
+ *
+ * mi_fill_value_bits: the bit pattern the apply calls store for fill_value
+ * in dtype (rounded once to nearest-even), in the low 16 or 32 bits of
+ * *bits_out.
+ */
+mi_status_t mi_resolve_vocab_size(int64_t cols, int64_t mask_cols, int64_t vocab_size,
+                                  int64_t *vocab_out);
+mi_status_t mi_fill_value_bits(double fill_value, mi_dtype_t dtype, uint32_t *bits_out);
+
+/* Static text for a status code ("MI_OK", ...); never NULL. */
+const char *mi_status_string(mi_status_t status);
+
+/* Detail of this thread's last non-OK return ("" if none yet). */
+const char *mi_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_BITMASK_H */

@@ -1,0 +1,235 @@
+"""ctypes binding of libmi_bitmask.so (include/mi_bitmask.h).
+
+Argument marshalling only: tensors become device pointers, element strides
+and torch's current HIP stream; every step of the apply runs in the
+library's kernels.  There is no fallback -- without the built library every
+entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import pathlib
+from typing import Optional, Sequence, Union
+
+PKG = pathlib.Path(__file__).resolve().parent
+LIBRARY = PKG / "libmi_bitmask.so"
+
+MI_DTYPE = {"float32": 0, "float16": 1, "bfloat16": 2}
+STATUS = ["MI_OK", "MI_ERR_NULL_POINTER", "MI_ERR_BAD_DTYPE", "MI_ERR_BAD_SHAPE", "MI_ERR_BAD_VOCAB",
+          "MI_ERR_BAD_INDICES", "MI_ERR_ALIAS", "MI_ERR_MISALIGNED", "MI_ERR_BAD_VARIANT", "MI_ERR_HIP"]
+VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3}
+
+# every symbol include/mi_bitmask.h declares
+EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",
+           "mi_apply_bitmask_out_ex", "mi_resolve_vocab_size", "mi_fill_value_bits",
+           "mi_status_string", "mi_last_error_message"]
+
+_i64, _p, _dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+_INPLACE = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _dbl]
+_OUT = [_p, _i64, _p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _dbl]
+
+_lib = None
+
+
+class BitmaskError(RuntimeError):
+    """A non-OK status from the library (``status`` holds its name)."""
+
+    def __init__(self, status: int, message: str):
+        self.status = STATUS[status] if 0 <= status < len(STATUS) else f"status {status}"
+        super().__init__(f"{self.status}: {message}")
+
+
+def load_library(path: Union[str, pathlib.Path, None] = None) -> ctypes.CDLL:
+    """Load (once) and return the C library; raises if it was never built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    so = pathlib.Path(path) if path else LIBRARY
+    if not so.exists():
+        raise ImportError(f"{so} is missing: build it with `python -m packed_logit_bitmask_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(str(so))
+    lib.mi_apply_bitmask_inplace.argtypes = _INPLACE + [_p]
+    lib.mi_apply_bitmask_inplace_ex.argtypes = _INPLACE + [ctypes.c_int, _p]
+    lib.mi_apply_bitmask_out.argtypes = _OUT + [_p]
+    lib.mi_apply_bitmask_out_ex.argtypes = _OUT + [ctypes.c_int, _p]
+    for f in ("mi_apply_bitmask_inplace", "mi_apply_bitmask_inplace_ex", "mi_apply_bitmask_out",
+              "mi_apply_bitmask_out_ex", "mi_resolve_vocab_size", "mi_fill_value_bits"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.mi_resolve_vocab_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64)]
+    lib.mi_fill_value_bits.argtypes = [_dbl, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
+    lib.mi_status_string.argtypes = [ctypes.c_int]
+    lib.mi_status_string.restype = ctypes.c_char_p
+    lib.mi_last_error_message.argtypes = []
+    lib.mi_last_error_message.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        msg = load_library().mi_last_error_message().decode(errors="replace")
+        raise BitmaskError(status, msg)
+
+
+# ----------------------------------------------------------------------------
+# host helpers
+# ----------------------------------------------------------------------------
+
+def resolve_vocab_size(cols: int, mask_cols: int, vocab_size: Optional[int] = None) -> int:
+    out = _i64()
+    check(load_library().mi_resolve_vocab_size(cols, mask_cols, -1 if vocab_size is None else vocab_size,
+                                               ctypes.byref(out)))
+    return out.value
+
+
+def fill_value_bits(fill_value: float, dtype: str) -> int:
+    out = ctypes.c_uint32()
+    check(load_library().mi_fill_value_bits(float(fill_value), MI_DTYPE[dtype], ctypes.byref(out)))
+    return out.value
+
+
+# ----------------------------------------------------------------------------
+# tensor marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_name(t) -> str:
+    torch = _torch()
+    names = {torch.float32: "float32", torch.float16: "float16", torch.bfloat16: "bfloat16"}
+    if t.dtype not in names:
+        raise TypeError(f"logits dtype {t.dtype} is not float32, float16 or bfloat16")
+    return names[t.dtype]
+
+
+def _as_rows(t, what: str):
+    """A [rows, cols] view of ``t`` (leading dims flattened), last dim contiguous."""
+    if t.dim() == 1:
+        t = t.unsqueeze(0)
+    if t.dim() > 2:
+        try:
+            t = t.view(-1, t.shape[-1])
+        except RuntimeError as e:
+            raise ValueError(f"{what}: leading dimensions cannot be flattened without a copy") from e
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{what}: last dimension must be contiguous")
+    return t
+
+
+def _row_stride(t) -> int:
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _stream_handle(device, stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def _indices_arg(indices, device, limit: int):
+    """(pointer, count, keepalive) for an index list or int tensor."""
+    torch = _torch()
+    if indices is None:
+        return None, 0, None
+    if isinstance(indices, torch.Tensor):
+        t = indices
+        if t.dim() != 1:
+            raise ValueError("indices must be 1-D")
+        if t.dtype != torch.int32 or t.device != device or (t.numel() > 1 and t.stride(0) != 1):
+            t = t.to(device=device, dtype=torch.int32).contiguous()
+    else:
+        lst = [int(i) for i in indices]
+        bad = [i for i in lst if not 0 <= i < limit]
+        if bad:
+            raise ValueError(f"indices {bad[:5]} outside [0, {limit})")
+        t = torch.tensor(lst, dtype=torch.int32, device=device)
+    # An empty list still needs a non-NULL pointer: NULL means "every row".
+    # The library never dereferences it when the count is 0.
+    ptr = t.data_ptr() if t.numel() else _EMPTY_LIST_PTR
+    return ptr, t.numel(), t
+
+
+_EMPTY_LIST_PTR = 256
+
+
+def _keep_alive(t, stream) -> None:
+    # An index tensor made here belongs to torch's current stream; when the
+    # kernel runs on another stream, tell the allocator so the memory is not
+    # reused before that stream is done with it.
+    if t is not None and stream is not None and t.numel():
+        t.record_stream(stream)
+
+
+def _check_mask(mask, device):
+    torch = _torch()
+    if not isinstance(mask, torch.Tensor) or mask.dtype != torch.int32:
+        raise TypeError("bitmask must be an int32 tensor")
+    if mask.device != device:
+        raise ValueError(f"bitmask is on {mask.device}, logits on {device}: copy the bitmask to the GPU first")
+    return _as_rows(mask, "bitmask")
+
+
+def mi_apply_bitmask_inplace(logits, mask, vocab_size: Optional[int] = None,
+                             indices: Union[None, Sequence[int], "torch.Tensor"] = None,
+                             fill_value: float = -math.inf, *, variant: str = "auto", stream=None):
+    """In-place apply on a GPU tensor; returns ``logits``.
+
+    XGrammar "Bitmask Operations", apply_token_bitmask_inplace semantics with
+    the Modular MAX fill_value: masked entries of the processed rows below
+    the vocab size become ``fill_value`` (default -inf).
+    """
+    if not logits.is_cuda:
+        raise ValueError("logits must be on the GPU (the library has no CPU path)")
+    lib = load_library()
+    L = _as_rows(logits, "logits")
+    M = _check_mask(mask, logits.device)
+    ip, n, keep = _indices_arg(indices, logits.device, min(L.shape[0], M.shape[0]))
+    args = (L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
+            M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
+            -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value))
+    st = _stream_handle(logits.device, stream)
+    _keep_alive(keep, stream)
+    if variant == "auto":
+        check(lib.mi_apply_bitmask_inplace(*args, st))
+    else:
+        check(lib.mi_apply_bitmask_inplace_ex(*args, VARIANT[variant], st))
+    return logits
+
+
+def mi_apply_bitmask_out(logits, mask, out=None, vocab_size: Optional[int] = None,
+                         indices: Union[None, Sequence[int], "torch.Tensor"] = None,
+                         fill_value: float = -math.inf, *, variant: str = "auto", stream=None):
+    """Out-of-place apply (Modular MAX "apply_packed_bitmask"); returns ``out``.
+
+    ``out`` defaults to a new tensor shaped like ``logits``.  Elements outside
+    the processed region are copies of ``logits``.
+    """
+    torch = _torch()
+    if not logits.is_cuda:
+        raise ValueError("logits must be on the GPU (the library has no CPU path)")
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(logits, memory_format=torch.contiguous_format)
+    if out.dtype != logits.dtype or out.shape != logits.shape or out.device != logits.device:
+        raise ValueError("out must match logits in dtype, shape and device")
+    L = _as_rows(logits, "logits")
+    O = _as_rows(out, "out")
+    M = _check_mask(mask, logits.device)
+    ip, n, keep = _indices_arg(indices, logits.device, min(L.shape[0], M.shape[0]))
+    args = (O.data_ptr(), _row_stride(O), L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1],
+            _row_stride(L), M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
+            -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value))
+    st = _stream_handle(logits.device, stream)
+    _keep_alive(keep, stream)
+    if variant == "auto":
+        check(lib.mi_apply_bitmask_out(*args, st))
+    else:
+        check(lib.mi_apply_bitmask_out_ex(*args, VARIANT[variant], st))
+    return out

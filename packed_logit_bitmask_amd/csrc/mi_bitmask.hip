@@ -1,0 +1,400 @@
+// Host side of the packed-bitmask apply: argument checks, vocab-size rule,
+// fill conversion, variant choice and kernel launches.  The C ABI is
+// declared (and documented) in include/mi_bitmask.h.
+//
+// Nothing here allocates, synchronises or touches device memory; every
+// check runs before the first HIP call, so a rejected call enqueues nothing.
+
+#include "mi_bitmask.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "apply_kernels.h"
+
+#define MI_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_message[512] = "";
+
+mi_status_t fail(mi_status_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_message, sizeof g_message, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+// Limits keep every index computation inside int32 (within a row) and
+// int64 (across rows), and the grid inside what one launch can carry.
+constexpr int64_t kMaxCols = int64_t(1) << 30;
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxPitch = int64_t(1) << 40;
+constexpr int64_t kMaxBytes = int64_t(1) << 56;
+constexpr int64_t kMaxBlocksPerLaunch = (int64_t(1) << 24) - 1;  // blocks * 256 < 2^32
+constexpr int kVecUnroll = 4;   // 16-byte vectors per lane in the vector kernels
+
+int elem_bytes(mi_dtype_t d) { return d == MI_DTYPE_F32 ? 4 : 2; }
+
+bool valid_dtype(int d) { return d == MI_DTYPE_F32 || d == MI_DTYPE_F16 || d == MI_DTYPE_BF16; }
+
+// Round a double once, to nearest-even, into a binary format with `ebits`
+// exponent and `mbits` fraction bits; returns the pattern in the low bits.
+// Works on the double's fields: drop the low bits of the 53-bit significand
+// (more of them below the target's normal range), round on the dropped
+// part, then re-encode, carrying into the exponent and overflowing to inf.
+uint32_t round_to_format(double x, int ebits, int mbits) {
+  uint64_t b;
+  std::memcpy(&b, &x, sizeof b);
+  const int width = 1 + ebits + mbits;
+  const uint32_t sbit = static_cast<uint32_t>(b >> 63) << (width - 1);
+  const uint32_t exp_all = (1u << ebits) - 1u;
+  const int dexp = static_cast<int>((b >> 52) & 0x7FF);
+  const uint64_t frac = b & ((uint64_t(1) << 52) - 1);
+  if (dexp == 0x7FF)  // inf, or NaN -> quiet NaN without payload
+    return frac ? (sbit | (exp_all << mbits) | (1u << (mbits - 1))) : (sbit | (exp_all << mbits));
+  if (dexp == 0) return sbit;  // zero or a double subnormal: far below every target's subnormals
+  const int bias = (1 << (ebits - 1)) - 1;
+  const int emin = 1 - bias;
+  int e = dexp - 1023;                                   // x = sig * 2^(e - 52)
+  const uint64_t sig = frac | (uint64_t(1) << 52);
+  const int drop = 52 - mbits + (e < emin ? emin - e : 0);
+  if (drop > 63) return sbit;
+  uint64_t kept = sig >> drop;
+  const uint64_t rem = sig & ((uint64_t(1) << drop) - 1);
+  const uint64_t half = uint64_t(1) << (drop - 1);
+  if (rem > half || (rem == half && (kept & 1u))) ++kept;
+  if (e < emin)  // subnormal; a carry to 2^mbits is the smallest normal, same integer
+    return sbit | static_cast<uint32_t>(kept);
+  if (kept == (uint64_t(1) << (mbits + 1))) {
+    kept >>= 1;
+    ++e;
+  }
+  const int ef = e + bias;
+  if (ef >= static_cast<int>(exp_all)) return sbit | (exp_all << mbits);
+  return sbit | (static_cast<uint32_t>(ef) << mbits) | static_cast<uint32_t>(kept - (uint64_t(1) << mbits));
+}
+
+uint32_t fill_pattern(double v, mi_dtype_t d) {
+  switch (d) {
+    case MI_DTYPE_F32: return round_to_format(v, 8, 23);
+    case MI_DTYPE_F16: return round_to_format(v, 5, 10);
+    default: return round_to_format(v, 8, 7);
+  }
+}
+
+struct ByteRange {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+bool extent(const void* p, int64_t rows, int64_t width, int64_t pitch, int64_t esize, ByteRange* out) {
+  *out = ByteRange{};
+  if (rows <= 0 || width <= 0) return true;
+  int64_t n, bytes;
+  if (__builtin_mul_overflow(rows - 1, pitch, &n) || __builtin_add_overflow(n, width, &n) ||
+      __builtin_mul_overflow(n, esize, &bytes) || bytes > kMaxBytes)
+    return false;
+  out->lo = reinterpret_cast<uintptr_t>(p);
+  out->hi = out->lo + static_cast<uintptr_t>(bytes);
+  return out->hi > out->lo;
+}
+
+bool overlaps(const ByteRange& a, const ByteRange& b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+mi_status_t resolve_vocab(int64_t cols, int64_t mask_cols, int64_t vocab_size, int64_t* V) {
+  if (cols < 0 || mask_cols < 0) return fail(MI_ERR_BAD_SHAPE, "negative width (cols %lld, mask_cols %lld)",
+                                             (long long)cols, (long long)mask_cols);
+  if (cols > kMaxCols || mask_cols > kMaxCols)
+    return fail(MI_ERR_BAD_SHAPE, "width above the limit 2^30 (cols %lld, mask_cols %lld)",
+                (long long)cols, (long long)mask_cols);
+  const int64_t limit = std::min(cols, 32 * mask_cols);
+  if (vocab_size == -1) {
+    *V = limit;
+    return MI_OK;
+  }
+  if (vocab_size < 0 || vocab_size > limit)
+    return fail(MI_ERR_BAD_VOCAB, "vocab_size %lld outside [0, min(cols %lld, 32 * mask_cols %lld) = %lld]",
+                (long long)vocab_size, (long long)cols, (long long)mask_cols, (long long)limit);
+  *V = vocab_size;
+  return MI_OK;
+}
+
+// Everything the kernels need after validation.
+struct Plan {
+  int64_t V = 0, W = 0;       // vocab and words per row actually used
+  int64_t R = 0;              // processed row slots
+  int64_t row_limit = 0;      // valid row numbers for an index list
+  int esize = 0;
+  uint32_t fill = 0;
+  ByteRange logits, mask, indices;
+};
+
+mi_status_t check_common(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t ls,
+                         const int32_t* mask, int64_t mask_rows, int64_t mask_cols, int64_t ms,
+                         int64_t vocab_size, const int32_t* indices, int64_t num_indices,
+                         double fill_value, Plan* p) {
+  if (!logits) return fail(MI_ERR_NULL_POINTER, "logits is NULL");
+  if (!mask) return fail(MI_ERR_NULL_POINTER, "mask is NULL");
+  if (!indices && num_indices > 0) return fail(MI_ERR_NULL_POINTER, "indices is NULL but num_indices is %lld",
+                                              (long long)num_indices);
+  if (!valid_dtype(static_cast<int>(dtype))) return fail(MI_ERR_BAD_DTYPE, "unknown dtype %d", (int)dtype);
+  if (rows < 0 || cols < 0 || mask_rows < 0 || mask_cols < 0)
+    return fail(MI_ERR_BAD_SHAPE, "negative size (rows %lld, cols %lld, mask_rows %lld, mask_cols %lld)",
+                (long long)rows, (long long)cols, (long long)mask_rows, (long long)mask_cols);
+  if (rows > kMaxRows || mask_rows > kMaxRows)
+    return fail(MI_ERR_BAD_SHAPE, "row count above the limit 2^31 - 1");
+  if (ls < cols || ls > kMaxPitch)
+    return fail(MI_ERR_BAD_SHAPE, "logits_row_stride %lld must be in [cols %lld, 2^40]", (long long)ls,
+                (long long)cols);
+  if (ms < mask_cols || ms > kMaxPitch)
+    return fail(MI_ERR_BAD_SHAPE, "mask_row_stride %lld must be in [mask_cols %lld, 2^40]", (long long)ms,
+                (long long)mask_cols);
+  mi_status_t st = resolve_vocab(cols, mask_cols, vocab_size, &p->V);
+  if (st != MI_OK) return st;
+  if (num_indices < 0 || num_indices > kMaxRows)
+    return fail(MI_ERR_BAD_INDICES, "num_indices %lld outside [0, 2^31 - 1]", (long long)num_indices);
+  if (indices) {
+    p->R = num_indices;
+    p->row_limit = std::min(rows, mask_rows);
+  } else {
+    if (mask_rows < rows)
+      return fail(MI_ERR_BAD_SHAPE, "mask has %lld rows for %lld logits rows (no index list)",
+                  (long long)mask_rows, (long long)rows);
+    p->R = rows;
+    p->row_limit = rows;
+  }
+  p->esize = elem_bytes(dtype);
+  if (reinterpret_cast<uintptr_t>(logits) % p->esize)
+    return fail(MI_ERR_MISALIGNED, "logits not aligned to its %d-byte elements", p->esize);
+  if (reinterpret_cast<uintptr_t>(mask) % 4) return fail(MI_ERR_MISALIGNED, "mask not 4-byte aligned");
+  if (indices && reinterpret_cast<uintptr_t>(indices) % 4)
+    return fail(MI_ERR_MISALIGNED, "indices not 4-byte aligned");
+  if (!extent(logits, rows, cols, ls, p->esize, &p->logits) ||
+      !extent(mask, mask_rows, mask_cols, ms, 4, &p->mask) ||
+      !extent(indices, indices ? 1 : 0, num_indices, num_indices, 4, &p->indices))
+    return fail(MI_ERR_BAD_SHAPE, "buffer extent overflows");
+  p->W = (p->V + 31) / 32;
+  p->fill = fill_pattern(fill_value, dtype);
+  return MI_OK;
+}
+
+mi_status_t after_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MI_OK;
+}
+
+template <typename Launch>
+mi_status_t launch_slots(int64_t slots, int64_t chunks, Launch&& launch) {
+  const int64_t per = std::max<int64_t>(1, kMaxBlocksPerLaunch / chunks);
+  for (int64_t s0 = 0; s0 < slots; s0 += per) {
+    const int64_t n = std::min(per, slots - s0);
+    launch(s0, static_cast<uint32_t>(n * chunks), static_cast<uint32_t>(chunks));
+  }
+  return MI_OK;
+}
+
+template <typename T>
+mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64_t ms, const int32_t* indices,
+                        const Plan& p, mi_variant_t variant, hipStream_t stream) {
+  T* logits = static_cast<T*>(logits_v);
+  const uint32_t* mask = reinterpret_cast<const uint32_t*>(mask_i);
+  const mi::RowMap map{indices, p.row_limit};
+  const T fill = static_cast<T>(p.fill);
+  const int32_t V = static_cast<int32_t>(p.V), W = static_cast<int32_t>(p.W);
+  (void)hipGetLastError();  // report only what this call's launches raise
+  switch (variant) {
+    case MI_VARIANT_SCALAR: {
+      const int64_t chunks = (p.V + mi::kBlock * 8 - 1) / (mi::kBlock * 8);
+      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+        mi::inplace_scalar<T><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, map, s0, ch, fill);
+      });
+      return after_launch("inplace_scalar");
+    }
+    case MI_VARIANT_VEC: {
+      constexpr int VW = mi::Bits16B<T>::VW;
+      const int64_t per = int64_t(mi::kBlock) * kVecUnroll;
+      const int64_t chunks = std::max<int64_t>(1, (p.V / VW + per - 1) / per);
+      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+        mi::inplace_vec<T, kVecUnroll><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, W, map, s0, ch,
+                                                                          fill);
+      });
+      return after_launch("inplace_vec");
+    }
+    case MI_VARIANT_WRONLY: {
+      const int64_t chunks = (p.W + 255) / 256;
+      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+        mi::inplace_wronly<T><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, W, map, s0, ch, fill);
+      });
+      return after_launch("inplace_wronly");
+    }
+    default:
+      return fail(MI_ERR_BAD_VARIANT, "variant %d", (int)variant);
+  }
+}
+
+// Out of place over every row: apply != 0 masks [0, V), apply == 0 copies.
+template <typename T>
+mi_status_t run_out(void* out_v, int64_t os, const void* in_v, int64_t ls, const int32_t* mask_i, int64_t ms,
+                    int64_t rows, int64_t cols, const Plan& p, int32_t apply, bool vec, hipStream_t stream) {
+  T* out = static_cast<T*>(out_v);
+  const T* in = static_cast<const T*>(in_v);
+  const uint32_t* mask = reinterpret_cast<const uint32_t*>(mask_i);
+  const T fill = static_cast<T>(p.fill);
+  const int32_t V = static_cast<int32_t>(p.V), W = static_cast<int32_t>(p.W), C = static_cast<int32_t>(cols);
+  (void)hipGetLastError();
+  if (vec) {
+    constexpr int VW = mi::Bits16B<T>::VW;
+    const int64_t per = int64_t(mi::kBlock) * kVecUnroll;
+    const int64_t chunks = std::max<int64_t>(1, (cols / VW + per - 1) / per);
+    launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+      mi::out_vec<T, kVecUnroll><<<blocks, mi::kBlock, 0, stream>>>(out, os, in, ls, mask, ms, V, W, C, apply, s0, ch,
+                                                                    fill);
+    });
+    return after_launch("out_vec");
+  }
+  const int64_t chunks = (cols + mi::kBlock * 8 - 1) / (mi::kBlock * 8);
+  launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+    mi::out_scalar<T><<<blocks, mi::kBlock, 0, stream>>>(out, os, in, ls, mask, ms, V, C, apply, s0, ch, fill);
+  });
+  return after_launch("out_scalar");
+}
+
+mi_variant_t auto_inplace(mi_dtype_t) { return MI_VARIANT_VEC; }
+
+mi_status_t inplace_impl(void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t ls,
+                         const int32_t* mask, int64_t mask_rows, int64_t mask_cols, int64_t ms, int64_t vocab_size,
+                         const int32_t* indices, int64_t num_indices, double fill_value, mi_variant_t variant,
+                         hipStream_t stream) {
+  Plan p;
+  mi_status_t st = check_common(logits, dtype, rows, cols, ls, mask, mask_rows, mask_cols, ms, vocab_size, indices,
+                                num_indices, fill_value, &p);
+  if (st != MI_OK) return st;
+  if (overlaps(p.mask, p.logits)) return fail(MI_ERR_ALIAS, "mask overlaps logits");
+  if (overlaps(p.indices, p.logits)) return fail(MI_ERR_ALIAS, "indices overlap logits");
+  if (variant == MI_VARIANT_AUTO) variant = auto_inplace(dtype);
+  if (variant != MI_VARIANT_SCALAR && variant != MI_VARIANT_VEC && variant != MI_VARIANT_WRONLY)
+    return fail(MI_ERR_BAD_VARIANT, "unknown in-place variant %d", (int)variant);
+  if (p.V == 0 || p.R == 0) return MI_OK;
+  if (p.esize == 4) return run_inplace<uint32_t>(logits, ls, mask, ms, indices, p, variant, stream);
+  return run_inplace<uint16_t>(logits, ls, mask, ms, indices, p, variant, stream);
+}
+
+mi_status_t out_impl(void* out, int64_t os, const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                     int64_t ls, const int32_t* mask, int64_t mask_rows, int64_t mask_cols, int64_t ms,
+                     int64_t vocab_size, const int32_t* indices, int64_t num_indices, double fill_value,
+                     mi_variant_t variant, hipStream_t stream) {
+  if (!out) return fail(MI_ERR_NULL_POINTER, "out is NULL");
+  if (variant != MI_VARIANT_AUTO && variant != MI_VARIANT_SCALAR && variant != MI_VARIANT_VEC)
+    return fail(MI_ERR_BAD_VARIANT, "variant %d has no out-of-place form", (int)variant);
+  Plan p;
+  mi_status_t st = check_common(logits, dtype, rows, cols, ls, mask, mask_rows, mask_cols, ms, vocab_size, indices,
+                                num_indices, fill_value, &p);
+  if (st != MI_OK) return st;
+  if (os < cols || os > kMaxPitch)
+    return fail(MI_ERR_BAD_SHAPE, "out_row_stride %lld must be in [cols %lld, 2^40]", (long long)os, (long long)cols);
+  if (reinterpret_cast<uintptr_t>(out) % p.esize)
+    return fail(MI_ERR_MISALIGNED, "out not aligned to its %d-byte elements", p.esize);
+  ByteRange ob;
+  if (!extent(out, rows, cols, os, p.esize, &ob)) return fail(MI_ERR_BAD_SHAPE, "out extent overflows");
+  if (out == logits && os == ls) {  // the output is the input: this is the in-place apply
+    return inplace_impl(out, dtype, rows, cols, ls, mask, mask_rows, mask_cols, ms, vocab_size, indices,
+                        num_indices, fill_value, variant, stream);
+  }
+  if (overlaps(ob, p.logits)) return fail(MI_ERR_ALIAS, "out overlaps logits");
+  if (overlaps(ob, p.mask)) return fail(MI_ERR_ALIAS, "out overlaps mask");
+  if (overlaps(ob, p.indices)) return fail(MI_ERR_ALIAS, "out overlaps indices");
+  if (rows == 0 || cols == 0) return MI_OK;
+
+  // 16-byte vectors need out and logits rows at the same offset modulo 16.
+  const bool same_phase =
+      (reinterpret_cast<uintptr_t>(out) - reinterpret_cast<uintptr_t>(logits)) % 16 == 0 &&
+      (rows == 1 || ((os - ls) * p.esize) % 16 == 0);
+  const bool vec = variant == MI_VARIANT_SCALAR ? false : same_phase;
+  // Without an index list every row is processed in one fused pass.  With one,
+  // out first becomes a copy of logits and the listed rows are then masked in
+  // place on out (rows outside the list stay copies).
+  const int32_t apply = (indices == nullptr && p.V > 0) ? 1 : 0;
+  st = p.esize == 4 ? run_out<uint32_t>(out, os, logits, ls, mask, ms, rows, cols, p, apply, vec, stream)
+                    : run_out<uint16_t>(out, os, logits, ls, mask, ms, rows, cols, p, apply, vec, stream);
+  if (st != MI_OK || indices == nullptr || p.V == 0 || p.R == 0) return st;
+  const mi_variant_t iv = variant == MI_VARIANT_SCALAR ? MI_VARIANT_SCALAR : auto_inplace(dtype);
+  return p.esize == 4 ? run_inplace<uint32_t>(out, os, mask, ms, indices, p, iv, stream)
+                      : run_inplace<uint16_t>(out, os, mask, ms, indices, p, iv, stream);
+}
+
+}  // namespace
+
+MI_API mi_status_t mi_apply_bitmask_inplace(void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                                            int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
+                                            int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
+                                            const int32_t* indices, int64_t num_indices, double fill_value,
+                                            hipStream_t stream) {
+  return inplace_impl(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
+                      vocab_size, indices, num_indices, fill_value, MI_VARIANT_AUTO, stream);
+}
+
+MI_API mi_status_t mi_apply_bitmask_inplace_ex(void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                                               int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
+                                               int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
+                                               const int32_t* indices, int64_t num_indices, double fill_value,
+                                               mi_variant_t variant, hipStream_t stream) {
+  return inplace_impl(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
+                      vocab_size, indices, num_indices, fill_value, variant, stream);
+}
+
+MI_API mi_status_t mi_apply_bitmask_out(void* out, int64_t out_row_stride, const void* logits, mi_dtype_t dtype,
+                                        int64_t rows, int64_t cols, int64_t logits_row_stride, const int32_t* mask,
+                                        int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+                                        int64_t vocab_size, const int32_t* indices, int64_t num_indices,
+                                        double fill_value, hipStream_t stream) {
+  return out_impl(out, out_row_stride, logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols,
+                  mask_row_stride, vocab_size, indices, num_indices, fill_value, MI_VARIANT_AUTO, stream);
+}
+
+MI_API mi_status_t mi_apply_bitmask_out_ex(void* out, int64_t out_row_stride, const void* logits, mi_dtype_t dtype,
+                                           int64_t rows, int64_t cols, int64_t logits_row_stride, const int32_t* mask,
+                                           int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+                                           int64_t vocab_size, const int32_t* indices, int64_t num_indices,
+                                           double fill_value, mi_variant_t variant, hipStream_t stream) {
+  return out_impl(out, out_row_stride, logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols,
+                  mask_row_stride, vocab_size, indices, num_indices, fill_value, variant, stream);
+}
+
+MI_API mi_status_t mi_resolve_vocab_size(int64_t cols, int64_t mask_cols, int64_t vocab_size, int64_t* vocab_out) {
+  if (!vocab_out) return fail(MI_ERR_NULL_POINTER, "vocab_out is NULL");
+  return resolve_vocab(cols, mask_cols, vocab_size, vocab_out);
+}
+
+MI_API mi_status_t mi_fill_value_bits(double fill_value, mi_dtype_t dtype, uint32_t* bits_out) {
+  if (!bits_out) return fail(MI_ERR_NULL_POINTER, "bits_out is NULL");
+  if (!valid_dtype(static_cast<int>(dtype))) return fail(MI_ERR_BAD_DTYPE, "unknown dtype %d", (int)dtype);
+  *bits_out = fill_pattern(fill_value, dtype);
+  return MI_OK;
+}
+
+MI_API const char* mi_status_string(mi_status_t s) {
+  switch (s) {
+    case MI_OK: return "MI_OK";
+    case MI_ERR_NULL_POINTER: return "MI_ERR_NULL_POINTER";
+    case MI_ERR_BAD_DTYPE: return "MI_ERR_BAD_DTYPE";
+    case MI_ERR_BAD_SHAPE: return "MI_ERR_BAD_SHAPE";
+    case MI_ERR_BAD_VOCAB: return "MI_ERR_BAD_VOCAB";
+    case MI_ERR_BAD_INDICES: return "MI_ERR_BAD_INDICES";
+    case MI_ERR_ALIAS: return "MI_ERR_ALIAS";
+    case MI_ERR_MISALIGNED: return "MI_ERR_MISALIGNED";
+    case MI_ERR_BAD_VARIANT: return "MI_ERR_BAD_VARIANT";
+    case MI_ERR_HIP: return "MI_ERR_HIP";
+  }
+  return "MI_ERR_UNKNOWN";
+}
+
+MI_API const char* mi_last_error_message(void) { return g_message; }
