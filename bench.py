@@ -46,7 +46,55 @@ def parse():
     ap.add_argument("--variant", default="auto", choices=["auto", "scalar", "vec", "wronly"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU work for the oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip the warm, per-variant and ceiling figures")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain 64 MiB device copies (for scaling FETCH_SIZE/WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = [ROOT / "packed_logit_bitmask_amd" / "csrc" / "apply_kernels.h",
+                  ROOT / "packed_logit_bitmask_amd" / "csrc" / "mi_bitmask.hip"]
+PMC_SUMMARY = ROOT / "profiles" / "inplace_vec_mixed_bf16_pmc.md"
+
+
+def counted_traffic():
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary.
+
+    None when the summary is missing or was taken on kernel sources other
+    than the ones in this tree.
+    """
+    import hashlib
+    import re
+
+    if not PMC_SUMMARY.exists():
+        return None
+    text = PMC_SUMMARY.read_text()
+    m_bytes = re.search(r"^traffic_bytes_per_dispatch:\s*(\d+)", text, re.M)
+    m_sha = re.search(r"^kernel_source_sha256_16:\s*([0-9a-f]+)", text, re.M)
+    if not (m_bytes and m_sha):
+        return None
+    h = hashlib.sha256(b"".join(p.read_bytes() for p in KERNEL_SOURCES)).hexdigest()[:16]
+    return int(m_bytes.group(1)) if h == m_sha.group(1) else None
+
+
+def copy_calibration():
+    """Five plain copies of 64 MiB, caches flushed between them by a 600 MiB fill.
+
+    Under rocprofv3 --pmc the copy kernel's FETCH_SIZE and WRITE_SIZE per
+    dispatch, against the 65536 KiB it really reads and writes, give the
+    factors that turn the counters into bytes.
+    """
+    import torch
+
+    n = 64 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(600 << 20, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    for k in range(5):
+        flush.fill_(k)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "dispatches": 5}}), flush=True)
 
 
 def effective_bytes(rows: int, vocab: int, esize: int, out_of_place: bool = False) -> int:
@@ -56,6 +104,9 @@ def effective_bytes(rows: int, vocab: int, esize: int, out_of_place: bool = Fals
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the apply has no cross-GPU step, and this build runs on a "
               "single GPU only (--gpus 1).", file=sys.stderr)
@@ -168,7 +219,7 @@ def main():
             "peak": PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps / PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(),
         },
         "cpu_baseline": cpu,
     }

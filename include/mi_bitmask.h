@@ -17,7 +17,8 @@
  * ---------------------------------------
  * Memory.  Every pointer except the ``out`` parameters of the host helpers
  * is DEVICE memory, borrowed from the caller, and must stay valid until the
- * work enqueued on ``stream`` has finished.  The library allocates nothing,
+ * work enqueued on ``stream`` has finished.  A buffer with no elements (zero
+ * rows or zero columns) may be NULL.  The library allocates nothing,
  * keeps no state between calls and never synchronises: each call validates
  * on the host, enqueues its kernel(s) on ``stream`` (0 = the null stream)
  * and returns.  Calls are therefore legal under HIP graph capture.

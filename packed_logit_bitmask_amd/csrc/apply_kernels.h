@@ -38,6 +38,18 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Cache-policy bits of a gfx950 vector memory instruction (the `aux`
+// operand): SC0 = 1, NT = 2, SC1 = 16.  A store with SC1 set has device
+// scope: it is written through the XCD's L2 instead of lying dirty there
+// until the end-of-kernel writeback, so a kernel whose output does not fit
+// the L2s streams its writes while it runs.  NT marks the data as
+// non-temporal (streamed, not kept).
+enum StorePolicy : int {
+  kStoreWriteBack = 0,          // default: lines stay dirty in L2
+  kStoreDevice = 16,            // SC1: write through L2
+  kStoreDeviceStream = 16 | 2,  // SC1 + NT: write through, do not keep
+};
+
 __device__ __forceinline__ uint32_t load_word(Rsrc r, int32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
 }
@@ -45,10 +57,11 @@ __device__ __forceinline__ uint4 load16(Rsrc r, int32_t byte_off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int POLICY>
 __device__ __forceinline__ void store16(Rsrc r, int32_t byte_off, uint4 v) {
   u32x4 d;
   d.x = v.x; d.y = v.y; d.z = v.z; d.w = v.w;
-  __builtin_amdgcn_raw_buffer_store_b128(d, r, byte_off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, byte_off, 0, POLICY);
 }
 
 // Slot -> row.  Without an index list the slot is the row.  With one, an
@@ -144,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void inplace_scalar(
 // row.  When the row start is not 16-byte aligned the mask window of a
 // vector can straddle two words; a funnel shift joins them.
 // ---------------------------------------------------------------------------
-template <typename T, int U>
+template <typename T, int U, int POLICY>
 __global__ __launch_bounds__(kBlock) void inplace_vec(
     T* __restrict__ logits, int64_t ls, const uint32_t* __restrict__ mask, int64_t ms,
     int32_t V, int32_t W, RowMap map, int64_t slot_base, uint32_t chunks, T fill) {
@@ -194,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void inplace_vec(
   const uint32_t fw = fill_word_of(fill);
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    store16(rl, keep[u] != FULL ? (u * kBlock + t) * 16 : kSkip, select16<T>(v[u], keep[u], fw));
+    store16<POLICY>(rl, keep[u] != FULL ? (u * kBlock + t) * 16 : kSkip, select16<T>(v[u], keep[u], fw));
 }
 
 // ---------------------------------------------------------------------------
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void out_scalar(
 // otherwise read, select (tokens >= V, and every token when `apply` is 0,
 // count as kept), write.  Head and tail elements go one at a time.
 // ---------------------------------------------------------------------------
-template <typename T, int U>
+template <typename T, int U, int POLICY>
 __global__ __launch_bounds__(kBlock) void out_vec(
     T* __restrict__ out, int64_t os, const T* __restrict__ in, int64_t ls,
     const uint32_t* __restrict__ mask, int64_t ms, int32_t V, int32_t W, int32_t cols,
@@ -323,7 +336,7 @@ __global__ __launch_bounds__(kBlock) void out_vec(
   for (int u = 0; u < U; ++u) v[u] = load16(ri, keep[u] != 0u ? (u * kBlock + t) * 16 : kSkip);
   const uint32_t fw = fill_word_of(fill);
 #pragma unroll
-  for (int u = 0; u < U; ++u) store16(ro, (u * kBlock + t) * 16, select16<T>(v[u], keep[u], fw));
+  for (int u = 0; u < U; ++u) store16<POLICY>(ro, (u * kBlock + t) * 16, select16<T>(v[u], keep[u], fw));
 }
 
 }  // namespace mi

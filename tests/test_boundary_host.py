@@ -123,6 +123,7 @@ def outofplace(**kw):
 REJECT_INPLACE = [
     ("null logits", dict(logits=None), NULLP),
     ("null mask", dict(mask=None), NULLP),
+    ("null logits with rows but empty mask", dict(logits=None, mask=None, mask_cols=0), NULLP),
     ("indices NULL with count", dict(indices=None, n=3), NULLP),
     ("bad dtype", dict(dtype=3), DTYPE),
     ("negative dtype", dict(dtype=-1), DTYPE),
@@ -153,6 +154,13 @@ REJECT_INPLACE = [
 def test_inplace_rejections(name, kw, code):
     assert inplace(**kw) == code
     assert mb.load_library().mi_last_error_message().decode()
+
+
+def test_null_is_fine_for_empty_buffers():
+    # checked through a later error so that nothing is launched
+    assert inplace(logits=None, rows=0, mask=None, mask_rows=0, variant=7) == VARIANT
+    assert inplace(logits=None, cols=0, ls=0, variant=7) == VARIANT
+    assert outofplace(out=None, logits=None, rows=0, mask_rows=0, variant=3) == VARIANT
 
 
 def test_adjacent_buffers_are_not_aliases():

@@ -192,6 +192,21 @@ def test_named_large_fp32(large, variant):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,rows,cols,vocab", [
+    ("bfloat16", 800, 40001, 39999),   # > 48 MB of 16-bit writes: one vector per lane, streaming stores
+    ("float16", 700, 50003, None),
+    ("float32", 500, 30001, 29990),    # > 48 MB of 32-bit writes: four vectors per lane
+])
+def test_large_shapes_misaligned(dtype, rows, cols, vocab):
+    rng = np.random.default_rng(rows)
+    say(f"[gpu] large misaligned {dtype} [{rows},{cols}] vocab={vocab}")
+    wl, _, _ = workloads.random_case(rng, dtype, rows, cols, vocab_size=vocab, density=0.3, specials=True)
+    run_inplace_case(rng, wl, "auto", stride=cols + 3, guard=3)
+    wl.indices = rng.permutation(rows)[: rows - 7].astype(np.int32)
+    run_inplace_case(rng, wl, "vec", stride=cols + 1, guard=1)
+    run_out_case(rng, wl, "auto", stride=cols + 2, out_stride=cols + 6, guard=2, out_guard=6)
+
+
 # ----------------------------------------------------------------------------
 # seeded fuzz: ragged shapes, every index form, every variant
 # ----------------------------------------------------------------------------
