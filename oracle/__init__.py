@@ -7,13 +7,13 @@ here, and nothing here imports the product.
 
 What the oracle computes, and where each piece comes from:
 
-* ``get_bitmask_value`` -- bit ``j % 32`` of word ``j // 32`` of row ``i``;
-  a 1 keeps the token, a 0 masks it.  XGrammar "Bitmask Operations",
-  apply_token_bitmask_inplace ("0 means the token is masked and 1 means the
-  token is not masked"; get_bitmask_value takes the j-th bit of row i);
-  Modular MAX "apply_packed_bitmask" (kept "when bit v % 32 of word
-  packed[b, v // 32] is set").  Words are int32 only for old-PyTorch reasons
-  (XGrammar, allocate_token_bitmask), so they are read as uint32.
+* ``get_bitmask_value`` -- row i's token j sits at bit ``j % 32`` of word
+  ``j // 32``; a set bit keeps the token and a clear bit masks it.
+  XGrammar "Bitmask Operations", apply_token_bitmask_inplace (a zero bit
+  masks, a one bit keeps; the j-th bit of row i); Modular MAX
+  "apply_packed_bitmask" (the bit-within-word and word-within-row rule).
+  Words are int32 only for old-PyTorch reasons (XGrammar,
+  allocate_token_bitmask), so they are read as uint32.
 * ``resolve_vocab_size`` -- XGrammar "Bitmask Operations", Notes: Padding:
   a given vocab size restricts the op to logits[..., :V] and
   bitmask[..., :ceil(V/32)]; without one V = min(logits cols, 32 * mask cols).

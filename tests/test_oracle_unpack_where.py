@@ -30,7 +30,7 @@ def unpack_where(logits, mask, dtype, vocab, rows, fill_value):
 
 
 def test_numpy_bit_order_matches_pages():
-    # word 1 -> token 0 only; INT32_MIN -> token 31 only (bit v % 32 of word v // 32)
+    # word 1 -> token 0 only; INT32_MIN -> token 31 only (LSB-first tokens in each word)
     m = np.array([[1, -(2**31)]], dtype=np.int32)
     u = np.unpackbits(m.view(np.uint8), axis=1, bitorder="little")
     assert u[0, 0] == 1 and u[0, 1:32].sum() == 0
