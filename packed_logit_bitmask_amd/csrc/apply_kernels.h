@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kBlock) void inplace_scalar(
 // ---------------------------------------------------------------------------
 // In place, 16-byte vectors.  Each lane owns U vectors spaced one block
 // apart, so every wave instruction covers 1 KiB of consecutive logits.
-// Per vector: all kept -> nothing; all masked -> store the fill vector
-// without reading; mixed -> read, select, write.  Loads and stores are
+// Per 128-byte line: all kept -> nothing; otherwise every vector is written:
+// all masked -> the fill vector, without reading; the others read, selected
+// and written (kept elements get their own bits back).  Loads and stores are
 // predicated through buffer range checks, not branches.
 // The row's elements before the first 16-byte boundary (head) and after the
 // last whole vector below V (tail) are done one element at a time by block 0
@@ -190,24 +191,44 @@ __global__ __launch_bounds__(kBlock) void inplace_vec(
   const Rsrc rl = make_rsrc(row + h + static_cast<int64_t>(kbase) * VW, static_cast<uint32_t>(nv) * 16u);
   const Rsrc rm = make_rsrc(mrow, static_cast<uint32_t>(W) * 4u);
 
-  uint32_t keep[U];
+  uint32_t lo[U], hi[U], keep[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int32_t e = h + (kbase + u * kBlock + t) * VW;   // first token of the vector
-    const uint32_t lo = load_word(rm, (e >> 5) * 4);
-    const uint32_t hi = h ? load_word(rm, ((e >> 5) + 1) * 4) : 0u;
-    keep[u] = __builtin_amdgcn_alignbit(hi, lo, static_cast<uint32_t>(e) & 31u) & FULL;
+    lo[u] = load_word(rm, (e >> 5) * 4);
+    hi[u] = load_word(rm, h ? ((e >> 5) + 1) * 4 : kSkip);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t e = h + (kbase + u * kBlock + t) * VW;
+    // lanes past the chunk's last vector count as all kept (nothing to write)
+    const uint32_t past = u * kBlock + t < nv ? 0u : FULL;
+    keep[u] = (__builtin_amdgcn_alignbit(hi[u], lo[u], static_cast<uint32_t>(e) & 31u) & FULL) | past;
+  }
+  // Line-complete writes: the (up to) 8 lanes whose vectors share a 128-byte
+  // line decide together.  If any vector of the line needs a store, every
+  // vector of the line is stored -- all-kept ones written back with their own
+  // bits -- so the line leaves the L2 whole; a partly written line would cost
+  // a read-modify-write at the memory side.  A vector is read unless it is
+  // all masked (its line is being read anyway when a neighbour is).
+  const int lane = t & 63;
+  const int line_pos = static_cast<int>(((reinterpret_cast<uintptr_t>(row + h) >> 4) + kbase + t) & 7u);
+  const int first = lane - line_pos;                      // lane holding the line's first vector
+  const uint64_t line_lanes = first >= 0 ? (uint64_t(0xFF) << first) : (uint64_t(0xFF) >> -first);
+  bool write[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t needs = __builtin_amdgcn_ballot_w64(keep[u] != FULL);
+    write[u] = (needs & line_lanes) != 0;
   }
   uint4 v[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool mixed = keep[u] != FULL && keep[u] != 0u;
-    v[u] = load16(rl, mixed ? (u * kBlock + t) * 16 : kSkip);
-  }
+  for (int u = 0; u < U; ++u)
+    v[u] = load16(rl, (write[u] && keep[u] != 0u) ? (u * kBlock + t) * 16 : kSkip);
   const uint32_t fw = fill_word_of(fill);
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    store16<POLICY>(rl, keep[u] != FULL ? (u * kBlock + t) * 16 : kSkip, select16<T>(v[u], keep[u], fw));
+    store16<POLICY>(rl, write[u] ? (u * kBlock + t) * 16 : kSkip, select16<T>(v[u], keep[u], fw));
 }
 
 // ---------------------------------------------------------------------------
