@@ -143,6 +143,30 @@ mi_status_t mi_apply_bitmask_out_ex(
     double fill_value, mi_variant_t variant, hipStream_t stream);
 
 /*
+ * Host-memory apply, for logits and masks that live on the CPU (XGrammar
+ * "Bitmask Operations", Notes: Device: CPU tensors get a CPU
+ * implementation).  Same arguments, rules and results as the device entry
+ * points, except that every pointer is HOST memory, the call runs
+ * synchronously on the calling thread plus up to `num_threads` worker
+ * threads (<= 0: half the hardware threads; inputs below 2^20 elements run
+ * on one thread), and -- since the host can read the index list -- an index
+ * outside [0, min(rows, mask_rows)) is MI_ERR_BAD_INDICES before anything is
+ * written.  These never touch a GPU and are never used for device memory.
+ */
+mi_status_t mi_apply_bitmask_inplace_host(
+    void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const int32_t *indices, int64_t num_indices,
+    double fill_value, int num_threads);
+
+mi_status_t mi_apply_bitmask_out_host(
+    void *out, int64_t out_row_stride,
+    const void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const int32_t *indices, int64_t num_indices,
+    double fill_value, int num_threads);
+
+/*
  * Host helpers (no device access, usable without a GPU).
  *
  * mi_resolve_vocab_size: the V the apply calls use (XGrammar "Bitmask

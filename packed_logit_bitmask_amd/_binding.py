@@ -23,8 +23,8 @@ VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3}
 
 # every symbol include/mi_bitmask.h declares
 EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",
-           "mi_apply_bitmask_out_ex", "mi_resolve_vocab_size", "mi_fill_value_bits",
-           "mi_status_string", "mi_last_error_message"]
+           "mi_apply_bitmask_out_ex", "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
+           "mi_resolve_vocab_size", "mi_fill_value_bits", "mi_status_string", "mi_last_error_message"]
 
 _i64, _p, _dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
 _INPLACE = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _dbl]
@@ -55,8 +55,11 @@ def load_library(path: Union[str, pathlib.Path, None] = None) -> ctypes.CDLL:
     lib.mi_apply_bitmask_inplace_ex.argtypes = _INPLACE + [ctypes.c_int, _p]
     lib.mi_apply_bitmask_out.argtypes = _OUT + [_p]
     lib.mi_apply_bitmask_out_ex.argtypes = _OUT + [ctypes.c_int, _p]
+    lib.mi_apply_bitmask_inplace_host.argtypes = _INPLACE + [ctypes.c_int]
+    lib.mi_apply_bitmask_out_host.argtypes = _OUT + [ctypes.c_int]
     for f in ("mi_apply_bitmask_inplace", "mi_apply_bitmask_inplace_ex", "mi_apply_bitmask_out",
-              "mi_apply_bitmask_out_ex", "mi_resolve_vocab_size", "mi_fill_value_bits"):
+              "mi_apply_bitmask_out_ex", "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
+              "mi_resolve_vocab_size", "mi_fill_value_bits"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mi_resolve_vocab_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64)]
     lib.mi_fill_value_bits.argtypes = [_dbl, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
@@ -232,4 +235,55 @@ def mi_apply_bitmask_out(logits, mask, out=None, vocab_size: Optional[int] = Non
         check(lib.mi_apply_bitmask_out(*args, st))
     else:
         check(lib.mi_apply_bitmask_out_ex(*args, VARIANT[variant], st))
+    return out
+
+
+# ----------------------------------------------------------------------------
+# host-memory (CPU tensor) entry points
+# ----------------------------------------------------------------------------
+
+def _host_indices(indices):
+    torch = _torch()
+    if indices is None:
+        return None, 0, None
+    t = torch.as_tensor(indices if isinstance(indices, torch.Tensor) else list(indices), dtype=torch.int32)
+    t = t.to("cpu").contiguous().reshape(-1)
+    return (t.data_ptr() if t.numel() else _EMPTY_LIST_PTR), t.numel(), t
+
+
+def mi_apply_bitmask_inplace_host(logits, mask, vocab_size: Optional[int] = None, indices=None,
+                                  fill_value: float = -math.inf, *, num_threads: int = 0):
+    """In-place apply on CPU tensors (native host code, not the GPU kernels)."""
+    if logits.is_cuda or mask.is_cuda:
+        raise ValueError("the host entry point takes CPU tensors only")
+    lib = load_library()
+    L = _as_rows(logits, "logits")
+    M = _as_rows(mask, "bitmask")
+    ip, n, keep = _host_indices(indices)
+    check(lib.mi_apply_bitmask_inplace_host(
+        L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
+        M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
+        -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value), int(num_threads)))
+    del keep
+    return logits
+
+
+def mi_apply_bitmask_out_host(logits, mask, out=None, vocab_size: Optional[int] = None, indices=None,
+                              fill_value: float = -math.inf, *, num_threads: int = 0):
+    """Out-of-place apply on CPU tensors (native host code)."""
+    torch = _torch()
+    if logits.is_cuda or mask.is_cuda or (out is not None and out.is_cuda):
+        raise ValueError("the host entry point takes CPU tensors only")
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(logits, memory_format=torch.contiguous_format)
+    L = _as_rows(logits, "logits")
+    O = _as_rows(out, "out")
+    M = _as_rows(mask, "bitmask")
+    ip, n, keep = _host_indices(indices)
+    check(lib.mi_apply_bitmask_out_host(
+        O.data_ptr(), _row_stride(O), L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1],
+        _row_stride(L), M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
+        -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value), int(num_threads)))
+    del keep
     return out

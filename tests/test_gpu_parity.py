@@ -339,3 +339,18 @@ def test_cross_phase_out_uses_any_alignment():
         wl, _, _ = workloads.random_case(rng, dtype, 5, 777, vocab_size=700)
         for variant in OUT_VARIANTS:
             run_out_case(rng, wl, variant, stride=781, out_stride=779, guard=1, out_guard=6)
+
+
+def test_xgrammar_surface_on_gpu():
+    rng = np.random.default_rng(12)
+    say("[gpu] XGrammar-compatible apply_token_bitmask_inplace on GPU tensors")
+    for dtype in ("float32", "float16", "bfloat16"):
+        wl, _, _ = workloads.random_case(rng, dtype, 6, 1000, mask_cols=34, n_indices=4)
+        want = oracle.apply_inplace(np.array(wl.logits), wl.mask, dtype, 999, list(wl.indices))
+        x = to_device(np.array(wl.logits), dtype).view(6, 1000)
+        m = torch.from_numpy(np.ascontiguousarray(wl.mask)).to("cuda")
+        mb.apply_token_bitmask_inplace(x, m, vocab_size=999, indices=list(wl.indices))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(x, dtype), want)
+    with pytest.raises(ValueError):
+        mb.apply_token_bitmask_inplace(x, m.cpu())          # mixed devices: the caller copies the mask
