@@ -128,6 +128,28 @@ mi_status_t mi_apply_bitmask_out(
     int64_t vocab_size, const int32_t *indices, int64_t num_indices,
     double fill_value, hipStream_t stream);
 
+/*
+ * Gated in-place apply with a per-row report (TensorRT-Edge-LLM "Guided
+ * Decoder": the apply kernel leaves a row whose per-row flag is zero alone;
+ * a row whose mask admits no token is unsatisfiable, rowHasAnyToken).
+ * Rows 0..rows-1 as without indices (mask_rows >= rows).  Leading logits
+ * dimensions such as [activeBatchSize, rowsPerSlot] are flattened rows.
+ *
+ * row_needs_mask: device int8 [rows], or NULL for every row; a zero entry
+ *   leaves that logits row untouched.
+ * row_any_allowed: device uint8 [rows] output, or NULL.  Entry r becomes 1
+ *   when row r still admits at least one of its first V tokens after the
+ *   call -- for a gated-off row that is V > 0; for the others, whether any
+ *   of mask bits [0, V) is set (bits past V never count) -- else 0.  Every
+ *   entry is written; no initialisation is needed.
+ * Neither may overlap logits, mask or each other (MI_ERR_ALIAS).
+ */
+mi_status_t mi_apply_bitmask_rows(
+    void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const int8_t *row_needs_mask, uint8_t *row_any_allowed,
+    double fill_value, hipStream_t stream);
+
 /* As above, with an explicit kernel variant (MI_VARIANT_WRONLY: in place only). */
 mi_status_t mi_apply_bitmask_inplace_ex(
     void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,

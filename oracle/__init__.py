@@ -28,6 +28,13 @@ What the oracle computes, and where each piece comes from:
   where the bit is set, else ``fill_value``.  Where an index list or a vocab
   size leaves part of the output outside the processed region, that part is
   a copy of the input (out-of-place = copy, then the in-place op).
+* ``apply_rows`` -- TensorRT-Edge-LLM "Guided Decoder": the apply kernel
+  leaves a row whose per-row flag is zero alone (``deviceRowNeedsMask``), and
+  a row whose mask admits no token is unsatisfiable (``rowHasAnyToken``,
+  ``fillMasks``' unsatisfiable slots).  Rows with a nonzero flag get the
+  in-place op; the report is, per row, whether any of its first V tokens is
+  still admitted afterwards: for a gated-off row that is simply V > 0 (the
+  row is not masked), for the others whether any of bits [0, V) is set.
 * ``fill_bits`` -- the fill as the dtype's bit pattern: the exact value of
   the double, rounded once to nearest-even in the target format (overflow to
   infinity, NaN to a quiet NaN with the input's sign and no payload).  The
@@ -193,6 +200,9 @@ def _load():
             so = pathlib.Path(tempfile.mkdtemp(prefix="oracle_")) / "_apply_loop.so"
             build_c(so)
     lib = ctypes.CDLL(str(so))
+    lib.oracle_rows_any_allowed.restype = None
+    lib.oracle_rows_any_allowed.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_void_p]
     for name, ctype in (("oracle_apply_u32", ctypes.c_uint32), ("oracle_apply_u16", ctypes.c_uint16)):
         fn = getattr(lib, name)
         fn.restype = None
@@ -243,3 +253,35 @@ def apply_out(logits: np.ndarray, mask: np.ndarray, dtype: str,
     """Out-of-place apply: a fresh [rows, cols] array (copy, then in place)."""
     out = np.array(logits, copy=True, order="C")
     return apply_inplace(out, mask, dtype, vocab_size, indices, fill_value)
+
+
+def rows_any_allowed(mask: np.ndarray, vocab_size: int) -> np.ndarray:
+    """uint8 [mask_rows]: 1 where the row admits a token below ``vocab_size``."""
+    if mask.dtype != np.int32:
+        raise TypeError("bitmask must be int32")
+    out = np.zeros(mask.shape[0], dtype=np.uint8)
+    if mask.shape[0]:
+        _load().oracle_rows_any_allowed(mask.ctypes.data, _row_stride(mask), int(vocab_size), mask.shape[0],
+                                        out.ctypes.data)
+    return out
+
+
+def apply_rows(logits: np.ndarray, mask: np.ndarray, dtype: str, vocab_size: Optional[int] = None,
+               row_needs_mask: Optional[np.ndarray] = None, fill_value: float = -math.inf):
+    """Gated in-place apply plus the per-row report; returns (logits, any_allowed).
+
+    ``row_needs_mask`` is one flag per logits row (None: every row); rows with
+    a zero flag are left alone.  Needs mask_rows >= rows, as without indices.
+    """
+    rows, cols = logits.shape
+    V = resolve_vocab_size(cols, mask.shape[1], vocab_size)
+    if mask.shape[0] < rows:
+        raise ValueError(f"bitmask has {mask.shape[0]} rows for {rows} logits rows")
+    gate = np.ones(rows, dtype=np.int8) if row_needs_mask is None else np.asarray(row_needs_mask).reshape(rows)
+    active = [r for r in range(rows) if gate[r] != 0]
+    apply_inplace(logits, mask, dtype, V, active, fill_value)
+    any_allowed = rows_any_allowed(mask[:rows], V)
+    for r in range(rows):
+        if gate[r] == 0:
+            any_allowed[r] = 1 if V > 0 else 0
+    return logits, any_allowed

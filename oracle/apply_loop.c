@@ -51,3 +51,25 @@ void oracle_apply_u16(uint16_t *logits, int64_t logits_row_stride,
         }
     }
 }
+
+/*
+ * Whether row r's mask admits at least one token below the vocab size
+ * (TensorRT-Edge-LLM "Guided Decoder": a row whose mask admits no token is
+ * unsatisfiable; rowHasAnyToken).  The same bit test as above, token by
+ * token, stopping at the first allowed one.
+ */
+void oracle_rows_any_allowed(const int32_t *mask, int64_t mask_row_stride, int64_t vocab_size,
+                             int64_t rows, uint8_t *out)
+{
+    for (int64_t b = 0; b < rows; ++b) {
+        uint8_t any = 0;
+        for (int64_t j = 0; j < vocab_size; ++j) {
+            uint32_t word = (uint32_t)mask[b * mask_row_stride + j / 32];
+            if ((word >> (j % 32)) & 1u) {
+                any = 1;
+                break;
+            }
+        }
+        out[b] = any;
+    }
+}

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     mi_apply_bitmask_inplace_host,
     mi_apply_bitmask_out,
     mi_apply_bitmask_out_host,
+    mi_apply_bitmask_rows,
     resolve_vocab_size,
 )
 from .xgrammar_api import (  # noqa: F401
@@ -35,7 +36,7 @@ from .xgrammar_api import (  # noqa: F401
 __all__ = [
     "BitmaskError", "EXPORTS", "MI_DTYPE", "VARIANT", "fill_value_bits", "load_library",
     "mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_host",
-    "mi_apply_bitmask_out_host", "resolve_vocab_size",
+    "mi_apply_bitmask_out_host", "mi_apply_bitmask_rows", "resolve_vocab_size",
     "allocate_token_bitmask", "apply_token_bitmask_inplace", "bitmask_dtype", "get_bitmask_shape",
     "reset_token_bitmask",
 ]

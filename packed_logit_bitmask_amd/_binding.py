@@ -23,7 +23,8 @@ VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3}
 
 # every symbol include/mi_bitmask.h declares
 EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",
-           "mi_apply_bitmask_out_ex", "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
+           "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_inplace_host",
+           "mi_apply_bitmask_out_host",
            "mi_resolve_vocab_size", "mi_fill_value_bits", "mi_status_string", "mi_last_error_message"]
 
 _i64, _p, _dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
@@ -55,10 +56,13 @@ def load_library(path: Union[str, pathlib.Path, None] = None) -> ctypes.CDLL:
     lib.mi_apply_bitmask_inplace_ex.argtypes = _INPLACE + [ctypes.c_int, _p]
     lib.mi_apply_bitmask_out.argtypes = _OUT + [_p]
     lib.mi_apply_bitmask_out_ex.argtypes = _OUT + [ctypes.c_int, _p]
+    lib.mi_apply_bitmask_rows.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _p,
+                                          _dbl, _p]
     lib.mi_apply_bitmask_inplace_host.argtypes = _INPLACE + [ctypes.c_int]
     lib.mi_apply_bitmask_out_host.argtypes = _OUT + [ctypes.c_int]
     for f in ("mi_apply_bitmask_inplace", "mi_apply_bitmask_inplace_ex", "mi_apply_bitmask_out",
-              "mi_apply_bitmask_out_ex", "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
+              "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_inplace_host",
+           "mi_apply_bitmask_out_host",
               "mi_resolve_vocab_size", "mi_fill_value_bits"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mi_resolve_vocab_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64)]
@@ -204,6 +208,38 @@ def mi_apply_bitmask_inplace(logits, mask, vocab_size: Optional[int] = None,
     else:
         check(lib.mi_apply_bitmask_inplace_ex(*args, VARIANT[variant], st))
     return logits
+
+
+def mi_apply_bitmask_rows(logits, mask, row_needs_mask=None, vocab_size: Optional[int] = None,
+                          fill_value: float = -math.inf, *, report: bool = False, stream=None):
+    """Gated in-place apply; returns the uint8 per-row report when ``report``.
+
+    TensorRT-Edge-LLM "Guided Decoder": logits may be [activeBatchSize,
+    rowsPerSlot, vocab] (leading dims are flattened into rows); a zero entry
+    of ``row_needs_mask`` (int8/bool, one per row) leaves that row alone.  The
+    report holds 1 where a row still admits one of its first V tokens, 0 for
+    an unsatisfiable row.
+    """
+    torch = _torch()
+    if not logits.is_cuda:
+        raise ValueError("logits must be on the GPU (the library has no CPU path for this call)")
+    lib = load_library()
+    L = _as_rows(logits, "logits")
+    M = _check_mask(mask, logits.device)
+    gate = None
+    if row_needs_mask is not None:
+        gate = row_needs_mask.reshape(-1)
+        if gate.numel() != L.shape[0]:
+            raise ValueError(f"row_needs_mask has {gate.numel()} entries for {L.shape[0]} rows")
+        gate = gate.to(device=logits.device, dtype=torch.int8).contiguous()
+    out = torch.empty(L.shape[0], dtype=torch.uint8, device=logits.device) if report else None
+    _keep_alive(gate, stream)
+    check(lib.mi_apply_bitmask_rows(
+        L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
+        M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M), -1 if vocab_size is None else int(vocab_size),
+        None if gate is None else gate.data_ptr(), None if out is None else out.data_ptr(), float(fill_value),
+        _stream_handle(logits.device, stream)))
+    return out
 
 
 def mi_apply_bitmask_out(logits, mask, out=None, vocab_size: Optional[int] = None,

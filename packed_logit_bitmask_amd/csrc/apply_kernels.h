@@ -66,17 +66,48 @@ __device__ __forceinline__ void store16(Rsrc r, int32_t byte_off, uint4 v) {
 
 // Slot -> row.  Without an index list the slot is the row.  With one, an
 // entry outside [0, row_limit) is skipped: the host cannot check device
-// memory, so the kernel defines that case as "no write".
+// memory, so the kernel defines that case as "no write".  An optional
+// per-row gate (one byte per row; TensorRT-Edge-LLM "Guided Decoder": the
+// apply leaves a row whose flag is zero alone) turns rows off.
 struct RowMap {
   const int32_t* indices;
   int64_t row_limit;
+  const int8_t* gate = nullptr;
 
   __device__ __forceinline__ bool row(int64_t slot, int64_t* r) const {
     const int64_t v = indices ? static_cast<int64_t>(indices[slot]) : slot;
     *r = v;
     return v >= 0 && v < row_limit;
   }
+  __device__ __forceinline__ bool gated_off(int64_t r) const { return gate && gate[r] == 0; }
 };
+
+// Per-row report for the gated apply: 1 when row r still admits one of its
+// first V tokens (TensorRT-Edge-LLM "Guided Decoder": rowHasAnyToken; an
+// all-zero row is unsatisfiable).  A gated-off row is not masked, so it
+// admits a token whenever V > 0.  Called by every thread of the row's first
+// block (it ends with a block barrier); one thread writes the byte, so no
+// atomics and no prior initialisation are needed.  Bits past V in the last
+// word are masked off; words past it are never read.
+__device__ __forceinline__ void report_row(const uint32_t* __restrict__ mrow, int32_t V, int32_t W,
+                                           bool gated_off, uint8_t* __restrict__ out_r) {
+  constexpr int kBatch = 8;  // loads in flight per thread
+  uint32_t acc = 0;
+  if (!gated_off) {
+    const Rsrc rm = make_rsrc(mrow, static_cast<uint32_t>(W) * 4u);
+    const uint32_t tail = (V & 31) ? (1u << (V & 31)) - 1u : 0xFFFFFFFFu;
+    const int t = static_cast<int>(threadIdx.x);
+    for (int32_t base = 0; base < W; base += kBlock * kBatch) {
+      uint32_t w[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) w[k] = load_word(rm, (base + k * kBlock + t) * 4);  // past W: 0
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) acc |= (base + k * kBlock + t == W - 1) ? (w[k] & tail) : w[k];
+    }
+  }
+  const int any = __syncthreads_or(acc != 0u);
+  if (threadIdx.x == 0) *out_r = gated_off ? static_cast<uint8_t>(V > 0) : static_cast<uint8_t>(any != 0);
+}
 
 template <typename T>
 struct Bits16B {
@@ -134,7 +165,7 @@ __global__ __launch_bounds__(kBlock) void inplace_scalar(
   const int64_t slot = slot_base + blockIdx.x / chunks;
   const int32_t chunk = static_cast<int32_t>(blockIdx.x % chunks);
   int64_t r;
-  if (!map.row(slot, &r)) return;
+  if (!map.row(slot, &r) || map.gated_off(r)) return;
   T* __restrict__ row = logits + r * ls;
   const uint32_t* __restrict__ mrow = mask + r * ms;
   const int32_t j0 = chunk * (kBlock * 8) + static_cast<int32_t>(threadIdx.x);
@@ -161,15 +192,18 @@ __global__ __launch_bounds__(kBlock) void inplace_scalar(
 template <typename T, int U, int POLICY>
 __global__ __launch_bounds__(kBlock) void inplace_vec(
     T* __restrict__ logits, int64_t ls, const uint32_t* __restrict__ mask, int64_t ms,
-    int32_t V, int32_t W, RowMap map, int64_t slot_base, uint32_t chunks, T fill) {
+    int32_t V, int32_t W, RowMap map, int64_t slot_base, uint32_t chunks, T fill,
+    uint8_t* __restrict__ any_out) {
   constexpr int VW = Bits16B<T>::VW;
   constexpr uint32_t FULL = Bits16B<T>::FULL;
   const int64_t slot = slot_base + blockIdx.x / chunks;
   const int32_t chunk = static_cast<int32_t>(blockIdx.x % chunks);
   int64_t r;
   if (!map.row(slot, &r)) return;
-  T* __restrict__ row = logits + r * ls;
   const uint32_t* __restrict__ mrow = mask + r * ms;
+  if (any_out && chunk == 0) report_row(mrow, V, W, map.gated_off(r), any_out + r);
+  if (map.gated_off(r)) return;
+  T* __restrict__ row = logits + r * ls;
 
   const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);
   int32_t h = static_cast<int32_t>(((16u - mis) & 15u) / sizeof(T));
@@ -246,7 +280,7 @@ __global__ __launch_bounds__(kBlock) void inplace_wronly(
   const int64_t slot = slot_base + blockIdx.x / chunks;
   const int32_t chunk = static_cast<int32_t>(blockIdx.x % chunks);
   int64_t r;
-  if (!map.row(slot, &r)) return;
+  if (!map.row(slot, &r) || map.gated_off(r)) return;
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int wave = static_cast<int>(threadIdx.x) >> 6;
   const int32_t wbase = chunk * 256 + wave * 64;

@@ -229,10 +229,11 @@ mi_status_t launch_slots(int64_t slots, int64_t chunks, Launch&& launch) {
 
 template <typename T>
 mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64_t ms, const int32_t* indices,
-                        const Plan& p, mi_variant_t variant, hipStream_t stream) {
+                        const Plan& p, mi_variant_t variant, hipStream_t stream, const int8_t* gate = nullptr,
+                        uint8_t* any_out = nullptr) {
   T* logits = static_cast<T*>(logits_v);
   const uint32_t* mask = reinterpret_cast<const uint32_t*>(mask_i);
-  const mi::RowMap map{indices, p.row_limit};
+  const mi::RowMap map{indices, p.row_limit, gate};
   const T fill = static_cast<T>(p.fill);
   const int32_t V = static_cast<int32_t>(p.V), W = static_cast<int32_t>(p.W);
   (void)hipGetLastError();  // report only what this call's launches raise
@@ -252,7 +253,7 @@ mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64
       launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
 #define MI_INPLACE_VEC(UNROLL, POLICY)                                                            \
   mi::inplace_vec<T, UNROLL, POLICY><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, W, map, s0, \
-                                                                        ch, fill)
+                                                                        ch, fill, any_out)
         if (shape.unroll == 2) MI_INPLACE_VEC(2, mi::kStoreDevice);
         else if (shape.unroll == 1) MI_INPLACE_VEC(1, mi::kStoreDeviceStream);
         else MI_INPLACE_VEC(4, mi::kStoreDeviceStream);
@@ -362,7 +363,36 @@ mi_status_t out_impl(void* out, int64_t os, const void* logits, mi_dtype_t dtype
                       : run_inplace<uint16_t>(out, os, mask, ms, indices, p, iv, stream);
 }
 
+mi_status_t rows_impl(void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t ls, const int32_t* mask,
+                      int64_t mask_rows, int64_t mask_cols, int64_t ms, int64_t vocab_size, const int8_t* gate,
+                      uint8_t* any_out, double fill_value, hipStream_t stream) {
+  Plan p;
+  mi_status_t st = check_common(logits, dtype, rows, cols, ls, mask, mask_rows, mask_cols, ms, vocab_size, nullptr,
+                                0, fill_value, &p);
+  if (st != MI_OK) return st;
+  ByteRange gb, ab;
+  if (!extent(gate, gate ? 1 : 0, rows, rows, 1, &gb) || !extent(any_out, any_out ? 1 : 0, rows, rows, 1, &ab))
+    return fail(MI_ERR_BAD_SHAPE, "row flag extent overflows");
+  if (overlaps(p.mask, p.logits)) return fail(MI_ERR_ALIAS, "mask overlaps logits");
+  if (overlaps(gb, p.logits)) return fail(MI_ERR_ALIAS, "row_needs_mask overlaps logits");
+  if (overlaps(ab, p.logits) || overlaps(ab, p.mask) || overlaps(ab, gb))
+    return fail(MI_ERR_ALIAS, "row_any_allowed overlaps an input");
+  if (p.R == 0 || (p.V == 0 && !any_out)) return MI_OK;
+  // The per-row report lives in the vector kernel (its first block per row).
+  if (p.esize == 4) return run_inplace<uint32_t>(logits, ls, mask, ms, nullptr, p, MI_VARIANT_VEC, stream, gate, any_out);
+  return run_inplace<uint16_t>(logits, ls, mask, ms, nullptr, p, MI_VARIANT_VEC, stream, gate, any_out);
+}
+
 }  // namespace
+
+MI_API mi_status_t mi_apply_bitmask_rows(void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                                         int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
+                                         int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
+                                         const int8_t* row_needs_mask, uint8_t* row_any_allowed, double fill_value,
+                                         hipStream_t stream) {
+  return rows_impl(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
+                   vocab_size, row_needs_mask, row_any_allowed, fill_value, stream);
+}
 
 MI_API mi_status_t mi_apply_bitmask_inplace(void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
                                             int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,

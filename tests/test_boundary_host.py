@@ -202,3 +202,30 @@ def test_binding_rejects_cpu_tensors_and_bad_indices():
         mb.mi_apply_bitmask_inplace(x, m)
     with pytest.raises(ValueError):
         mb.mi_apply_bitmask_out(x, m)
+
+
+def rows_call(**kw):
+    a = dict(logits=LOGITS, dtype=2, rows=4, cols=100, ls=100, mask=MASK, mask_rows=4, mask_cols=4, ms=4,
+             vocab=-1, gate=None, out=None, fill=-math.inf)
+    a.update(kw)
+    return mb.load_library().mi_apply_bitmask_rows(
+        a["logits"], a["dtype"], a["rows"], a["cols"], a["ls"], a["mask"], a["mask_rows"], a["mask_cols"],
+        a["ms"], a["vocab"], a["gate"], a["out"], a["fill"], None)
+
+
+REJECT_ROWS = [
+    ("null logits", dict(logits=None), NULLP),
+    ("too few mask rows", dict(mask_rows=3), SHAPE),
+    ("vocab too large", dict(vocab=129), VOCAB),
+    ("gate inside logits", dict(gate=LOGITS + 10), ALIAS),
+    ("report inside logits", dict(out=LOGITS + 100), ALIAS),
+    ("report inside mask", dict(out=MASK + 8), ALIAS),
+    ("report overlaps gate", dict(gate=OUT, out=OUT + 2), ALIAS),
+    ("mask inside logits", dict(mask=LOGITS + 64), ALIAS),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", REJECT_ROWS, ids=[r[0] for r in REJECT_ROWS])
+def test_rows_rejections(name, kw, code):
+    assert rows_call(**kw) == code
+    assert mb.load_library().mi_last_error_message().decode()

@@ -354,3 +354,78 @@ def test_xgrammar_surface_on_gpu():
         assert np.array_equal(to_host(x, dtype), want)
     with pytest.raises(ValueError):
         mb.apply_token_bitmask_inplace(x, m.cpu())          # mixed devices: the caller copies the mask
+
+
+# ----------------------------------------------------------------------------
+# gated apply with the per-row report
+# ----------------------------------------------------------------------------
+
+def run_rows_case(rng, logits_bits, mask, dtype, vocab, gate, *, stride=None, shape3=None, report=True):
+    rows, cols = logits_bits.shape
+    stride = cols if stride is None else stride
+    P = Placed(rng, logits_bits, dtype, stride, 4)
+    hmask, dmask = place_mask(rng, mask, mask.shape[1] + 1, 2)
+    want = P.host.copy()
+    _, want_rep = oracle.apply_rows(P.view(want), hmask, dtype, vocab, gate, -math.inf)
+    dl = P.device()
+    if shape3 is not None:
+        dl = P.dev[P.guard:P.guard + rows * stride].view(shape3[0], shape3[1], stride)[:, :, :cols]
+    g = None if gate is None else torch.from_numpy(np.asarray(gate, dtype=np.int8)).to("cuda")
+    rep = mb.mi_apply_bitmask_rows(dl, dmask, g, vocab, report=report)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(P.dev, dtype), want)
+    if report:
+        assert rep.cpu().numpy().tolist() == want_rep.tolist()
+
+
+def test_rows_hand_cases_on_gpu():
+    from _golden import build_case, load
+    say("[gpu] gated apply: hand cases")
+    for case in load()["rows_cases"]["cases"]:
+        logits, mask = build_case(case)
+        gate = None if case["gate"] is None else np.array(case["gate"], dtype=np.int8)
+        run_rows_case(np.random.default_rng(0), logits, mask, case["dtype"], case["vocab_size"], gate)
+
+
+def test_rows_verify_shape_with_gate_and_report():
+    rng = np.random.default_rng(13)
+    say("[gpu] gated apply: verify_fp16 shape as [256,4,32000] with random gate")
+    wl = workloads.verify_fp16()
+    gate = (rng.random(wl.rows) < 0.8).astype(np.int8)
+    run_rows_case(rng, wl.logits, wl.mask, wl.dtype, None, gate, shape3=(256, 4))
+    run_rows_case(rng, wl.logits, wl.mask, wl.dtype, None, None)
+    run_rows_case(rng, wl.logits, wl.mask, wl.dtype, None, np.zeros(wl.rows, np.int8))
+    run_rows_case(rng, wl.logits, wl.mask, wl.dtype, 0, gate)
+
+
+@pytest.mark.parametrize("name", ["tail_bf16", "mixed_bf16", "tiny"])
+def test_rows_named_with_garbage_tails(name):
+    rng = np.random.default_rng(14)
+    say(f"[gpu] gated apply: {name}")
+    wl = workloads.NAMED[name]()
+    gate = (rng.random(wl.rows) < 0.5).astype(np.int8)
+    # zero the in-range bits of some rows so they are unsatisfiable; garbage past V stays
+    V = oracle.resolve_vocab_size(wl.cols, wl.mask.shape[1], wl.vocab_size)
+    mask = wl.mask.copy().view(np.uint32)
+    W, t = (V + 31) // 32, V % 32
+    for r in range(0, wl.rows, 3):
+        mask[r, :W - (1 if t else 0)] = 0
+        if t:
+            mask[r, W - 1] &= np.uint32((0xFFFFFFFF << t) & 0xFFFFFFFF)
+    run_rows_case(rng, wl.logits, mask.view(np.int32), wl.dtype, wl.vocab_size, gate, stride=wl.cols + 5)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_rows_fuzz(seed):
+    rng = np.random.default_rng(2000 + seed)
+    dtype = ["float32", "float16", "bfloat16"][seed % 3]
+    rows = int(rng.integers(1, 30))
+    cols = int(rng.choice([5, 33, 100, 1000, 4097, 20000]))
+    mask_cols = (cols + 31) // 32 + int(rng.integers(0, 2))
+    wl, _, _ = workloads.random_case(rng, dtype, rows, cols, mask_cols=mask_cols,
+                                     density=float(rng.choice([0.0, 0.001, 0.5])))
+    vocab = [None, int(rng.integers(0, min(cols, 32 * mask_cols) + 1))][seed % 2]
+    gate = None if seed % 4 == 0 else (rng.random(rows) < 0.6).astype(np.int8)
+    say(f"[gpu] gated fuzz seed={seed} {dtype} [{rows},{cols}] vocab={vocab}")
+    run_rows_case(rng, wl.logits, wl.mask, dtype, vocab, gate, stride=cols + int(rng.integers(0, 9)),
+                  report=seed % 3 != 0)
