@@ -186,6 +186,9 @@ def main():
             per[var] = {"ms_per_step": t, "GBps": eff / (t * 1e-3) / 1e9}
         extras["variants_cold"] = per
         extras["ceiling_cold"] = ceilings(torch, dev, eff, nsets, args.steps, stream)
+        extras["gated_rows_cold"] = gated_rows(torch, dev, mb, workloads, args.steps, stream)
+        extras["host_path"] = host_path(torch, mb, wl, eff)
+        extras["mask_upload_overlap"] = upload_overlap(torch, dev, mb, wl)
 
     cpu = cpu_baseline(wl, eff, args.cpu_seconds)
 
@@ -258,6 +261,129 @@ def ceilings(torch, dev, eff, nsets, steps, stream):
         out[name] = {"bytes_per_step": eff, "ms_per_step": ms, "GBps": eff / (ms * 1e-3) / 1e9}
         del g
     return out
+
+
+def graph_ms(torch, fn, steps, stream, warmup=10):
+    with torch.cuda.stream(stream):
+        for k in range(warmup):
+            fn(k)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for k in range(steps):
+            fn(k)
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    del g
+    return ms
+
+
+def gated_rows(torch, dev, mb, workloads, steps, stream):
+    """Gated apply with the per-row report on the speculative-verify shape.
+
+    fp16 logits [256 slots, 4 rows, 32000] applied in place with 80 % of the
+    rows flagged, against the plain in-place apply given the same rows as an
+    index list; both cold (rotating buffer sets).
+    """
+    import numpy as np
+
+    wl = workloads.verify_fp16()
+    rng = np.random.default_rng(6)
+    gate = (rng.random(wl.rows) < 0.8).astype(np.int8)
+    active = np.flatnonzero(gate).astype(np.int32)
+    W = (wl.cols + 31) // 32
+    eff = len(active) * (W * 4 + wl.cols * 2)
+    nsets = max(2, math.ceil(2 * INFINITY_CACHE / (wl.logits.nbytes + wl.mask.nbytes)))
+    sets = [(torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(torch.float16).view(256, 4, wl.cols),
+             torch.from_numpy(wl.mask).to(dev)) for _ in range(nsets)]
+    g = torch.from_numpy(gate).to(dev)
+    idx = torch.from_numpy(active).to(dev)
+    t_rep = graph_ms(torch, lambda k: mb.mi_apply_bitmask_rows(sets[k % nsets][0], sets[k % nsets][1], g,
+                                                               report=True), steps, stream)
+    t_gate = graph_ms(torch, lambda k: mb.mi_apply_bitmask_rows(sets[k % nsets][0], sets[k % nsets][1], g),
+                      steps, stream)
+    t_idx = graph_ms(torch, lambda k: mb.mi_apply_bitmask_inplace(sets[k % nsets][0], sets[k % nsets][1], None,
+                                                                  idx), steps, stream)
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": f"fp16 [256,4,32000] in place, {len(active)} of 1024 rows flagged",
+            "effective_bytes": eff,
+            "gated_with_report": {"ms_per_step": t_rep, "GBps": eff / (t_rep * 1e-3) / 1e9},
+            "gated": {"ms_per_step": t_gate, "GBps": eff / (t_gate * 1e-3) / 1e9},
+            "index_list_same_rows": {"ms_per_step": t_idx, "GBps": eff / (t_idx * 1e-3) / 1e9}}
+
+
+def upload_overlap(torch, dev, mb, wl, steps=30):
+    """A decode step with the mask uploaded on the compute stream vs behind the forward.
+
+    Per step: a bf16 GEMM [256, 8192] x [8192, 32000] stands in for the
+    forward pass, the 256 x 4008 int32 mask (4.1 MB, already filled in pinned
+    host memory) goes host -> device, and the apply runs on the GEMM's
+    output.  "serial" copies the mask on the compute stream before the apply;
+    "staged" uses MaskStager: the copy runs on a side stream while the GEMM
+    runs.  Times are per step (HIP events on the compute stream).
+    """
+    import numpy as np
+
+    B = 256
+    a = torch.randn(B, 8192, device=dev, dtype=torch.bfloat16)
+    w = torch.randn(8192, 32000, device=dev, dtype=torch.bfloat16)
+    logits = torch.empty(B, 32000, device=dev, dtype=torch.bfloat16)
+    host = torch.from_numpy(wl.mask).pin_memory()
+    dmask = torch.empty_like(host, device=dev)
+    stager = mb.MaskStager(B, 32 * wl.mask.shape[1], device=dev, depth=2)
+    for _ in range(stager.depth):          # the grammar engine's host fill is not timed here
+        stager.host().copy_(host)
+    compute = torch.cuda.Stream()
+    out = {}
+    for mode in ("serial", "staged", "gemm_only"):
+        for rep in range(2):   # first pass warms up
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            s.record(compute)
+            with torch.cuda.stream(compute):
+                for _ in range(steps):
+                    if mode == "staged":
+                        stager.host()
+                        stager.upload()
+                    torch.mm(a, w, out=logits)
+                    if mode == "serial":
+                        dmask.copy_(host, non_blocking=True)
+                        mb.mi_apply_bitmask_inplace(logits, dmask, 32000, None)
+                    elif mode == "staged":
+                        stager.apply_inplace(logits, 32000, None, stream=compute)
+            e.record(compute)
+            torch.cuda.synchronize()
+        out[mode] = {"ms_per_step": s.elapsed_time(e) / steps}
+    return {"what": "per decode step: bf16 GEMM [256,8192]x[8192,32000], 4.1 MB mask upload, apply",
+            **out}
+
+
+def host_path(torch, mb, wl, eff, seconds=2.0):
+    """The library's native host-memory apply (CPU tensors) on the same workload."""
+    import numpy as np
+
+    x = torch.from_numpy(wl.logits.copy().view(np.int16)).view(torch.bfloat16)
+    m = torch.from_numpy(wl.mask)
+    idx = list(wl.indices)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        mb.mi_apply_bitmask_inplace_host(x, m, wl.vocab_size, idx)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max(1, (os.cpu_count() or 2) // 2)
+    return {"GBps": eff * passes / el / 1e9, "passes": passes, "threads": threads,
+            "note": "native C++ host entry point (not the oracle), default thread count"}
 
 
 def cpu_baseline(wl, eff, seconds):

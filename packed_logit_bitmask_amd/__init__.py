@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     mi_apply_bitmask_rows,
     resolve_vocab_size,
 )
+from .staging import MaskStager  # noqa: F401
 from .xgrammar_api import (  # noqa: F401
     allocate_token_bitmask,
     apply_token_bitmask_inplace,
@@ -38,5 +39,5 @@ __all__ = [
     "mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_host",
     "mi_apply_bitmask_out_host", "mi_apply_bitmask_rows", "resolve_vocab_size",
     "allocate_token_bitmask", "apply_token_bitmask_inplace", "bitmask_dtype", "get_bitmask_shape",
-    "reset_token_bitmask",
+    "reset_token_bitmask", "MaskStager",
 ]

@@ -85,10 +85,11 @@ struct RowMap {
 // Per-row report for the gated apply: 1 when row r still admits one of its
 // first V tokens (TensorRT-Edge-LLM "Guided Decoder": rowHasAnyToken; an
 // all-zero row is unsatisfiable).  A gated-off row is not masked, so it
-// admits a token whenever V > 0.  Called by every thread of the row's first
-// block (it ends with a block barrier); one thread writes the byte, so no
+// admits a token whenever V > 0.  Called by every thread of one block (it
+// ends with a block barrier); one thread writes the byte, so no
 // atomics and no prior initialisation are needed.  Bits past V in the last
-// word are masked off; words past it are never read.
+// word are masked off; words past it are never read.  The apply runs it in
+// blocks of their own, one per row, alongside the apply blocks.
 __device__ __forceinline__ void report_row(const uint32_t* __restrict__ mrow, int32_t V, int32_t W,
                                            bool gated_off, uint8_t* __restrict__ out_r) {
   constexpr int kBatch = 8;  // loads in flight per thread
@@ -193,16 +194,22 @@ template <typename T, int U, int POLICY>
 __global__ __launch_bounds__(kBlock) void inplace_vec(
     T* __restrict__ logits, int64_t ls, const uint32_t* __restrict__ mask, int64_t ms,
     int32_t V, int32_t W, RowMap map, int64_t slot_base, uint32_t chunks, T fill,
-    uint8_t* __restrict__ any_out) {
+    uint8_t* __restrict__ any_out, uint32_t nrep) {
   constexpr int VW = Bits16B<T>::VW;
   constexpr uint32_t FULL = Bits16B<T>::FULL;
-  const int64_t slot = slot_base + blockIdx.x / chunks;
-  const int32_t chunk = static_cast<int32_t>(blockIdx.x % chunks);
+  // With a per-row report, the first `nrep` blocks of the grid are report
+  // blocks, one per slot; they run beside the apply blocks, not before them.
+  if (blockIdx.x < nrep) {
+    int64_t rr;
+    if (map.row(slot_base + blockIdx.x, &rr)) report_row(mask + rr * ms, V, W, map.gated_off(rr), any_out + rr);
+    return;
+  }
+  const uint32_t b = blockIdx.x - nrep;
+  const int64_t slot = slot_base + b / chunks;
+  const int32_t chunk = static_cast<int32_t>(b % chunks);
   int64_t r;
-  if (!map.row(slot, &r)) return;
+  if (!map.row(slot, &r) || map.gated_off(r)) return;
   const uint32_t* __restrict__ mrow = mask + r * ms;
-  if (any_out && chunk == 0) report_row(mrow, V, W, map.gated_off(r), any_out + r);
-  if (map.gated_off(r)) return;
   T* __restrict__ row = logits + r * ls;
 
   const uint32_t mis = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(row) & 15u);

@@ -217,12 +217,18 @@ mi_status_t after_launch(const char* what) {
   return MI_OK;
 }
 
+// Launch over `slots` row slots, `chunks` blocks per slot, splitting into
+// several launches when one grid would be too large.  With `extra_per_slot`
+// set, each launch also carries one extra block per slot (the per-row report
+// blocks, placed first); launch() gets (first slot, blocks, chunks, extra).
 template <typename Launch>
-mi_status_t launch_slots(int64_t slots, int64_t chunks, Launch&& launch) {
-  const int64_t per = std::max<int64_t>(1, kMaxBlocksPerLaunch / chunks);
+mi_status_t launch_slots(int64_t slots, int64_t chunks, Launch&& launch, bool extra_per_slot = false) {
+  const int64_t per_slot = chunks + (extra_per_slot ? 1 : 0);
+  const int64_t per = std::max<int64_t>(1, kMaxBlocksPerLaunch / per_slot);
   for (int64_t s0 = 0; s0 < slots; s0 += per) {
     const int64_t n = std::min(per, slots - s0);
-    launch(s0, static_cast<uint32_t>(n * chunks), static_cast<uint32_t>(chunks));
+    launch(s0, static_cast<uint32_t>(n * per_slot), static_cast<uint32_t>(chunks),
+           static_cast<uint32_t>(extra_per_slot ? n : 0));
   }
   return MI_OK;
 }
@@ -240,7 +246,7 @@ mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64
   switch (variant) {
     case MI_VARIANT_SCALAR: {
       const int64_t chunks = (p.V + mi::kBlock * 8 - 1) / (mi::kBlock * 8);
-      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t) {
         mi::inplace_scalar<T><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, map, s0, ch, fill);
       });
       return after_launch("inplace_scalar");
@@ -250,20 +256,20 @@ mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64
       const VecShape shape = inplace_shape(sizeof(T), p.R * p.V * static_cast<int64_t>(sizeof(T)));
       const int64_t per = int64_t(mi::kBlock) * shape.unroll;
       const int64_t chunks = std::max<int64_t>(1, (p.V / VW + per - 1) / per);
-      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t nrep) {
 #define MI_INPLACE_VEC(UNROLL, POLICY)                                                            \
   mi::inplace_vec<T, UNROLL, POLICY><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, W, map, s0, \
-                                                                        ch, fill, any_out)
+                                                                        ch, fill, any_out, nrep)
         if (shape.unroll == 2) MI_INPLACE_VEC(2, mi::kStoreDevice);
         else if (shape.unroll == 1) MI_INPLACE_VEC(1, mi::kStoreDeviceStream);
         else MI_INPLACE_VEC(4, mi::kStoreDeviceStream);
 #undef MI_INPLACE_VEC
-      });
+      }, any_out != nullptr);
       return after_launch("inplace_vec");
     }
     case MI_VARIANT_WRONLY: {
       const int64_t chunks = (p.W + 255) / 256;
-      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t) {
         mi::inplace_wronly<T><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, W, map, s0, ch, fill);
       });
       return after_launch("inplace_wronly");
@@ -287,14 +293,14 @@ mi_status_t run_out(void* out_v, int64_t os, const void* in_v, int64_t ls, const
     constexpr int VW = mi::Bits16B<T>::VW;
     const int64_t per = int64_t(mi::kBlock) * kOutShape.unroll;
     const int64_t chunks = std::max<int64_t>(1, (cols / VW + per - 1) / per);
-    launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+    launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t) {
       mi::out_vec<T, kOutShape.unroll, kOutShape.policy><<<blocks, mi::kBlock, 0, stream>>>(
           out, os, in, ls, mask, ms, V, W, C, apply, s0, ch, fill);
     });
     return after_launch("out_vec");
   }
   const int64_t chunks = (cols + mi::kBlock * 8 - 1) / (mi::kBlock * 8);
-  launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch) {
+  launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t) {
     mi::out_scalar<T><<<blocks, mi::kBlock, 0, stream>>>(out, os, in, ls, mask, ms, V, C, apply, s0, ch, fill);
   });
   return after_launch("out_scalar");

@@ -429,3 +429,36 @@ def test_rows_fuzz(seed):
     say(f"[gpu] gated fuzz seed={seed} {dtype} [{rows},{cols}] vocab={vocab}")
     run_rows_case(rng, wl.logits, wl.mask, dtype, vocab, gate, stride=cols + int(rng.integers(0, 9)),
                   report=seed % 3 != 0)
+
+
+# ----------------------------------------------------------------------------
+# mask staging: host fill -> async upload on a side stream -> apply
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("depth", [1, 2, 3])
+def test_staged_decode_loop(depth):
+    say(f"[gpu] MaskStager depth={depth}")
+    rng = np.random.default_rng(40 + depth)
+    B, V, cols = 16, 5000, 5024
+    stager = mb.MaskStager(B, V, depth=depth)
+    compute = torch.cuda.Stream()
+    w = torch.randn(256, cols, device="cuda", dtype=torch.float16)
+    results = []
+    with torch.cuda.stream(compute):
+        for step in range(7):
+            h = stager.host()
+            bits = rng.random((B, V)) < rng.uniform(0.05, 0.9)
+            mask_np = workloads.pack_allowed(bits, h.shape[1], rng)
+            h.copy_(torch.from_numpy(mask_np))
+            stager.upload()
+            # the "forward": logits produced on the compute stream while the mask uploads
+            a = torch.randn(B, 256, device="cuda", dtype=torch.float16)
+            logits = a @ w
+            keep_in = logits.clone()
+            stager.apply_inplace(logits, vocab_size=V, stream=compute)
+            results.append((keep_in, logits, mask_np))
+    torch.cuda.synchronize()
+    for step, (before, after, mask_np) in enumerate(results):
+        src = before.view(torch.int16).cpu().numpy().view(np.uint16)
+        want = oracle.apply_inplace(src.copy(), mask_np, "float16", V)
+        assert np.array_equal(after.view(torch.int16).cpu().numpy().view(np.uint16), want), step
