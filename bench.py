@@ -189,6 +189,7 @@ def main():
         extras["gated_rows_cold"] = gated_rows(torch, dev, mb, workloads, args.steps, stream)
         extras["host_path"] = host_path(torch, mb, wl, eff)
         extras["mask_upload_overlap"] = upload_overlap(torch, dev, mb, wl)
+        extras["fused_sampler_cold"] = sampler_times(torch, dev, mb, workloads, stream)
 
     cpu = cpu_baseline(wl, eff, args.cpu_seconds)
 
@@ -365,6 +366,40 @@ def upload_overlap(torch, dev, mb, wl, steps=30):
         out[mode] = {"ms_per_step": s.elapsed_time(e) / steps}
     return {"what": "per decode step: bf16 GEMM [256,8192]x[8192,32000], 4.1 MB mask upload, apply",
             **out}
+
+
+def sampler_times(torch, dev, mb, workloads, stream, steps=200):
+    """The fused apply + sampler at the two batch/vocab shapes the logits-processor page times.
+
+    Per launch: one token per row from the masked logits.  Bytes counted: one
+    read of the logits of every row plus its mask words; the kernel reads the
+    row once per pass (1 pass greedy / unfiltered, 5-6 with top-k or top-p).
+    Cold: rotating buffer sets.
+    """
+    import numpy as np
+
+    out = {}
+    for label, wl in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0)),
+                      ("B1024_V32000_fp16", workloads.verify_fp16())):
+        R, V = wl.rows, (wl.vocab_size or wl.cols)
+        nbytes = R * V * (2) + R * ((V + 31) // 32) * 4
+        nsets = max(2, math.ceil(2 * INFINITY_CACHE / (wl.logits.nbytes + wl.mask.nbytes)))
+        tdt = torch.bfloat16 if wl.dtype == "bfloat16" else torch.float16
+        sets = [(torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(tdt), torch.from_numpy(wl.mask).to(dev))
+                for _ in range(nsets)]
+        tok = torch.empty(R, dtype=torch.int64, device=dev)
+        res = {}
+        for mode, kw in (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperature=1.0)),
+                         ("top_p_0.9", dict(top_p=0.9)), ("top_k_50", dict(top_k=50)),
+                         ("top_k_50_top_p_0.9_min_p_0.05", dict(top_k=50, top_p=0.9, min_p=0.05))):
+            ms = graph_ms(torch, lambda k, kw=kw: mb.mi_apply_bitmask_sample(
+                sets[k % nsets][0], sets[k % nsets][1], wl.vocab_size, seed=1, offset=k, out=tok, **kw),
+                steps, stream)
+            res[mode] = {"us_per_call": ms * 1e3, "GBps_one_read": nbytes / (ms * 1e-3) / 1e9}
+        out[label] = res
+        del sets
+        torch.cuda.empty_cache()
+    return out
 
 
 def host_path(torch, mb, wl, eff, seconds=2.0):

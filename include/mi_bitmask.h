@@ -165,6 +165,52 @@ mi_status_t mi_apply_bitmask_out_ex(
     double fill_value, mi_variant_t variant, hipStream_t stream);
 
 /*
+ * Fused apply + sample: one token per row (logits-processor page, "Ops:
+ * sample" and "How it works").  Per row: z = logit / temperature; top-k,
+ * top-p and min-p each keep the largest-probability tokens above a cutoff
+ * (k <= 0, p >= 1, m <= 0 disable them; ties at a cutoff are kept) and the
+ * kept set is their intersection; one token is drawn from it with
+ * probability proportional to its softmax probability (Gumbel-max).
+ * temperature <= 0 takes the argmax (lowest index on ties).
+ *
+ * Candidates are the tokens v < V whose logit is finite and, when mask is
+ * not NULL, whose bit v % 32 of word mask[row, v / 32] is set -- the apply
+ * is folded into the reads and the logits are not modified; a masked token
+ * is never drawn.  With a mask the vocab-size rule and mask_rows >= rows
+ * are those of the apply; without one (mask == NULL, mask_* ignored)
+ * V = vocab_size, or cols when vocab_size == -1.  A row with no candidate
+ * gets token -1.
+ *
+ * Randomness: Philox4x32-10 (Salmon et al., SC 2011) with key (seed low,
+ * seed high) and, for token v of row r, counter (v / 4, r, offset low,
+ * offset high), word v % 4; u = (floor(x / 2^9) + 1/2) / 2^23; Gumbel
+ * variate -ln(-ln u).  The same (seed, offset) replays the same tokens;
+ * advance offset (or seed) per decoding step.
+ *
+ * params: HOST struct.  Each per-row array is a device array of `rows`
+ * entries, or NULL to use the matching *_all value for every row.
+ * tokens: device int64 [rows] output (8-byte aligned; may not overlap logits
+ * or mask).  Asynchronous on `stream` like the apply calls.
+ */
+typedef struct mi_sample_params {
+    const float *temperature;     /* device [rows] or NULL */
+    const int32_t *top_k;         /* device [rows] or NULL */
+    const float *top_p;           /* device [rows] or NULL */
+    const float *min_p;           /* device [rows] or NULL */
+    float temperature_all;
+    int32_t top_k_all;
+    float top_p_all;
+    float min_p_all;
+    uint64_t seed;
+    uint64_t offset;
+} mi_sample_params_t;
+
+mi_status_t mi_apply_bitmask_sample(
+    const void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const mi_sample_params_t *params, int64_t *tokens, hipStream_t stream);
+
+/*
  * Host-memory apply, for logits and masks that live on the CPU (XGrammar
  * "Bitmask Operations", Notes: Device: CPU tensors get a CPU
  * implementation).  Same arguments, rules and results as the device entry

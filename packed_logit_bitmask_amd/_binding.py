@@ -23,8 +23,8 @@ VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3}
 
 # every symbol include/mi_bitmask.h declares
 EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",
-           "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_inplace_host",
-           "mi_apply_bitmask_out_host",
+           "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample",
+           "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
            "mi_resolve_vocab_size", "mi_fill_value_bits", "mi_status_string", "mi_last_error_message"]
 
 _i64, _p, _dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
@@ -32,6 +32,14 @@ _INPLACE = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, 
 _OUT = [_p, _i64, _p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _dbl]
 
 _lib = None
+
+
+class SampleParams(ctypes.Structure):
+    """mi_sample_params_t."""
+    _fields_ = [("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
+                ("min_p", ctypes.c_void_p), ("temperature_all", ctypes.c_float), ("top_k_all", ctypes.c_int32),
+                ("top_p_all", ctypes.c_float), ("min_p_all", ctypes.c_float), ("seed", ctypes.c_uint64),
+                ("offset", ctypes.c_uint64)]
 
 
 class BitmaskError(RuntimeError):
@@ -58,11 +66,13 @@ def load_library(path: Union[str, pathlib.Path, None] = None) -> ctypes.CDLL:
     lib.mi_apply_bitmask_out_ex.argtypes = _OUT + [ctypes.c_int, _p]
     lib.mi_apply_bitmask_rows.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _p,
                                           _dbl, _p]
+    lib.mi_apply_bitmask_sample.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64,
+                                            ctypes.POINTER(SampleParams), _p, _p]
     lib.mi_apply_bitmask_inplace_host.argtypes = _INPLACE + [ctypes.c_int]
     lib.mi_apply_bitmask_out_host.argtypes = _OUT + [ctypes.c_int]
     for f in ("mi_apply_bitmask_inplace", "mi_apply_bitmask_inplace_ex", "mi_apply_bitmask_out",
-              "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_inplace_host",
-           "mi_apply_bitmask_out_host",
+              "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample",
+           "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
               "mi_resolve_vocab_size", "mi_fill_value_bits"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mi_resolve_vocab_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64)]
@@ -238,6 +248,65 @@ def mi_apply_bitmask_rows(logits, mask, row_needs_mask=None, vocab_size: Optiona
         L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
         M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M), -1 if vocab_size is None else int(vocab_size),
         None if gate is None else gate.data_ptr(), None if out is None else out.data_ptr(), float(fill_value),
+        _stream_handle(logits.device, stream)))
+    return out
+
+
+def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None, *, temperature=1.0, top_k=0,
+                            top_p=1.0, min_p=0.0, seed: int = 0, offset: int = 0, out=None, stream=None):
+    """One token per row (int64 [rows]) from the masked, filtered softmax.
+
+    logits-processor page, "Ops: sample": per-row temperature (<= 0: argmax),
+    top-k / top-p / min-p intersected as one keep threshold, Gumbel-max draw
+    from a Philox stream keyed by (seed, row, offset).  Each of temperature,
+    top_k, top_p and min_p is a scalar for every row or a length-rows tensor.
+    With ``mask`` (int32 [rows, ceil(V/32)] on the same GPU) masked tokens
+    take no part; the logits are not modified.  A row with no allowed token
+    gets -1.
+    """
+    torch = _torch()
+    if not logits.is_cuda:
+        raise ValueError("logits must be on the GPU")
+    lib = load_library()
+    L = _as_rows(logits, "logits")
+    rows = L.shape[0]
+    keep = []
+
+    def per_row(v, dtype, name):
+        """(device pointer, 0) for a per-row tensor, (None, v) for a scalar."""
+        if isinstance(v, torch.Tensor):
+            t = v.reshape(-1).to(device=logits.device, dtype=dtype).contiguous()
+            if t.numel() != rows:
+                raise ValueError(f"{name} has {t.numel()} entries for {rows} rows")
+            keep.append(t)
+            return t.data_ptr(), 0
+        return None, v
+
+    prm = SampleParams()
+    prm.temperature, v = per_row(temperature, torch.float32, "temperature")
+    prm.temperature_all = float(v)
+    prm.top_k, v = per_row(top_k, torch.int32, "top_k")
+    prm.top_k_all = int(v)
+    prm.top_p, v = per_row(top_p, torch.float32, "top_p")
+    prm.top_p_all = float(v)
+    prm.min_p, v = per_row(min_p, torch.float32, "min_p")
+    prm.min_p_all = float(v)
+    prm.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    prm.offset = int(offset) & 0xFFFFFFFFFFFFFFFF
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int64, device=logits.device)
+    if out.dtype != torch.int64 or out.numel() != rows or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int64 tensor with one entry per row")
+    if mask is not None:
+        M = _check_mask(mask, logits.device)
+        mp, mr, mc, ms = M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M)
+    else:
+        mp, mr, mc, ms = None, 0, 0, 0
+    for t in keep:
+        _keep_alive(t, stream)
+    check(lib.mi_apply_bitmask_sample(
+        L.data_ptr(), MI_DTYPE[_dtype_name(L)], rows, L.shape[1], _row_stride(L), mp, mr, mc, ms,
+        -1 if vocab_size is None else int(vocab_size), ctypes.byref(prm), out.data_ptr(),
         _stream_handle(logits.device, stream)))
     return out
 

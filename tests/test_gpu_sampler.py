@@ -1,0 +1,192 @@
+"""GPU parity of the fused apply + sampler against the sampler oracle.
+
+Exact where the decision is exact: greedy picks (integer comparisons on the
+same values) and rows with no candidate.  For draws, the GPU works in
+binary32 and the oracle in binary64, so a draw may legitimately differ where
+two Gumbel keys, or a token's probability and a filter's cutoff, agree to
+within float rounding; the oracle reports those cases as a candidate set
+(margin 1e-4) and the GPU token must be in it.  The number of draws that
+match the oracle's own draw exactly is checked too.  The draw distribution
+is checked with a chi-square test against the renormalised filtered softmax.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import sampler as S
+from packed_logit_bitmask_amd import workloads
+import packed_logit_bitmask_amd as mb
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TORCH = {"float32": (np.int32, torch.float32), "float16": (np.int16, torch.float16),
+         "bfloat16": (np.int16, torch.bfloat16)}
+MARGIN = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests need an MI355X")
+    mb.load_library()
+
+
+def values64(bits, dtype):
+    if dtype == "float32":
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "float16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def dev_logits(bits, dtype):
+    ndt, tdt = TORCH[dtype]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(ndt)).to("cuda").view(tdt)
+
+
+def per_row(v, i):
+    return v[i] if isinstance(v, np.ndarray) else v
+
+
+def check_rows(bits, dtype, mask, vocab, T, k, p, m, seed, offset, rows=None, min_exact=0.98):
+    """Sample on the GPU and check every row against the oracle; returns the tokens."""
+    R, cols = bits.shape
+    dl = dev_logits(bits, dtype)
+    dm = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask)).to("cuda")
+    targs = {}
+    for name, v, td in (("temperature", T, torch.float32), ("top_k", k, torch.int32),
+                        ("top_p", p, torch.float32), ("min_p", m, torch.float32)):
+        targs[name] = torch.from_numpy(v).to("cuda", td) if isinstance(v, np.ndarray) else v
+    tok = mb.mi_apply_bitmask_sample(dl, dm, vocab, seed=seed, offset=offset, **targs).cpu().numpy()
+    V = cols if vocab is None and mask is None else (vocab if vocab is not None else
+                                                     min(cols, 32 * mask.shape[1]))
+    vals = values64(bits, dtype)
+    exact = 0
+    for r in (range(R) if rows is None else rows):
+        allowed = S.allowed_tokens(None if mask is None else mask[r], V, cols)
+        want, det = S.sample_row(vals[r], allowed, float(per_row(T, r)), int(per_row(k, r)), float(per_row(p, r)),
+                                 float(per_row(m, r)), seed, offset, r, margin=MARGIN)
+        assert tok[r] in det["candidates"], (r, tok[r], want, sorted(det["candidates"])[:5])
+        if tok[r] >= 0:
+            assert allowed[tok[r]], (r, tok[r])
+        exact += int(tok[r] == want)
+    n = R if rows is None else len(rows)
+    assert exact >= min_exact * n, f"only {exact}/{n} draws equal the oracle's"
+    return tok
+
+
+def random_logits(rng, dtype, R, cols, sigma=2.0, ties=False):
+    """N(0, sigma) logits as dtype bit patterns; with ties, rounded to halves (many equal values)."""
+    x = rng.standard_normal((R, cols)).astype(np.float32) * np.float32(sigma)
+    if ties:
+        x = np.round(x * 2) / 2
+    if dtype == "float32":
+        return x.view(np.uint32)
+    if dtype == "float16":
+        return x.astype(np.float16).view(np.uint16)
+    b = x.view(np.uint32)
+    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_greedy_exact_with_ties_and_masks(dtype):
+    rng = np.random.default_rng(1)
+    R, cols = 40, 3000
+    bits = random_logits(rng, dtype, R, cols, ties=True)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.3, (cols + 31) // 32, rng)
+    mask[5] = 0                                       # an unsatisfiable row
+    say(f"[gpu] sampler greedy {dtype}")
+    tok = check_rows(bits, dtype, mask, None, 0.0, 0, 1.0, 0.0, 1, 2, min_exact=1.0)
+    assert tok[5] == -1
+    check_rows(bits, dtype, None, 2500, -1.0, 5, 0.5, 0.1, 1, 2, min_exact=1.0)
+
+
+@pytest.mark.parametrize("T,k,p,m", [(1.0, 0, 1.0, 0.0), (0.7, 40, 1.0, 0.0), (1.2, 0, 0.9, 0.0),
+                                      (1.0, 0, 1.0, 0.02), (0.8, 100, 0.95, 0.01), (1.5, 1, 1.0, 0.0),
+                                      (1.0, 5000, 0.3, 0.0)])
+def test_draws_match_oracle(T, k, p, m):
+    rng = np.random.default_rng(2)
+    R, cols = 48, 4100
+    dtype = "bfloat16"
+    bits = random_logits(rng, dtype, R, cols)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < rng.uniform(0.05, 0.9, (R, 1)), 129, rng)
+    say(f"[gpu] sampler draws T={T} k={k} p={p} m={m}")
+    check_rows(bits, dtype, mask, 4100, T, k, p, m, seed=11, offset=3)
+
+
+def test_per_row_parameters_verify_shape():
+    rng = np.random.default_rng(3)
+    wl = workloads.verify_fp16()
+    R = wl.rows
+    T = rng.choice([0.0, 0.5, 1.0, 1.3], R).astype(np.float32)
+    k = rng.choice([0, 1, 20, 500], R).astype(np.int32)
+    p = rng.choice([1.0, 0.9, 0.6], R).astype(np.float32)
+    m = rng.choice([0.0, 0.05], R).astype(np.float32)
+    say("[gpu] sampler per-row parameters on the [1024, 32000] fp16 verify shape")
+    tok = check_rows(wl.logits, "float16", wl.mask, None, T, k, p, m, seed=7, offset=9,
+                     rows=list(range(0, R, 4)))
+    zero_rows = [r for r in range(R) if not (wl.mask[r] != 0).any()]
+    assert all(tok[r] == -1 for r in zero_rows) and zero_rows
+
+
+def test_full_size_mixed_bf16_with_mask():
+    wl = workloads.mixed_bf16()
+    say("[gpu] sampler on the [256, 128256] bf16 shape, vocab 128000, masked")
+    check_rows(wl.logits, "bfloat16", wl.mask, 128000, 0.8, 0, 0.9, 0.0, seed=123, offset=1,
+               rows=list(range(0, 256, 8)))
+    check_rows(wl.logits, "bfloat16", wl.mask, 128000, 1.0, 50, 1.0, 0.0, seed=123, offset=2,
+               rows=list(range(3, 256, 16)))
+
+
+def test_large_vocab_fp32():
+    wl = workloads.large_fp32(rows=8)
+    say("[gpu] sampler on fp32 rows of 262144 (vocab 262100)")
+    check_rows(wl.logits, "float32", wl.mask, 262100, 1.0, 0, 0.95, 0.001, seed=5, offset=5)
+
+
+def test_determinism_and_offset():
+    rng = np.random.default_rng(4)
+    bits = random_logits(rng, "float32", 256, 2000)
+    dl = dev_logits(bits, "float32")
+    a = mb.mi_apply_bitmask_sample(dl, seed=9, offset=4, top_p=0.95).cpu().numpy()
+    b = mb.mi_apply_bitmask_sample(dl, seed=9, offset=4, top_p=0.95).cpu().numpy()
+    c = mb.mi_apply_bitmask_sample(dl, seed=9, offset=5, top_p=0.95).cpu().numpy()
+    d = mb.mi_apply_bitmask_sample(dl, seed=10, offset=4, top_p=0.95).cpu().numpy()
+    assert np.array_equal(a, b)
+    assert (a != c).mean() > 0.7 and (a != d).mean() > 0.7
+
+
+def test_distribution_chi_square():
+    rng = np.random.default_rng(5)
+    z = (rng.standard_normal(64) * 2.0).astype(np.float32)
+    allowed = np.ones(64, bool)
+    allowed[[7, 30, 31]] = False
+    mask_row = workloads.pack_allowed(allowed[None, :], 2, None, garbage=False)
+    R = 4096
+    bits = np.repeat(z.view(np.uint32)[None, :], R, axis=0)
+    mask = np.repeat(mask_row, R, axis=0)
+    T, k, p, m = 0.9, 20, 0.95, 0.01
+    dl = dev_logits(bits, "float32")
+    dm = torch.from_numpy(mask).to("cuda")
+    toks = np.concatenate([mb.mi_apply_bitmask_sample(dl, dm, temperature=T, top_k=k, top_p=p, min_p=m, seed=3,
+                                                      offset=o).cpu().numpy() for o in range(5)])
+    probs = S.filtered_probs(z.astype(np.float64), allowed, T, k, p, m)
+    counts = np.bincount(toks, minlength=64)
+    assert counts[probs == 0].sum() == 0
+    exp = probs * toks.size
+    big = exp >= 5
+    stat = (((counts[big] - exp[big]) ** 2) / exp[big]).sum()
+    dof = int(big.sum()) - 1
+    zscore = ((stat / dof) ** (1 / 3) - (1 - 2 / (9 * dof))) / math.sqrt(2 / (9 * dof))
+    say(f"[gpu] chi-square {stat:.1f} on {dof} dof (z = {zscore:.2f})")
+    assert zscore < 4.75
+    assert np.abs(counts / toks.size - probs).max() < 0.01
