@@ -596,7 +596,7 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
   const uint32_t* m = reinterpret_cast<const uint32_t*>(mask);
   const int32_t V = static_cast<int32_t>(p.V);
   (void)hipGetLastError();
-  constexpr int64_t kRowsPerLaunch = int64_t(1) << 20;   // blocks * 1024 threads < 2^32
+  constexpr int64_t kRowsPerLaunch = int64_t(1) << 20;   // blocks * threads < 2^32
   for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
     const uint32_t n = static_cast<uint32_t>(std::min(kRowsPerLaunch, rows - r0));
     const int64_t mr0 = m ? r0 * mask_row_stride : 0;
@@ -606,22 +606,29 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     if (ar.top_k) ar.top_k += r0;
     if (ar.top_p) ar.top_p += r0;
     if (ar.min_p) ar.min_p += r0;
+    const auto* lg = static_cast<const char*>(logits) + r0 * logits_row_stride * p.esize;
+    const uint32_t* mk = m ? m + mr0 : nullptr;
+    // Histogram LDS only when some row may filter; deep load pipeline when a
+    // compute unit holds one row at a time (rows <= 256), shallow otherwise.
+    const bool may_filter = ar.top_k || ar.top_p || ar.top_k_all > 0 || ar.top_p_all < 1.0f;
+    const bool deep = n <= 256;
+    const int threads = deep ? 1024 : 256;
+    const size_t lds = may_filter ? mi::sample_hist_bytes(threads) : 0;
+#define MI_SAMPLE(TAG, BITS, DEPTH, THREADS)                                                                   \
+  mi::sample_rows<TAG, DEPTH, THREADS><<<n, THREADS, lds, stream>>>(reinterpret_cast<const BITS*>(lg),          \
+                                                                    logits_row_stride, mk, mask_row_stride, V,   \
+                                                                    ar, r0, tokens + r0)
     switch (dtype) {
       case MI_DTYPE_F32:
-        mi::sample_rows<mi::F32Bits><<<n, mi::kSampleThreads, 0, stream>>>(
-            static_cast<const uint32_t*>(logits) + r0 * logits_row_stride, logits_row_stride, m ? m + mr0 : nullptr,
-            mask_row_stride, V, ar, r0, tokens + r0);
+        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 4, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 2, 256);
         break;
       case MI_DTYPE_F16:
-        mi::sample_rows<mi::F16Bits><<<n, mi::kSampleThreads, 0, stream>>>(
-            static_cast<const uint16_t*>(logits) + r0 * logits_row_stride, logits_row_stride, m ? m + mr0 : nullptr,
-            mask_row_stride, V, ar, r0, tokens + r0);
+        if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 4, 1024); else MI_SAMPLE(mi::F16Bits, uint16_t, 2, 256);
         break;
       default:
-        mi::sample_rows<mi::BF16Bits><<<n, mi::kSampleThreads, 0, stream>>>(
-            static_cast<const uint16_t*>(logits) + r0 * logits_row_stride, logits_row_stride, m ? m + mr0 : nullptr,
-            mask_row_stride, V, ar, r0, tokens + r0);
+        if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 4, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 2, 256);
     }
+#undef MI_SAMPLE
   }
   return after_launch("sample_rows");
 }

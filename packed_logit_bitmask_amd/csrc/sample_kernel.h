@@ -10,40 +10,37 @@
 // "apply_packed_bitmask"), it lies below the vocab size and its logit is
 // finite -- so a masked token is never drawn.  The logits are only read.
 //
-// One block of 1024 threads (16 wave64s) per row.  Each pass walks the row
-// in groups of 4 consecutive tokens per thread (one generator call serves a
-// group); trip counts are uniform across the block so wave-wide shuffles and
-// ballots always see every lane.
+// One block per row (1024 threads when each compute unit holds one row, 256
+// when many rows share one).  Each pass walks the row
+// in groups of 8 consecutive tokens per thread (16-byte vector loads when
+// the row start is aligned; four groups in flight per thread); trip counts
+// are uniform across the block.
 //
 //   pass 1   max logit and its (lowest) index, count of candidate tokens
 //            -> greedy rows and rows with no candidate end here;
-//   top-k    4 radix passes over an order-preserving 32-bit key of the logit
+//   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
-//   top-p    one pass for the softmax mass Z, then 4 radix passes summing
-//            mass instead of counts: the largest key whose tokens at or above
-//            it hold at least p * Z.  Masses are fixed-point integers
-//            (2^31 * exp(z - z_max)), so the sums do not depend on the order
-//            of the atomic adds and the cut is deterministic;
+//   top-p    the same radix search summing softmax mass instead of counts:
+//            the largest key whose tokens at or above it hold at least p * Z
+//            (Z is the total of the first pass's mass histogram).  Masses
+//            are fixed-point integers (2^31 * exp(z - z_max)), so the sums do
+//            not depend on the order of the atomic adds: the cut is
+//            deterministic.  Both searches share 4 passes of 8-bit digits;
 //   min-p    z - z_max >= ln(min_p), no pass of its own;
-//   draw     Gumbel-max over the kept tokens: key = z - ln(-ln u), u from
+//   draw     Gumbel-max over the kept tokens: key = z - ln(-ln u) (logarithms
+//            by the hardware log2 instruction, rescaled), u from
 //            Philox4x32-10 (counter (i / 4, row, offset lo, offset hi), key
 //            (seed lo, seed hi), word i % 4; u = (floor(x / 2^9) + 1/2) / 2^23),
 //            ties to the lowest index.
 //
-// Histogram updates go through wave-level aggregation: lanes that hit the
-// same bin are combined with a ballot and one lane adds the group's total,
-// so the clustered high digits of float keys do not serialise on LDS
-// atomics.
+// Histograms are private to each wave (LDS), folded after every pass.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mi {
-
-constexpr int kSampleThreads = 1024;
-constexpr int kSampleWaves = kSampleThreads / 64;
 
 struct SampleArgs {
   const float* temperature;   // per row, or nullptr: temperature_all
@@ -100,113 +97,109 @@ __device__ __forceinline__ float unit_uniform(uint32_t x) {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & 63; }
 
-template <typename V>
-__device__ __forceinline__ V wave_sum(V v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
-// Add w (for every lane with `active`) into hist[bin], one LDS atomic per
-// distinct bin in the wave.  Every lane of the wave must call it.
-template <typename V>
-__device__ __forceinline__ void wave_hist_add(V* hist, bool active, uint32_t bin, V w) {
-  uint64_t pending = __ballot(active);
-  while (pending) {
-    const int leader = __ffsll(static_cast<long long>(pending)) - 1;
-    const uint32_t lb = __shfl(bin, leader);
-    const bool same = active && bin == lb;
-    const uint64_t group = __ballot(same);
-    const V total = wave_sum(same ? w : V(0));
-    if (lane_id() == leader) atomicAdd(&hist[lb], total);
-    active = active && !same;
-    pending &= ~group;
-  }
-}
-
+// One row's logits and mask, read 8 consecutive tokens at a time.
 template <typename D>
 struct RowView {
   const typename D::Bits* row;
   const uint32_t* mrow;   // nullptr: no mask
   int32_t V;
+  bool aligned;           // row start 16-byte aligned: whole groups load as vectors
 
-  // value and candidacy of token i (< V)
-  __device__ __forceinline__ float value(int32_t i, uint32_t word, bool* ok) const {
-    const float x = D::value(row[i]);
-    const bool bit = mrow ? ((word >> (static_cast<uint32_t>(i) & 31u)) & 1u) : true;
-    *ok = bit && __builtin_isfinite(x);
-    return x;
+  // Tokens i0..i0+7 (i0 a multiple of 8): values and a bit per token that
+  // is a candidate (below V, mask bit set, finite logit).
+  __device__ __forceinline__ uint32_t load8(int32_t i0, float x[8]) const {
+    uint32_t bits = 0;
+    if (i0 < V) {
+      bits = mrow ? (mrow[i0 >> 5] >> (static_cast<uint32_t>(i0) & 31u)) & 0xFFu : 0xFFu;
+      if (aligned && i0 + 8 <= V) {
+        if constexpr (sizeof(typename D::Bits) == 2) {
+          const uint4 v = *reinterpret_cast<const uint4*>(row + i0);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            x[2 * q] = D::value(static_cast<typename D::Bits>(w[q] & 0xFFFFu));
+            x[2 * q + 1] = D::value(static_cast<typename D::Bits>(w[q] >> 16));
+          }
+        } else {
+          const uint4 a = *reinterpret_cast<const uint4*>(row + i0);
+          const uint4 b = *reinterpret_cast<const uint4*>(row + i0 + 4);
+          const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) x[q] = D::value(w[q]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = i0 + q < V ? D::value(row[i0 + q]) : 0.f;
+      }
+    }
+    uint32_t ok = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (((bits >> q) & 1u) && i0 + q < V && __builtin_isfinite(x[q])) ok |= 1u << q;
+    return ok;
   }
 };
 
-// Radix select from the top: the largest key K such that the weight (count
-// or mass) of candidate tokens with key >= K reaches `need`.  `keep_ok`
-// filters the tokens that take part.
-template <typename D, typename W>
-__device__ uint32_t radix_select(const RowView<D>& rv, int32_t ngroups, W need, float inv_t, float zmax,
-                                 bool by_mass, W* hist, uint32_t* s_digit, W* s_need) {
+// Walk the row: f(i0, x[8], ok) for every 8-token group, IN_FLIGHT groups
+// loaded before any is used (4 keeps 64 bytes of 16-bit logits in flight per
+// thread; 2 halves the registers so more rows share a compute unit).  The
+// trip count is the same for every thread of the block (groups past the row
+// come with ok == 0).
+template <int IN_FLIGHT, int THREADS, typename D, typename F>
+__device__ __forceinline__ void walk_row(const RowView<D>& rv, F&& f) {
+  const int32_t ngroups = (rv.V + 7) / 8;
   const int t = static_cast<int>(threadIdx.x);
-  uint32_t prefix = 0, pmask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = t; b < 256; b += kSampleThreads) hist[b] = W(0);
-    __syncthreads();
-    for (int32_t base = 0; base < ngroups; base += kSampleThreads) {
-      const int32_t g = base + t;
-      const int32_t i0 = 4 * g;
-      const uint32_t word = (rv.mrow && i0 < rv.V) ? rv.mrow[i0 >> 5] : 0u;
+  for (int32_t base = 0; base < ngroups; base += IN_FLIGHT * THREADS) {
+    float x[IN_FLIGHT][8];
+    uint32_t ok[IN_FLIGHT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int32_t i = i0 + q;
-        bool ok = false;
-        float x = 0.f;
-        if (g < ngroups && i < rv.V) x = rv.value(i, word, &ok);
-        const uint32_t key = order_key(x);
-        ok = ok && (key & pmask) == prefix;
-        W w = W(1);
-        if (by_mass) w = ok ? static_cast<W>(expf(x * inv_t - zmax) * 2147483648.0f) : W(0);
-        wave_hist_add<W>(hist, ok, (key >> shift) & 255u, w);
-      }
+    for (int j = 0; j < IN_FLIGHT; ++j) {
+      const int32_t g = base + j * THREADS + t;
+      ok[j] = g < ngroups ? rv.load8(8 * g, x[j]) : 0u;
     }
-    __syncthreads();
-    if (t == 0) {
-      W cum = W(0);
-      int d = 255;
-      for (; d > 0; --d) {
-        if (cum + hist[d] >= need) break;
-        cum += hist[d];
-      }
-      *s_digit = static_cast<uint32_t>(d);
-      *s_need = need - cum;
-    }
-    __syncthreads();
-    prefix |= *s_digit << shift;
-    pmask |= 255u << shift;
-    need = *s_need;
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IN_FLIGHT; ++j) f(8 * (base + j * THREADS + t), x[j], ok[j]);
   }
-  return prefix;
 }
 
-template <typename D>
-__global__ __launch_bounds__(kSampleThreads) void sample_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
+// Per-wave private histograms for the threshold search: counts for top-k,
+// fixed-point softmax mass for top-p.
+struct SelectState {
+  uint32_t prefix_k, need_k;            // top-k: key prefix so far, count still needed below it
+  unsigned long long need_p;            // top-p: mass still needed below the prefix
+  uint32_t prefix_p;
+};
+
+// Dynamic LDS the kernel needs when a row may use top-k or top-p (the
+// per-wave histograms); 0 otherwise.
+constexpr size_t sample_hist_bytes(int threads) {
+  return static_cast<size_t>(threads / 64) * 256 * (sizeof(uint32_t) + sizeof(unsigned long long));
+}
+
+// One block of THREADS threads per row.  1024 threads with IN_FLIGHT 4 when
+// each compute unit holds one row at a time; 256 threads with IN_FLIGHT 2 so
+// several rows share a compute unit when there are many rows.
+template <typename D, int IN_FLIGHT, int THREADS>
+__global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
                                                               const uint32_t* __restrict__ mask, int64_t ms,
                                                               int32_t V, SampleArgs a, int64_t row_base,
                                                               int64_t* __restrict__ out) {
-  __shared__ float s_best[kSampleWaves];
-  __shared__ int32_t s_besti[kSampleWaves];
-  __shared__ uint32_t s_count[kSampleWaves];
-  __shared__ unsigned long long s_mass[kSampleWaves];
-  __shared__ uint32_t hist_n[256];
-  __shared__ unsigned long long hist_m[256];
-  __shared__ uint32_t s_digit;
-  __shared__ uint32_t s_need_n;
-  __shared__ unsigned long long s_need_m;
+  constexpr int kWaves = THREADS / 64;
+  __shared__ float s_best[kWaves];
+  __shared__ int32_t s_besti[kWaves];
+  __shared__ uint32_t s_count[kWaves];
+  __shared__ SelectState s_sel;
+  // per-wave histograms in dynamic LDS (present only when a filter may run)
+  extern __shared__ unsigned long long s_dyn[];
+  auto hist_m = reinterpret_cast<unsigned long long(*)[256]>(s_dyn);
+  auto hist_n = reinterpret_cast<uint32_t(*)[256]>(s_dyn + kWaves * 256);
 
   const int64_t r = blockIdx.x;
   const int t = static_cast<int>(threadIdx.x);
   const int wave = t >> 6;
-  const RowView<D> rv{logits + r * ls, mask ? mask + r * ms : nullptr, V};
-  const int32_t ngroups = (V + 3) / 4;
+  const typename D::Bits* row = logits + r * ls;
+  const RowView<D> rv{row, mask ? mask + r * ms : nullptr, V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0};
 
   const float temp = a.temperature ? a.temperature[r] : a.temperature_all;
   const int32_t top_k = a.top_k ? a.top_k[r] : a.top_k_all;
@@ -217,28 +210,15 @@ __global__ __launch_bounds__(kSampleThreads) void sample_rows(const typename D::
   float best = -__builtin_inff();
   int32_t besti = 0x7FFFFFFF;
   uint32_t count = 0;
-  for (int32_t base = 0; base < ngroups; base += kSampleThreads) {
-    const int32_t g = base + t;
-    const int32_t i0 = 4 * g;
-    if (g < ngroups) {
-      const uint32_t word = rv.mrow ? rv.mrow[i0 >> 5] : 0u;
+  walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+    count += __builtin_popcount(ok);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int32_t i = i0 + q;
-        if (i < V) {
-          bool ok;
-          const float x = rv.value(i, word, &ok);
-          if (ok) {
-            ++count;
-            if (x > best) {  // strictly greater: the first (lowest) index wins ties within a thread
-              best = x;
-              besti = i;
-            }
-          }
-        }
+    for (int q = 0; q < 8; ++q)
+      if (((ok >> q) & 1u) && x[q] > best) {  // strictly greater: each thread sees its tokens in order
+        best = x[q];
+        besti = i0 + q;
       }
-    }
-  }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ob = __shfl_xor(best, o);
@@ -258,7 +238,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_rows(const typename D::
   best = s_best[0];
   besti = s_besti[0];
   count = s_count[0];
-  for (int w = 1; w < kSampleWaves; ++w) {
+  for (int w = 1; w < kWaves; ++w) {
     if (s_best[w] > best || (s_best[w] == best && s_besti[w] < besti)) {
       best = s_best[w];
       besti = s_besti[w];
@@ -272,43 +252,85 @@ __global__ __launch_bounds__(kSampleThreads) void sample_rows(const typename D::
 
   const float inv_t = 1.0f / temp;
   const float zmax = best * inv_t;
-  uint32_t cut = 0;   // keep tokens with order_key(x) >= cut
+  const bool use_k = top_k > 0 && static_cast<uint32_t>(top_k) < count;
+  const bool use_p = top_p < 1.0f;
+  uint32_t cut = 0;  // keep tokens with order_key(x) >= cut
 
-  if (top_k > 0 && static_cast<uint32_t>(top_k) < count) {
-    const uint32_t k = radix_select<D, uint32_t>(rv, ngroups, static_cast<uint32_t>(top_k), inv_t, zmax, false,
-                                                 hist_n, &s_digit, &s_need_n);
-    cut = max(cut, k);
-  }
-  if (top_p < 1.0f) {
-    unsigned long long mass = 0;
-    for (int32_t base = 0; base < ngroups; base += kSampleThreads) {
-      const int32_t g = base + t;
-      const int32_t i0 = 4 * g;
-      if (g < ngroups) {
-        const uint32_t word = rv.mrow ? rv.mrow[i0 >> 5] : 0u;
+  // ---- top-k and top-p cuts: 4 radix passes (8-bit digits, high to low),
+  // both searches in the same passes.  The first mass histogram covers every
+  // candidate, so its total is the softmax mass Z.
+  if (use_k || use_p) {
+    if (t == 0) s_sel = SelectState{0u, static_cast<uint32_t>(top_k), 0ull, 0u};
+    uint32_t pmask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int b = t; b < kWaves * 256; b += THREADS) {
+        (&hist_n[0][0])[b] = 0u;
+        (&hist_m[0][0])[b] = 0ull;
+      }
+      __syncthreads();
+      const uint32_t pk = s_sel.prefix_k, pp = s_sel.prefix_p;
+      walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t, const float* x, uint32_t ok) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int32_t i = i0 + q;
-          if (i < V) {
-            bool ok;
-            const float x = rv.value(i, word, &ok);
-            if (ok) mass += static_cast<unsigned long long>(expf(x * inv_t - zmax) * 2147483648.0f);
+        for (int q = 0; q < 8; ++q) {
+          if ((ok >> q) & 1u) {
+            const uint32_t key = order_key(x[q]);
+            const uint32_t d = (key >> shift) & 255u;
+            if (use_k && (key & pmask) == pk) atomicAdd(&hist_n[wave][d], 1u);
+            if (use_p && (key & pmask) == pp)
+              atomicAdd(&hist_m[wave][d],
+                        static_cast<unsigned long long>(expf(x[q] * inv_t - zmax) * 2147483648.0f));
           }
         }
+      });
+      __syncthreads();
+      // fold the per-wave histograms into row 0
+      for (int b = t; b < 256; b += THREADS) {
+        uint32_t n = 0;
+        unsigned long long m = 0;
+        for (int w = 0; w < kWaves; ++w) {
+          n += hist_n[w][b];
+          m += hist_m[w][b];
+        }
+        hist_n[0][b] = n;
+        hist_m[0][b] = m;
       }
+      __syncthreads();
+      if (t == 0) {
+        SelectState st = s_sel;
+        if (use_k) {
+          uint32_t cum = 0;
+          int d = 255;
+          for (; d > 0; --d) {
+            if (cum + hist_n[0][d] >= st.need_k) break;
+            cum += hist_n[0][d];
+          }
+          st.prefix_k |= static_cast<uint32_t>(d) << shift;
+          st.need_k -= cum;
+        }
+        if (use_p) {
+          if (shift == 24) {  // every candidate is in this histogram: its total is Z
+            unsigned long long z = 0;
+            for (int b = 0; b < 256; ++b) z += hist_m[0][b];
+            unsigned long long target =
+                static_cast<unsigned long long>(ceil(static_cast<double>(top_p) * static_cast<double>(z)));
+            st.need_p = target ? target : 1ull;
+          }
+          unsigned long long cum = 0;
+          int d = 255;
+          for (; d > 0; --d) {
+            if (cum + hist_m[0][d] >= st.need_p) break;
+            cum += hist_m[0][d];
+          }
+          st.prefix_p |= static_cast<uint32_t>(d) << shift;
+          st.need_p -= cum;
+        }
+        s_sel = st;
+      }
+      __syncthreads();
+      pmask |= 255u << shift;
     }
-    mass = wave_sum(mass);
-    if (lane_id() == 0) s_mass[wave] = mass;
-    __syncthreads();
-    unsigned long long total = 0;
-    for (int w = 0; w < kSampleWaves; ++w) total += s_mass[w];
-    __syncthreads();
-    unsigned long long target = static_cast<unsigned long long>(ceil(static_cast<double>(top_p) *
-                                                                     static_cast<double>(total)));
-    if (target == 0) target = 1;
-    const uint32_t k = radix_select<D, unsigned long long>(rv, ngroups, target, inv_t, zmax, true, hist_m,
-                                                           &s_digit, &s_need_m);
-    cut = max(cut, k);
+    if (use_k) cut = max(cut, s_sel.prefix_k);
+    if (use_p) cut = max(cut, s_sel.prefix_p);
   }
   const bool use_min_p = min_p > 0.f;
   const float ln_min_p = use_min_p ? logf(min_p) : 0.f;
@@ -316,33 +338,33 @@ __global__ __launch_bounds__(kSampleThreads) void sample_rows(const typename D::
   // ---- draw: Gumbel-max over the kept tokens
   float bk = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
-  for (int32_t base = 0; base < ngroups; base += kSampleThreads) {
-    const int32_t g = base + t;
-    const int32_t i0 = 4 * g;
-    if (g < ngroups) {
-      const uint32_t word = rv.mrow ? rv.mrow[i0 >> 5] : 0u;
-      uint32_t c[4] = {static_cast<uint32_t>(g), static_cast<uint32_t>(row_base + r), a.offset_lo, a.offset_hi};
-      philox4x32_10(c, a.seed_lo, a.seed_hi);
+  walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+    uint32_t kept = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int32_t i = i0 + q;
-        if (i < V) {
-          bool ok;
-          const float x = rv.value(i, word, &ok);
-          const float z = x * inv_t;
-          ok = ok && order_key(x) >= cut && (!use_min_p || z - zmax >= ln_min_p);
-          if (ok) {
-            const float u = unit_uniform(c[q]);
-            const float key = z - logf(-logf(u));
-            if (key > bk) {
-              bk = key;
-              bi = i;
-            }
-          }
+    for (int q = 0; q < 8; ++q)
+      if (((ok >> q) & 1u) && order_key(x[q]) >= cut && (!use_min_p || x[q] * inv_t - zmax >= ln_min_p))
+        kept |= 1u << q;
+    if (!kept) return;
+    uint32_t c0[4] = {static_cast<uint32_t>(i0 >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo, a.offset_hi};
+    uint32_t c1[4] = {static_cast<uint32_t>(i0 >> 2) + 1u, static_cast<uint32_t>(row_base + r), a.offset_lo,
+                      a.offset_hi};
+    if (kept & 0x0Fu) philox4x32_10(c0, a.seed_lo, a.seed_hi);
+    if (kept & 0xF0u) philox4x32_10(c1, a.seed_lo, a.seed_hi);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if ((kept >> q) & 1u) {
+        // Gumbel variate -ln(-ln u) through the hardware base-2 logarithm:
+        // -ln u = -log2(u) * ln 2, then -ln(that) = -log2(that) * ln 2
+        const float u = unit_uniform(q < 4 ? c0[q] : c1[q - 4]);
+        const float e = -__log2f(u) * 0.6931471805599453f;
+        const float key = x[q] * inv_t - __log2f(e) * 0.6931471805599453f;
+        if (key > bk) {
+          bk = key;
+          bi = i0 + q;
         }
       }
     }
-  }
+  });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ob = __shfl_xor(bk, o);
@@ -359,12 +381,12 @@ __global__ __launch_bounds__(kSampleThreads) void sample_rows(const typename D::
   }
   __syncthreads();
   if (t == 0) {
-    for (int w = 1; w < kSampleWaves; ++w)
+    for (int w = 1; w < kWaves; ++w)
       if (s_best[w] > bk || (s_best[w] == bk && s_besti[w] < bi)) {
         bk = s_best[w];
         bi = s_besti[w];
       }
-    // bk == -inf only if no token survived the cut, which cannot happen (the max token always does)
+    // the max-logit token always survives every cut, so bi is set
     out[r] = bi == 0x7FFFFFFF ? besti : bi;
   }
 }
