@@ -93,8 +93,12 @@ typedef enum mi_variant {
     MI_VARIANT_SCALAR = 1,  /* one thread per element */
     MI_VARIANT_VEC = 2,     /* 16-byte vectors: all-masked vectors are stored without a
                                read, mixed ones read-select-write, all-kept ones skipped */
-    MI_VARIANT_WRONLY = 3   /* in place only: one lane per element, the store of the fill
+    MI_VARIANT_WRONLY = 3,  /* in place only: one lane per element, the store of the fill
                                predicated by the mask bit; logits are never read */
+    MI_VARIANT_VEC_RESIDENT = 4  /* in place only: the 16-byte-vector kernel shaped for logits
+                               that are still in the GPU's caches (just written by the
+                               producing kernel): write-back stores, 16 vectors per lane.
+                               AUTO is shaped for logits that must come from HBM. */
 } mi_variant_t;
 
 /*

@@ -19,7 +19,7 @@ LIBRARY = PKG / "libmi_bitmask.so"
 MI_DTYPE = {"float32": 0, "float16": 1, "bfloat16": 2}
 STATUS = ["MI_OK", "MI_ERR_NULL_POINTER", "MI_ERR_BAD_DTYPE", "MI_ERR_BAD_SHAPE", "MI_ERR_BAD_VOCAB",
           "MI_ERR_BAD_INDICES", "MI_ERR_ALIAS", "MI_ERR_MISALIGNED", "MI_ERR_BAD_VARIANT", "MI_ERR_HIP"]
-VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3}
+VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3, "vec_resident": 4}
 
 # every symbol include/mi_bitmask.h declares
 EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",

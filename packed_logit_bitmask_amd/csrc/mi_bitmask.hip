@@ -268,6 +268,18 @@ mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64
       }, any_out != nullptr);
       return after_launch("inplace_vec");
     }
+    case MI_VARIANT_VEC_RESIDENT: {
+      // cache-resident logits: keep the written lines in L2 (write-back) and
+      // give each lane 16 vectors
+      constexpr int VW = mi::Bits16B<T>::VW;
+      const int64_t per = int64_t(mi::kBlock) * 16;
+      const int64_t chunks = std::max<int64_t>(1, (p.V / VW + per - 1) / per);
+      launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t nrep) {
+        mi::inplace_vec<T, 16, mi::kStoreWriteBack><<<blocks, mi::kBlock, 0, stream>>>(
+            logits, ls, mask, ms, V, W, map, s0, ch, fill, any_out, nrep);
+      }, any_out != nullptr);
+      return after_launch("inplace_vec");
+    }
     case MI_VARIANT_WRONLY: {
       const int64_t chunks = (p.W + 255) / 256;
       launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t) {
@@ -320,7 +332,8 @@ mi_status_t inplace_impl(void* logits, mi_dtype_t dtype, int64_t rows, int64_t c
   if (overlaps(p.mask, p.logits)) return fail(MI_ERR_ALIAS, "mask overlaps logits");
   if (overlaps(p.indices, p.logits)) return fail(MI_ERR_ALIAS, "indices overlap logits");
   if (variant == MI_VARIANT_AUTO) variant = auto_inplace(dtype);
-  if (variant != MI_VARIANT_SCALAR && variant != MI_VARIANT_VEC && variant != MI_VARIANT_WRONLY)
+  if (variant != MI_VARIANT_SCALAR && variant != MI_VARIANT_VEC && variant != MI_VARIANT_WRONLY &&
+      variant != MI_VARIANT_VEC_RESIDENT)
     return fail(MI_ERR_BAD_VARIANT, "unknown in-place variant %d", (int)variant);
   if (p.V == 0 || p.R == 0) return MI_OK;
   if (p.esize == 4) return run_inplace<uint32_t>(logits, ls, mask, ms, indices, p, variant, stream);

@@ -177,6 +177,7 @@ def test_adjacent_buffers_are_not_aliases():
 REJECT_OUT = [
     ("null out", dict(out=None), NULLP),
     ("wronly has no out form", dict(variant=3), VARIANT),
+    ("resident variant has no out form", dict(variant=4), VARIANT),
     ("out stride below cols", dict(os=50), SHAPE),
     ("misaligned out", dict(out=OUT + 1), MISALIGNED),
     ("out overlaps logits", dict(out=LOGITS + 10), ALIAS),

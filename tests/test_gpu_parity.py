@@ -29,7 +29,7 @@ pytestmark = pytest.mark.gpu
 TORCH_DTYPE = {"float32": torch.float32, "float16": torch.float16, "bfloat16": torch.bfloat16}
 INT_VIEW = {"float32": (torch.int32, np.int32, np.uint32), "float16": (torch.int16, np.int16, np.uint16),
             "bfloat16": (torch.int16, np.int16, np.uint16)}
-INPLACE_VARIANTS = ["auto", "scalar", "vec", "wronly"]
+INPLACE_VARIANTS = ["auto", "scalar", "vec", "wronly", "vec_resident"]
 OUT_VARIANTS = ["auto", "scalar", "vec"]
 
 
