@@ -375,8 +375,8 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
 
     Per launch: one token per row from the masked logits.  Bytes counted: one
     read of the logits of every row plus its mask words; the kernel reads the
-    row once per pass (1 pass greedy / unfiltered, 5-6 with top-k or top-p).
-    Cold: rotating buffer sets.
+    row once per pass (greedy 1, unfiltered 2, with top-k or top-p 2 plus one
+    per radix digit: 2 for bf16, 3 for fp16).  Cold: rotating buffer sets.
     """
     import numpy as np
 
@@ -398,10 +398,66 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
                 sets[k % nsets][0], sets[k % nsets][1], wl.vocab_size, seed=1, offset=k, out=tok, **kw),
                 steps, stream)
             res[mode] = {"us_per_call": ms * 1e3, "GBps_one_read": nbytes / (ms * 1e-3) / 1e9}
+            ref_ms = torch_sort_sampler_ms(torch, sets, wl.vocab_size or wl.cols, kw, stream)
+            res[mode]["torch_sort_us_per_call"] = ref_ms * 1e3
+            res[mode]["speedup_vs_torch_sort"] = ref_ms / ms
         out[label] = res
         del sets
         torch.cuda.empty_cache()
     return out
+
+
+def torch_sort_sampler_ms(torch, sets, V, kw, stream, steps=20):
+    """The same draw done the usual way with stock torch ops, for comparison.
+
+    Unpack the bitmask into a bool mask, fill the masked logits with -inf,
+    then: greedy is an argmax; otherwise softmax of z = logit / T, and with
+    top-k or top-p a descending sort, the filters on the sorted
+    probabilities (top-k by rank, top-p on the exclusive cumulative sum,
+    min-p against the largest) and torch.multinomial on what is left;
+    unfiltered draws with torch.multinomial directly.  Rows with nothing
+    allowed draw from a flat row (the fused kernel returns -1 for them).
+    Eager launches on the same rotating buffer sets, timed by HIP events on
+    the stream.
+    """
+    temperature = kw.get("temperature", 1.0)
+    top_k, top_p, min_p = kw.get("top_k", 0), kw.get("top_p", 1.0), kw.get("min_p", 0.0)
+    dev = sets[0][0].device
+    tok_ids = torch.arange(V, device=dev)
+    word, bit = tok_ids // 32, (tok_ids % 32).to(torch.int32)
+
+    def one(k):
+        logits, mask = sets[k % len(sets)]
+        allowed = ((mask[:, word] >> bit) & 1).bool()
+        x = logits[:, :V].float().masked_fill(~allowed, float("-inf"))
+        # a row with nothing allowed would be all NaN after the softmax, which
+        # multinomial rejects: draw such rows from a flat row instead
+        x = torch.where(allowed.any(-1, keepdim=True), x, torch.zeros((), device=dev))
+        if temperature <= 0:
+            return x.argmax(-1)
+        probs = torch.softmax(x / temperature, -1)
+        if not (top_k or top_p < 1.0 or min_p):
+            return torch.multinomial(probs, 1)
+        sp, si = probs.sort(-1, descending=True)
+        if top_k:
+            sp[:, top_k:] = 0
+        if top_p < 1.0:
+            sp = sp.masked_fill(sp.cumsum(-1) - sp > top_p, 0)
+        if min_p:
+            sp = sp.masked_fill(sp < min_p * sp[:, :1], 0)
+        return si.gather(1, torch.multinomial(sp, 1))
+
+    with torch.cuda.stream(stream):
+        for k in range(3):
+            one(k)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for k in range(steps):
+            one(k)
+        e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
 
 
 def host_path(torch, mb, wl, eff, seconds=2.0):

@@ -26,7 +26,9 @@
 //            (Z is the total of the first pass's mass histogram).  Masses
 //            are fixed-point integers (2^31 * exp(z - z_max)), so the sums do
 //            not depend on the order of the atomic adds: the cut is
-//            deterministic.  Both searches share 4 passes of 8-bit digits;
+//            deterministic.  Both searches share the passes, one per 8-bit
+//            digit: 4 for fp32, 3 for fp16, 2 for bf16 (the low digits of a
+//            16-bit type's key are the same for every token of a prefix);
 //   min-p    z - z_max >= ln(min_p), no pass of its own;
 //   draw     Gumbel-max over the kept tokens: key = z - ln(-ln u) (logarithms
 //            by the hardware log2 instruction, rescaled), u from
@@ -54,22 +56,30 @@ struct SampleArgs {
   uint32_t seed_lo, seed_hi, offset_lo, offset_hi;
 };
 
+// kZeroLowBits: low bits of the binary32 pattern that are zero for every
+// value of the type (bf16 keeps 7 fraction bits, fp16 10, subnormals fewer),
+// so radix digits that lie wholly inside them never need a pass.
 struct F32Bits {
   using Bits = uint32_t;
+  static constexpr int kZeroLowBits = 0;
   static __device__ __forceinline__ float value(uint32_t b) { return __uint_as_float(b); }
 };
 struct BF16Bits {
   using Bits = uint16_t;
+  static constexpr int kZeroLowBits = 16;
   static __device__ __forceinline__ float value(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 };
 struct F16Bits {
   using Bits = uint16_t;
+  static constexpr int kZeroLowBits = 13;
   static __device__ __forceinline__ float value(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
 };
 
 // Monotone map from float order to unsigned order (for non-NaN values).
+// -0 takes the key of +0: the two compare equal, so a cut at zero keeps both.
 __device__ __forceinline__ uint32_t order_key(float x) {
-  const uint32_t b = __float_as_uint(x);
+  uint32_t b = __float_as_uint(x);
+  b = b == 0x80000000u ? 0u : b;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
@@ -261,8 +271,13 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // candidate, so its total is the softmax mass Z.
   if (use_k || use_p) {
     if (t == 0) s_sel = SelectState{0u, static_cast<uint32_t>(top_k), 0ull, 0u};
+    // Digits below kLastShift lie in the type's always-zero low bits: every
+    // token of a prefix shares them (all 0 under a positive prefix, all 1
+    // under a negative one, the key complementing negatives), so they are
+    // filled in after the passes instead of counted.
+    constexpr int kLastShift = (D::kZeroLowBits / 8) * 8;
     uint32_t pmask = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 24; shift >= kLastShift; shift -= 8) {
       for (int b = t; b < kWaves * 256; b += THREADS) {
         (&hist_n[0][0])[b] = 0u;
         (&hist_m[0][0])[b] = 0ull;
@@ -329,8 +344,10 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       __syncthreads();
       pmask |= 255u << shift;
     }
-    if (use_k) cut = max(cut, s_sel.prefix_k);
-    if (use_p) cut = max(cut, s_sel.prefix_p);
+    constexpr uint32_t kLow = (1u << kLastShift) - 1u;
+    const auto complete = [&](uint32_t prefix) { return prefix | ((prefix & 0x80000000u) ? 0u : kLow); };
+    if (use_k) cut = max(cut, complete(s_sel.prefix_k));
+    if (use_p) cut = max(cut, complete(s_sel.prefix_p));
   }
   const bool use_min_p = min_p > 0.f;
   const float ln_min_p = use_min_p ? logf(min_p) : 0.f;

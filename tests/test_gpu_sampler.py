@@ -190,3 +190,26 @@ def test_distribution_chi_square():
     say(f"[gpu] chi-square {stat:.1f} on {dof} dof (z = {zscore:.2f})")
     assert zscore < 4.75
     assert np.abs(counts / toks.size - probs).max() < 0.01
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_signed_zero_ties_at_the_cut(dtype):
+    """A top-k cut that falls on zero keeps +0 and -0 alike (they compare equal)."""
+    R, cols = 64, 96
+    x = np.full(cols, -3.0, np.float32)
+    x[0] = 2.0
+    x[1] = 0.0
+    x[2:22] = -0.0                    # twenty negative zeros after one positive zero
+    bits = np.repeat(x[None, :], R, axis=0)
+    if dtype == "float32":
+        bits = bits.view(np.uint32)
+    elif dtype == "float16":
+        bits = bits.astype(np.float16).view(np.uint16)
+    else:
+        bits = (bits.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    say(f"[gpu] sampler signed-zero ties {dtype}")
+    tok = check_rows(bits, dtype, None, None, 1.0, 2, 1.0, 0.0, seed=21, offset=0)
+    assert ((tok >= 2) & (tok < 22)).sum() > R // 4, "negative zeros were cut"
+    assert tok.max() < 22
+    tok = check_rows(bits, dtype, None, None, 1.0, 0, 0.3, 0.0, seed=22, offset=1)
+    assert tok.max() < 22
