@@ -183,7 +183,7 @@ mi_status_t mi_apply_bitmask_out_ex(
  * is never drawn.  With a mask the vocab-size rule and mask_rows >= rows
  * are those of the apply; without one (mask == NULL, mask_* ignored)
  * V = vocab_size, or cols when vocab_size == -1.  A row with no candidate
- * gets token -1.
+ * gets token -1.  V above 2^28 is rejected with MI_ERR_BAD_SHAPE.
  *
  * Randomness: Philox4x32-10 (Salmon et al., SC 2011) with key (seed low,
  * seed high) and, for token v of row r, counter (v / 4, r, offset low,

@@ -38,6 +38,7 @@ mi_status_t fail(mi_status_t status, const char* fmt, ...) {
 // Limits keep every index computation inside int32 (within a row) and
 // int64 (across rows), and the grid inside what one launch can carry.
 constexpr int64_t kMaxCols = int64_t(1) << 30;
+constexpr int64_t kMaxSampleVocab = int64_t(1) << 28;
 constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxPitch = int64_t(1) << 40;
 constexpr int64_t kMaxBytes = int64_t(1) << 56;
@@ -593,6 +594,8 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     st = check_logits_only(logits, dtype, rows, cols, logits_row_stride, vocab_size, &p);
   }
   if (st != MI_OK) return st;
+  // the kernel addresses a row through 32-bit byte offsets
+  if (p.V > kMaxSampleVocab) return fail(MI_ERR_BAD_SHAPE, "vocab size above 2^28 (the sampler's limit)");
   ByteRange tb;
   if (!extent(tokens, tokens ? 1 : 0, rows, rows, 8, &tb)) return fail(MI_ERR_BAD_SHAPE, "tokens extent overflows");
   if (reinterpret_cast<uintptr_t>(tokens) % 8) return fail(MI_ERR_MISALIGNED, "tokens not 8-byte aligned");

@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "apply_kernels.h"  // raw buffer resources (Rsrc, make_rsrc, load_word, load16, kSkip)
+
 namespace mi {
 
 struct SampleArgs {
@@ -108,68 +110,114 @@ __device__ __forceinline__ float unit_uniform(uint32_t x) {
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & 63; }
 
 
-// One row's logits and mask, read 8 consecutive tokens at a time.
+// One row's logits and mask, read 8 consecutive tokens (a group) at a time.
+// The loads go through raw buffer resources that end at the row's vocab
+// size (logits) and its last mask word, so a load for a group past the end
+// gets an out-of-range offset and returns 0 instead of branching: the
+// compiler then issues every load of a batch before the first wait.  A row
+// without a mask has a resource of size 0 and all tokens below V count.
 template <typename D>
 struct RowView {
-  const typename D::Bits* row;
-  const uint32_t* mrow;   // nullptr: no mask
+  using Bits = typename D::Bits;
+  const Bits* row;
+  bool has_mask;
   int32_t V;
-  bool aligned;           // row start 16-byte aligned: whole groups load as vectors
+  bool aligned;   // row start 16-byte aligned: whole groups load as vectors
+  Rsrc rl, rm;
 
-  // Tokens i0..i0+7 (i0 a multiple of 8): values and a bit per token that
-  // is a candidate (below V, mask bit set, finite logit).
-  __device__ __forceinline__ uint32_t load8(int32_t i0, float x[8]) const {
-    uint32_t bits = 0;
-    if (i0 < V) {
-      bits = mrow ? (mrow[i0 >> 5] >> (static_cast<uint32_t>(i0) & 31u)) & 0xFFu : 0xFFu;
-      if (aligned && i0 + 8 <= V) {
-        if constexpr (sizeof(typename D::Bits) == 2) {
-          const uint4 v = *reinterpret_cast<const uint4*>(row + i0);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  __device__ __forceinline__ RowView(const Bits* row_, const uint32_t* mrow, int32_t V_)
+      : row(row_), has_mask(mrow != nullptr), V(V_), aligned((reinterpret_cast<uintptr_t>(row_) & 15u) == 0),
+        rl(make_rsrc(row_, static_cast<uint32_t>(V_) * sizeof(Bits))),
+        rm(make_rsrc(mrow, mrow ? static_cast<uint32_t>((V_ + 31) / 32) * 4u : 0u)) {}
+
+  // Group g's values and a bit per token that is a candidate (mask bit set,
+  // finite logit); `full` says the whole group lies below V (else ok = 0).
+  template <bool VEC>
+  __device__ __forceinline__ uint32_t load8(int32_t g, bool full, float x[8]) const {
+    const uint32_t w = load_word(rm, full ? (g >> 2) * 4 : kSkip);
+    const uint32_t bits = has_mask ? (w >> ((g & 3) * 8)) & 0xFFu : 0xFFu;
+    if constexpr (sizeof(Bits) == 2) {
+      if constexpr (VEC) {
+        const uint4 v = load16(rl, full ? g * 16 : kSkip);
+        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            x[2 * q] = D::value(static_cast<typename D::Bits>(w[q] & 0xFFFFu));
-            x[2 * q + 1] = D::value(static_cast<typename D::Bits>(w[q] >> 16));
-          }
-        } else {
-          const uint4 a = *reinterpret_cast<const uint4*>(row + i0);
-          const uint4 b = *reinterpret_cast<const uint4*>(row + i0 + 4);
-          const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-          for (int q = 0; q < 8; ++q) x[q] = D::value(w[q]);
+        for (int q = 0; q < 4; ++q) {
+          x[2 * q] = D::value(static_cast<Bits>(u[q] & 0xFFFFu));
+          x[2 * q + 1] = D::value(static_cast<Bits>(u[q] >> 16));
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) x[q] = i0 + q < V ? D::value(row[i0 + q]) : 0.f;
+        for (int q = 0; q < 8; ++q)
+          x[q] = D::value(static_cast<Bits>(__builtin_amdgcn_raw_buffer_load_b16(rl, full ? (8 * g + q) * 2 : kSkip, 0, 0)));
+      }
+    } else {
+      if constexpr (VEC) {
+        const uint4 a = load16(rl, full ? g * 32 : kSkip);
+        const uint4 b = load16(rl, full ? g * 32 + 16 : kSkip);
+        const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = D::value(u[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = D::value(load_word(rl, full ? (8 * g + q) * 4 : kSkip));
       }
     }
     uint32_t ok = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      if (((bits >> q) & 1u) && i0 + q < V && __builtin_isfinite(x[q])) ok |= 1u << q;
+      if (((bits >> q) & 1u) && __builtin_isfinite(x[q])) ok |= 1u << q;
+    return full ? ok : 0u;
+  }
+
+  // The last, partial group (tokens 8 * (V / 8) .. V - 1), by plain loads.
+  __device__ __forceinline__ uint32_t load_tail(float x[8]) const {
+    const int32_t i0 = V & ~7;
+    uint32_t ok = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      x[q] = 0.f;
+      if (i0 + q < V) {
+        x[q] = D::value(row[i0 + q]);
+        const bool bit = has_mask ? ((load_word(rm, ((i0 + q) >> 5) * 4) >> ((i0 + q) & 31)) & 1u) : true;
+        if (bit && __builtin_isfinite(x[q])) ok |= 1u << q;
+      }
+    }
     return ok;
   }
 };
 
-// Walk the row: f(i0, x[8], ok) for every 8-token group, IN_FLIGHT groups
-// loaded before any is used (4 keeps 64 bytes of 16-bit logits in flight per
-// thread; 2 halves the registers so more rows share a compute unit).  The
-// trip count is the same for every thread of the block (groups past the row
-// come with ok == 0).
-template <int IN_FLIGHT, int THREADS, typename D, typename F>
-__device__ __forceinline__ void walk_row(const RowView<D>& rv, F&& f) {
-  const int32_t ngroups = (rv.V + 7) / 8;
+template <int IN_FLIGHT, int THREADS, bool VEC, typename D, typename F>
+__device__ __forceinline__ void walk_groups(const RowView<D>& rv, F& f) {
+  const int32_t nfull = rv.V >> 3;
   const int t = static_cast<int>(threadIdx.x);
-  for (int32_t base = 0; base < ngroups; base += IN_FLIGHT * THREADS) {
+  for (int32_t base = 0; base < nfull; base += IN_FLIGHT * THREADS) {
     float x[IN_FLIGHT][8];
     uint32_t ok[IN_FLIGHT];
 #pragma unroll
     for (int j = 0; j < IN_FLIGHT; ++j) {
       const int32_t g = base + j * THREADS + t;
-      ok[j] = g < ngroups ? rv.load8(8 * g, x[j]) : 0u;
+      ok[j] = rv.template load8<VEC>(g, g < nfull, x[j]);
     }
 #pragma unroll
     for (int j = 0; j < IN_FLIGHT; ++j) f(8 * (base + j * THREADS + t), x[j], ok[j]);
+  }
+}
+
+// Walk the row: f(i0, x[8], ok) for every 8-token group, IN_FLIGHT groups
+// loaded before any is used (4 keeps 64 bytes of 16-bit logits in flight per
+// thread; 2 halves the registers so more rows share a compute unit).  Every
+// thread of the block calls f the same number of times (groups it does not
+// own come with ok == 0), so f may hold block-uniform control flow.
+template <int IN_FLIGHT, int THREADS, typename D, typename F>
+__device__ __forceinline__ void walk_row(const RowView<D>& rv, F&& f) {
+  if (rv.aligned)
+    walk_groups<IN_FLIGHT, THREADS, true>(rv, f);
+  else
+    walk_groups<IN_FLIGHT, THREADS, false>(rv, f);
+  if (rv.V & 7) {
+    float x[8] = {};
+    const uint32_t ok = threadIdx.x == 0 ? rv.load_tail(x) : 0u;
+    f(rv.V & ~7, x, ok);
   }
 }
 
@@ -209,7 +257,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   const int t = static_cast<int>(threadIdx.x);
   const int wave = t >> 6;
   const typename D::Bits* row = logits + r * ls;
-  const RowView<D> rv{row, mask ? mask + r * ms : nullptr, V, (reinterpret_cast<uintptr_t>(row) & 15u) == 0};
+  const RowView<D> rv(row, mask ? mask + r * ms : nullptr, V);
 
   const float temp = a.temperature ? a.temperature[r] : a.temperature_all;
   const int32_t top_k = a.top_k ? a.top_k[r] : a.top_k_all;

@@ -230,3 +230,44 @@ REJECT_ROWS = [
 def test_rows_rejections(name, kw, code):
     assert rows_call(**kw) == code
     assert mb.load_library().mi_last_error_message().decode()
+
+
+def sample_call(**kw):
+    a = dict(logits=LOGITS, dtype=2, rows=4, cols=100, ls=100, mask=MASK, mask_rows=4, mask_cols=4, ms=4,
+             vocab=-1, tokens=OUT, params=True)
+    a.update(kw)
+    prm = _binding.SampleParams()
+    prm.temperature_all, prm.top_k_all, prm.top_p_all, prm.min_p_all = 1.0, 0, 1.0, 0.0
+    for name in ("temperature", "top_k", "top_p", "min_p"):
+        if name in kw:
+            setattr(prm, name, kw[name])
+    return mb.load_library().mi_apply_bitmask_sample(
+        a["logits"], a["dtype"], a["rows"], a["cols"], a["ls"], a["mask"], a["mask_rows"], a["mask_cols"],
+        a["ms"], a["vocab"], ctypes.byref(prm) if a["params"] else None, a["tokens"], None)
+
+
+REJECT_SAMPLE = [
+    ("null params", dict(params=False), NULLP),
+    ("null tokens", dict(tokens=None), NULLP),
+    ("null logits", dict(logits=None), NULLP),
+    ("bad dtype", dict(dtype=7), DTYPE),
+    ("too few mask rows", dict(mask_rows=3), SHAPE),
+    ("vocab too large for the mask", dict(vocab=129), VOCAB),
+    ("vocab above 2^28 without a mask", dict(mask=None, rows=1, cols=(1 << 28) + 8, ls=(1 << 28) + 8,
+                                             vocab=(1 << 28) + 1), SHAPE),
+    ("tokens inside logits", dict(tokens=LOGITS + 16), ALIAS),
+    ("tokens inside mask", dict(tokens=MASK + 8), ALIAS),
+    ("tokens misaligned", dict(tokens=OUT + 4), MISALIGNED),
+    ("per-row temperature misaligned", dict(temperature=IDX + 2), MISALIGNED),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", REJECT_SAMPLE, ids=[r[0] for r in REJECT_SAMPLE])
+def test_sample_rejections(name, kw, code):
+    assert sample_call(**kw) == code
+    assert mb.load_library().mi_last_error_message().decode()
+
+
+def test_sample_accepts_the_largest_vocab_at_the_checks():
+    """2^28 passes the size checks; with zero rows nothing is launched."""
+    assert sample_call(mask=None, rows=0, cols=1 << 28, ls=1 << 28, vocab=1 << 28) == OK

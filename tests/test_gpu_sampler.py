@@ -213,3 +213,35 @@ def test_signed_zero_ties_at_the_cut(dtype):
     assert tok.max() < 22
     tok = check_rows(bits, dtype, None, None, 1.0, 0, 0.3, 0.0, seed=22, offset=1)
     assert tok.max() < 22
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_misaligned_rows_and_ragged_tail(dtype):
+    """Rows that start off a 16-byte boundary (odd row length, and a view one
+    element into the buffer) and a vocab size that leaves a partial last
+    group of 8 tokens."""
+    rng = np.random.default_rng(8)
+    R, cols, V = 24, 4099, 4093
+    full = random_logits(rng, dtype, R, cols + 1)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.4, (cols + 31) // 32, rng)
+    ndt, tdt = TORCH[dtype]
+    dl = torch.from_numpy(np.ascontiguousarray(full).view(ndt)).to("cuda").view(tdt)[:, 1:]
+    assert dl.data_ptr() % 16 != 0
+    dm = torch.from_numpy(mask).to("cuda")
+    bits = np.ascontiguousarray(full[:, 1:])
+    vals = values64(bits, dtype)
+    say(f"[gpu] sampler misaligned rows {dtype}")
+    for (T, k, p, m) in ((0.0, 0, 1.0, 0.0), (1.0, 0, 1.0, 0.0), (0.9, 30, 1.0, 0.0), (1.1, 0, 0.8, 0.02)):
+        tok = mb.mi_apply_bitmask_sample(dl, dm, V, temperature=T, top_k=k, top_p=p, min_p=m, seed=4,
+                                         offset=2).cpu().numpy()
+        exact = 0
+        for r in range(R):
+            allowed = S.allowed_tokens(mask[r], V, cols)
+            want, det = S.sample_row(vals[r], allowed, T, k, p, m, 4, 2, r, margin=MARGIN)
+            assert tok[r] in det["candidates"], (T, k, p, m, r, tok[r], want)
+            exact += int(tok[r] == want)
+        assert exact >= R - 1
+        # a contiguous copy (other row alignments) gives the same tokens
+        again = mb.mi_apply_bitmask_sample(dl.contiguous(), dm, V, temperature=T, top_k=k, top_p=p, min_p=m,
+                                           seed=4, offset=2).cpu().numpy()
+        assert np.array_equal(tok, again)
