@@ -17,7 +17,9 @@
 // are uniform across the block.
 //
 //   pass 1   max logit and its (lowest) index, count of candidate tokens
-//            -> greedy rows and rows with no candidate end here;
+//            -> greedy rows and rows with no candidate end here; skipped
+//            when the row uses neither top-p nor min-p (nothing else needs
+//            it);
 //   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
@@ -92,14 +94,16 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c[0]), lo0 = 0xD2511F53u * c[0];
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c[2]), lo1 = 0xCD9E8D57u * c[2];
-    const uint32_t n0 = hi1 ^ c[1] ^ k0;
-    const uint32_t n2 = hi0 ^ c[3] ^ k1;
+    // each product as one 64-bit multiply: one v_mad_u64_u32 instead of a
+    // v_mul_hi_u32 / v_mul_lo_u32 pair (a third faster on gfx950)
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c[0];
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c[2];
+    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c[3] ^ k1;
     c[0] = n0;
-    c[1] = lo1;
+    c[1] = static_cast<uint32_t>(p1);
     c[2] = n2;
-    c[3] = lo0;
+    c[3] = static_cast<uint32_t>(p0);
   }
 }
 
@@ -264,53 +268,60 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   const float top_p = a.top_p ? a.top_p[r] : a.top_p_all;
   const float min_p = a.min_p ? a.min_p[r] : a.min_p_all;
 
-  // ---- pass 1: max, argmax (lowest index), candidate count
+  // ---- pass 1: max, argmax (lowest index), candidate count.  Greedy rows
+  // need the argmax, top-p and min-p need the max logit (their masses and
+  // cutoffs are relative to it); without those the pass is skipped: the
+  // Gumbel keys need no max, and top-k needs no count (a k at or above the
+  // number of candidates comes out of the radix search as "keep all").
+  const bool first_pass = !(temp > 0.f) || top_p < 1.0f || min_p > 0.f;
   float best = -__builtin_inff();
-  int32_t besti = 0x7FFFFFFF;
   uint32_t count = 0;
-  walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
-    count += __builtin_popcount(ok);
+  if (first_pass) {
+    int32_t besti = 0x7FFFFFFF;
+    walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+      count += __builtin_popcount(ok);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (((ok >> q) & 1u) && x[q] > best) {  // strictly greater: each thread sees its tokens in order
-        best = x[q];
-        besti = i0 + q;
+      for (int q = 0; q < 8; ++q)
+        if (((ok >> q) & 1u) && x[q] > best) {  // strictly greater: each thread sees its tokens in order
+          best = x[q];
+          besti = i0 + q;
+        }
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ob = __shfl_xor(best, o);
+      const int32_t oi = __shfl_xor(besti, o);
+      if (ob > best || (ob == best && oi < besti)) {
+        best = ob;
+        besti = oi;
       }
-  });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ob = __shfl_xor(best, o);
-    const int32_t oi = __shfl_xor(besti, o);
-    if (ob > best || (ob == best && oi < besti)) {
-      best = ob;
-      besti = oi;
+      count += __shfl_xor(count, o);
     }
-    count += __shfl_xor(count, o);
-  }
-  if (lane_id() == 0) {
-    s_best[wave] = best;
-    s_besti[wave] = besti;
-    s_count[wave] = count;
-  }
-  __syncthreads();
-  best = s_best[0];
-  besti = s_besti[0];
-  count = s_count[0];
-  for (int w = 1; w < kWaves; ++w) {
-    if (s_best[w] > best || (s_best[w] == best && s_besti[w] < besti)) {
-      best = s_best[w];
-      besti = s_besti[w];
+    if (lane_id() == 0) {
+      s_best[wave] = best;
+      s_besti[wave] = besti;
+      s_count[wave] = count;
     }
-    count += s_count[w];
-  }
-  if (count == 0 || !(temp > 0.f)) {  // no candidate, or greedy
-    if (t == 0) out[r] = count == 0 ? -1 : besti;
-    return;
+    __syncthreads();
+    best = s_best[0];
+    besti = s_besti[0];
+    count = s_count[0];
+    for (int w = 1; w < kWaves; ++w) {
+      if (s_best[w] > best || (s_best[w] == best && s_besti[w] < besti)) {
+        best = s_best[w];
+        besti = s_besti[w];
+      }
+      count += s_count[w];
+    }
+    if (count == 0 || !(temp > 0.f)) {  // no candidate, or greedy
+      if (t == 0) out[r] = count == 0 ? -1 : besti;
+      return;
+    }
   }
 
   const float inv_t = 1.0f / temp;
-  const float zmax = best * inv_t;
-  const bool use_k = top_k > 0 && static_cast<uint32_t>(top_k) < count;
+  const float zmax = best * inv_t;  // used only when the first pass ran
+  const bool use_k = top_k > 0 && (!first_pass || static_cast<uint32_t>(top_k) < count);
   const bool use_p = top_p < 1.0f;
   uint32_t cut = 0;  // keep tokens with order_key(x) >= cut
 
@@ -422,7 +433,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         // -ln u = -log2(u) * ln 2, then -ln(that) = -log2(that) * ln 2
         const float u = unit_uniform(q < 4 ? c0[q] : c1[q - 4]);
         const float e = -__log2f(u) * 0.6931471805599453f;
-        const float key = x[q] * inv_t - __log2f(e) * 0.6931471805599453f;
+        // clamped so an overflowed z (a tiny temperature) still draws a token
+        const float key = fmaxf(x[q] * inv_t - __log2f(e) * 0.6931471805599453f, -__FLT_MAX__);
         if (key > bk) {
           bk = key;
           bi = i0 + q;
@@ -451,8 +463,9 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         bk = s_best[w];
         bi = s_besti[w];
       }
-    // the max-logit token always survives every cut, so bi is set
-    out[r] = bi == 0x7FFFFFFF ? besti : bi;
+    // every kept token has a key above -inf, and a row with a candidate
+    // keeps at least its largest logit: bi is unset only without candidates
+    out[r] = bi == 0x7FFFFFFF ? -1 : bi;
   }
 }
 

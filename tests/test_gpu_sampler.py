@@ -245,3 +245,23 @@ def test_misaligned_rows_and_ragged_tail(dtype):
         again = mb.mi_apply_bitmask_sample(dl.contiguous(), dm, V, temperature=T, top_k=k, top_p=p, min_p=m,
                                            seed=4, offset=2).cpu().numpy()
         assert np.array_equal(tok, again)
+
+
+@pytest.mark.parametrize("T,k,p,m", [(0.0, 0, 1.0, 0.0), (1.0, 0, 1.0, 0.0), (1.0, 7, 1.0, 0.0),
+                                      (1.0, 0, 0.9, 0.0), (1.0, 0, 1.0, 0.1), (0.7, 7, 0.9, 0.1)])
+def test_rows_without_candidates_draw_minus_one(T, k, p, m):
+    """Every mode (some skip the max pass) returns -1 for a row with nothing
+    allowed: an all-zero mask row, or allowed tokens whose logits are all
+    -inf; a single allowed token is always drawn."""
+    rng = np.random.default_rng(9)
+    R, cols = 16, 777
+    x = rng.standard_normal((R, cols)).astype(np.float32)
+    allowed = rng.random((R, cols)) < 0.5
+    allowed[3] = False
+    x[7, allowed[7]] = -np.inf
+    allowed[11] = False
+    allowed[11, 500] = True
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    say(f"[gpu] sampler empty rows T={T} k={k} p={p} m={m}")
+    tok = check_rows(x.view(np.uint32), "float32", mask, None, T, k, p, m, seed=2, offset=5, min_exact=1.0)
+    assert tok[3] == -1 and tok[7] == -1 and tok[11] == 500
