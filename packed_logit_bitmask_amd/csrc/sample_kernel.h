@@ -233,6 +233,54 @@ struct SelectState {
   uint32_t prefix_p;
 };
 
+// One wave's view of a 256-bin histogram for the radix search: lane l
+// holds bins 4l .. 4l+3, and a shuffle scan gives every lane the suffix
+// total S(4l) = hist[4l] + ... + hist[255].
+template <typename T>
+struct WaveSuffix {
+  T h[4];
+  T incl;  // S(4l)
+
+  __device__ __forceinline__ explicit WaveSuffix(const T* hist) {
+    const int l = lane_id();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = hist[4 * l + j];
+    incl = h[0] + h[1] + h[2] + h[3];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const T v = __shfl_down(incl, o);
+      if (l + o < 64) incl += v;
+    }
+  }
+
+  __device__ __forceinline__ T total() const { return __shfl(incl, 0); }
+
+  // The digit d the search takes: the largest d >= 1 with S(d) >= need,
+  // else 0; and S(d + 1), the total of the bins above it.
+  __device__ __forceinline__ void pick(T need, int* d, T* above) const {
+    const int l = lane_id();
+    const uint64_t m = __ballot(incl >= need);   // lanes 0 .. L, as S falls with l
+    const int L = m ? 63 - __clzll(static_cast<long long>(m)) : 0;
+    T s = incl - (h[0] + h[1] + h[2] + h[3]);  // S(4l + 4), the bins above this lane
+    int j = 0;
+    T ab = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = 3; q >= 1; --q) {
+      const T next = s + h[q];
+      if (!found && next >= need) {
+        j = q;
+        ab = s;
+        found = true;
+      }
+      s = next;
+    }
+    if (!found) ab = s;  // j = 0: the bins above bin 4l
+    *d = __shfl(4 * l + j, L);
+    *above = __shfl(ab, L);
+  }
+};
+
 // Dynamic LDS the kernel needs when a row may use top-k or top-p (the
 // per-wave histograms); 0 otherwise.
 constexpr size_t sample_hist_bytes(int threads) {
@@ -369,36 +417,33 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         hist_m[0][b] = m;
       }
       __syncthreads();
-      if (t == 0) {
-        SelectState st = s_sel;
-        if (use_k) {
-          uint32_t cum = 0;
-          int d = 255;
-          for (; d > 0; --d) {
-            if (cum + hist_n[0][d] >= st.need_k) break;
-            cum += hist_n[0][d];
-          }
-          st.prefix_k |= static_cast<uint32_t>(d) << shift;
-          st.need_k -= cum;
+      // both searches pick their digit at once: top-k on wave 0, top-p on
+      // wave 1 (different fields of s_sel)
+      if (use_k && wave == 0) {
+        const WaveSuffix<uint32_t> ws(&hist_n[0][0]);
+        int d;
+        uint32_t above;
+        ws.pick(s_sel.need_k, &d, &above);
+        if (lane_id() == 0) {
+          s_sel.prefix_k |= static_cast<uint32_t>(d) << shift;
+          s_sel.need_k -= above;
         }
-        if (use_p) {
-          if (shift == 24) {  // every candidate is in this histogram: its total is Z
-            unsigned long long z = 0;
-            for (int b = 0; b < 256; ++b) z += hist_m[0][b];
-            unsigned long long target =
-                static_cast<unsigned long long>(ceil(static_cast<double>(top_p) * static_cast<double>(z)));
-            st.need_p = target ? target : 1ull;
-          }
-          unsigned long long cum = 0;
-          int d = 255;
-          for (; d > 0; --d) {
-            if (cum + hist_m[0][d] >= st.need_p) break;
-            cum += hist_m[0][d];
-          }
-          st.prefix_p |= static_cast<uint32_t>(d) << shift;
-          st.need_p -= cum;
+      }
+      if (use_p && wave == 1) {
+        const WaveSuffix<unsigned long long> ws(&hist_m[0][0]);
+        unsigned long long need = s_sel.need_p;
+        if (shift == 24) {  // every candidate is in this histogram: its total is Z
+          const unsigned long long target =
+              static_cast<unsigned long long>(ceil(static_cast<double>(top_p) * static_cast<double>(ws.total())));
+          need = target ? target : 1ull;
         }
-        s_sel = st;
+        int d;
+        unsigned long long above;
+        ws.pick(need, &d, &above);
+        if (lane_id() == 0) {
+          s_sel.prefix_p |= static_cast<uint32_t>(d) << shift;
+          s_sel.need_p = need - above;
+        }
       }
       __syncthreads();
       pmask |= 255u << shift;
