@@ -630,19 +630,19 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     const bool deep = n <= 256;
     const int threads = deep ? 1024 : 256;
     const size_t lds = may_filter ? mi::sample_hist_bytes(threads) : 0;
-#define MI_SAMPLE(TAG, BITS, DEPTH, THREADS)                                                                   \
-  mi::sample_rows<TAG, DEPTH, THREADS><<<n, THREADS, lds, stream>>>(reinterpret_cast<const BITS*>(lg),          \
+#define MI_SAMPLE(TAG, BITS, BYTES, THREADS)                                                                   \
+  mi::sample_rows<TAG, BYTES, THREADS><<<n, THREADS, lds, stream>>>(reinterpret_cast<const BITS*>(lg),          \
                                                                     logits_row_stride, mk, mask_row_stride, V,   \
                                                                     ar, r0, tokens + r0)
     switch (dtype) {
       case MI_DTYPE_F32:
-        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 4, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 2, 256);
+        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 64, 256);
         break;
       case MI_DTYPE_F16:
-        if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 4, 1024); else MI_SAMPLE(mi::F16Bits, uint16_t, 2, 256);
+        if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::F16Bits, uint16_t, 64, 256);
         break;
       default:
-        if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 4, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 2, 256);
+        if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 64, 256);
     }
 #undef MI_SAMPLE
   }

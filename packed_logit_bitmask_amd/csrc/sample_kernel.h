@@ -134,37 +134,68 @@ struct RowView {
         rl(make_rsrc(row_, static_cast<uint32_t>(V_) * sizeof(Bits))),
         rm(make_rsrc(mrow, mrow ? static_cast<uint32_t>((V_ + 31) / 32) * 4u : 0u)) {}
 
-  // Group g's values and a bit per token that is a candidate (mask bit set,
-  // finite logit); `full` says the whole group lies below V (else ok = 0).
+  // A group as loaded: its mask word and its logits as raw 32-bit words
+  // (2 tokens per word for 16-bit types), so a batch in flight costs 5 or 9
+  // registers per group rather than 8 decoded floats.
+  struct Raw {
+    uint32_t w;
+    uint32_t v[sizeof(Bits) == 2 ? 4 : 8];
+  };
+
+  // Issue group g's loads; `full` says the whole group lies below V (else
+  // every load takes the out-of-range offset and returns 0).
   template <bool VEC>
-  __device__ __forceinline__ uint32_t load8(int32_t g, bool full, float x[8]) const {
-    const uint32_t w = load_word(rm, full ? (g >> 2) * 4 : kSkip);
-    const uint32_t bits = has_mask ? (w >> ((g & 3) * 8)) & 0xFFu : 0xFFu;
+  __device__ __forceinline__ Raw load_raw(int32_t g, bool full) const {
+    Raw r;
+    r.w = load_word(rm, full ? (g >> 2) * 4 : kSkip);
     if constexpr (sizeof(Bits) == 2) {
       if constexpr (VEC) {
         const uint4 v = load16(rl, full ? g * 16 : kSkip);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          x[2 * q] = D::value(static_cast<Bits>(u[q] & 0xFFFFu));
-          x[2 * q + 1] = D::value(static_cast<Bits>(u[q] >> 16));
-        }
+        r.v[0] = v.x;
+        r.v[1] = v.y;
+        r.v[2] = v.z;
+        r.v[3] = v.w;
       } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          x[q] = D::value(static_cast<Bits>(__builtin_amdgcn_raw_buffer_load_b16(rl, full ? (8 * g + q) * 2 : kSkip, 0, 0)));
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rl, full ? (8 * g + 2 * q) * 2 : kSkip, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rl, full ? (8 * g + 2 * q + 1) * 2 : kSkip, 0, 0);
+          r.v[q] = lo | (hi << 16);
+        }
       }
     } else {
       if constexpr (VEC) {
         const uint4 a = load16(rl, full ? g * 32 : kSkip);
         const uint4 b = load16(rl, full ? g * 32 + 16 : kSkip);
-        const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q) x[q] = D::value(u[q]);
+        r.v[0] = a.x;
+        r.v[1] = a.y;
+        r.v[2] = a.z;
+        r.v[3] = a.w;
+        r.v[4] = b.x;
+        r.v[5] = b.y;
+        r.v[6] = b.z;
+        r.v[7] = b.w;
       } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) x[q] = D::value(load_word(rl, full ? (8 * g + q) * 4 : kSkip));
+        for (int q = 0; q < 8; ++q) r.v[q] = load_word(rl, full ? (8 * g + q) * 4 : kSkip);
       }
+    }
+    return r;
+  }
+
+  // Group g's values and a bit per token that is a candidate (mask bit set,
+  // finite logit); 0 for a group past the full ones.
+  __device__ __forceinline__ uint32_t decode(const Raw& r, int32_t g, bool full, float x[8]) const {
+    const uint32_t bits = has_mask ? (r.w >> ((g & 3) * 8)) & 0xFFu : 0xFFu;
+    if constexpr (sizeof(Bits) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * q] = D::value(static_cast<Bits>(r.v[q] & 0xFFFFu));
+        x[2 * q + 1] = D::value(static_cast<Bits>(r.v[q] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = D::value(r.v[q]);
     }
     uint32_t ok = 0;
 #pragma unroll
@@ -190,34 +221,42 @@ struct RowView {
   }
 };
 
-template <int IN_FLIGHT, int THREADS, bool VEC, typename D, typename F>
+template <int BYTES, int THREADS, bool VEC, typename D, typename F>
 __device__ __forceinline__ void walk_groups(const RowView<D>& rv, F& f) {
+  // groups in flight per thread: BYTES of logits (the misaligned path, with
+  // one load per token, keeps at most 4)
+  constexpr int kFull = BYTES / (8 * static_cast<int>(sizeof(typename D::Bits)));
+  constexpr int kInFlight = VEC ? kFull : (kFull < 4 ? kFull : 4);
   const int32_t nfull = rv.V >> 3;
   const int t = static_cast<int>(threadIdx.x);
-  for (int32_t base = 0; base < nfull; base += IN_FLIGHT * THREADS) {
-    float x[IN_FLIGHT][8];
-    uint32_t ok[IN_FLIGHT];
+  for (int32_t base = 0; base < nfull; base += kInFlight * THREADS) {
+    typename RowView<D>::Raw raw[kInFlight];
 #pragma unroll
-    for (int j = 0; j < IN_FLIGHT; ++j) {
+    for (int j = 0; j < kInFlight; ++j) {
       const int32_t g = base + j * THREADS + t;
-      ok[j] = rv.template load8<VEC>(g, g < nfull, x[j]);
+      raw[j] = rv.template load_raw<VEC>(g, g < nfull);
     }
 #pragma unroll
-    for (int j = 0; j < IN_FLIGHT; ++j) f(8 * (base + j * THREADS + t), x[j], ok[j]);
+    for (int j = 0; j < kInFlight; ++j) {
+      const int32_t g = base + j * THREADS + t;
+      float x[8];
+      const uint32_t ok = rv.decode(raw[j], g, g < nfull, x);
+      f(8 * g, x, ok);
+    }
   }
 }
 
-// Walk the row: f(i0, x[8], ok) for every 8-token group, IN_FLIGHT groups
-// loaded before any is used (4 keeps 64 bytes of 16-bit logits in flight per
-// thread; 2 halves the registers so more rows share a compute unit).  Every
-// thread of the block calls f the same number of times (groups it does not
-// own come with ok == 0), so f may hold block-uniform control flow.
-template <int IN_FLIGHT, int THREADS, typename D, typename F>
+// Walk the row: f(i0, x[8], ok) for every 8-token group, BYTES of logits
+// per thread loaded before any is used (128 when a compute unit holds one
+// row; 64 when several rows share it, for fewer registers).  Every thread of
+// the block calls f the same number of times (groups it does not own come
+// with ok == 0), so f may hold block-uniform control flow.
+template <int BYTES, int THREADS, typename D, typename F>
 __device__ __forceinline__ void walk_row(const RowView<D>& rv, F&& f) {
   if (rv.aligned)
-    walk_groups<IN_FLIGHT, THREADS, true>(rv, f);
+    walk_groups<BYTES, THREADS, true>(rv, f);
   else
-    walk_groups<IN_FLIGHT, THREADS, false>(rv, f);
+    walk_groups<BYTES, THREADS, false>(rv, f);
   if (rv.V & 7) {
     float x[8] = {};
     const uint32_t ok = threadIdx.x == 0 ? rv.load_tail(x) : 0u;
@@ -287,10 +326,12 @@ constexpr size_t sample_hist_bytes(int threads) {
   return static_cast<size_t>(threads / 64) * 256 * (sizeof(uint32_t) + sizeof(unsigned long long));
 }
 
-// One block of THREADS threads per row.  1024 threads with IN_FLIGHT 4 when
-// each compute unit holds one row at a time; 256 threads with IN_FLIGHT 2 so
-// several rows share a compute unit when there are many rows.
-template <typename D, int IN_FLIGHT, int THREADS>
+// One block of THREADS threads per row.  1024 threads with 128 bytes of
+// logits in flight per thread when each compute unit holds one row at a
+// time; 256 threads with 64 bytes so several rows share a compute unit when
+// there are many rows.  The draw, whose per-group work is heavy, keeps half
+// as much in flight.
+template <typename D, int BYTES, int THREADS>
 __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
                                                               const uint32_t* __restrict__ mask, int64_t ms,
                                                               int32_t V, SampleArgs a, int64_t row_base,
@@ -326,7 +367,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   uint32_t count = 0;
   if (first_pass) {
     int32_t besti = 0x7FFFFFFF;
-    walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+    walk_row<BYTES, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
       count += __builtin_popcount(ok);
 #pragma unroll
       for (int q = 0; q < 8; ++q)
@@ -391,7 +432,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       }
       __syncthreads();
       const uint32_t pk = s_sel.prefix_k, pp = s_sel.prefix_p;
-      walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t, const float* x, uint32_t ok) {
+      walk_row<BYTES, THREADS>(rv, [&](int32_t, const float* x, uint32_t ok) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           if ((ok >> q) & 1u) {
@@ -459,7 +500,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // ---- draw: Gumbel-max over the kept tokens
   float bk = -__builtin_inff();
   int32_t bi = 0x7FFFFFFF;
-  walk_row<IN_FLIGHT, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+  walk_row<BYTES / 2, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
     uint32_t kept = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
