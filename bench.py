@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip the warm, per-variant and ceiling figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 64 MiB device copies (for scaling FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the headline line, print one line timing the apply on each of the five "
+                         "workloads (cold) next to a plain fill of the same bytes")
     return ap.parse_args()
 
 
@@ -97,6 +100,76 @@ def copy_calibration():
     print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "dispatches": 5}}), flush=True)
 
 
+def all_configs():
+    """The apply on each of the five workloads, cold, next to a plain fill.
+
+    Per workload: K buffer sets with K x (logits + mask [+ out]) above
+    2 x the Infinity Cache (one set when a single set is larger; at most 64,
+    so the two launch-bound workloads of well under 1 MB stay in the
+    caches), a graph of
+    launches cycling through them, HIP events around its second replay on
+    the launch stream.  The fill ceiling is torch's fill of a buffer of the
+    workload's effective bytes under the same rotation.  Parity for every
+    workload is in the GPU tests, not here.
+    """
+    import numpy as np
+    import torch
+
+    import packed_logit_bitmask_amd as mb
+    from packed_logit_bitmask_amd import workloads
+
+    mb.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()
+    tdt = {"float32": (np.int32, torch.float32), "float16": (np.int16, torch.float16),
+           "bfloat16": (np.int16, torch.bfloat16)}
+    out = []
+    for make in (workloads.tiny, workloads.tail_bf16, workloads.mixed_bf16, workloads.verify_fp16,
+                 workloads.large_fp32):
+        wl = make()
+        ndt, dt = tdt[wl.dtype]
+        esize = wl.logits.dtype.itemsize
+        rows, cols = wl.logits.shape
+        V = wl.vocab_size if wl.vocab_size is not None else min(cols, 32 * wl.mask.shape[1])
+        R = len(wl.indices) if wl.indices is not None else rows
+        eff = effective_bytes(R, V, esize, wl.op == "out")
+        set_bytes = wl.logits.nbytes * (2 if wl.op == "out" else 1) + wl.mask.nbytes
+        nsets = min(64, max(1, math.ceil(2 * INFINITY_CACHE / set_bytes)))
+        host = torch.from_numpy(wl.logits.view(ndt))
+        sets = []
+        for _ in range(nsets):
+            x = host.to(dev).view(dt)
+            m = torch.from_numpy(wl.mask).to(dev)
+            i = torch.from_numpy(wl.indices).to(dev) if wl.indices is not None else None
+            o = torch.empty_like(x) if wl.op == "out" else None
+            sets.append((x, m, i, o))
+        steps = 1000 if eff < 1e6 else max(50, min(400, int(4e9 / eff)))
+        if wl.op == "out":
+            fn = lambda k: mb.mi_apply_bitmask_out(sets[k % nsets][0], sets[k % nsets][1], sets[k % nsets][3],
+                                                   wl.vocab_size, sets[k % nsets][2], wl.fill_value)
+        else:
+            fn = lambda k: mb.mi_apply_bitmask_inplace(sets[k % nsets][0], sets[k % nsets][1], wl.vocab_size,
+                                                       sets[k % nsets][2], wl.fill_value)
+        ms = graph_ms(torch, fn, steps, stream)
+        del sets
+        torch.cuda.empty_cache()
+        fsets = min(64, max(1, math.ceil(2 * INFINITY_CACHE / eff)))
+        bufs = [torch.empty(eff, dtype=torch.uint8, device=dev) for _ in range(fsets)]
+        fill_ms = graph_ms(torch, lambda k: bufs[k % fsets].fill_(7), steps, stream)
+        del bufs
+        torch.cuda.empty_cache()
+        gbps = eff / (ms * 1e-3) / 1e9
+        fill_gbps = eff / (fill_ms * 1e-3) / 1e9
+        out.append({"workload": wl.name, "op": wl.op, "dtype": wl.dtype, "shape": [rows, cols], "vocab_size": V,
+                    "rows_processed": R, "effective_bytes": eff, "buffer_sets": nsets, "launches": steps,
+                    "us_per_launch": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+                    "frac_of_peak": round(gbps / PEAK_GBPS, 4), "fill_ceiling_GBps": round(fill_gbps, 1),
+                    "frac_of_fill_ceiling": round(gbps / fill_gbps, 4), "variant": "auto"})
+        print(f"# {wl.name}: {ms * 1e3:.3f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+    print(json.dumps({"mode": "all_configs", "peak_GBps": PEAK_GBPS, "configs": out}), flush=True)
+
+
 def effective_bytes(rows: int, vocab: int, esize: int, out_of_place: bool = False) -> int:
     words = (vocab + 31) // 32
     return rows * words * 4 + rows * vocab * esize * (2 if out_of_place else 1)
@@ -106,6 +179,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.all_configs:
+        all_configs()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the apply has no cross-GPU step, and this build runs on a "
