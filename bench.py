@@ -270,6 +270,8 @@ def main():
         extras["fused_sampler_cold"] = sampler_times(torch, dev, mb, workloads, stream)
 
     cpu = cpu_baseline(wl, eff, args.cpu_seconds)
+    if not args.no_extras:
+        extras["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl, eff, args.cpu_seconds / 2)
 
     line = {
         "metric": METRIC,
@@ -571,6 +573,52 @@ def cpu_baseline(wl, eff, seconds):
     return {"value": round(eff * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{passes} full passes of the same workload (128 indexed rows x 128000 tokens) "
                       f"in {el:.1f} s on one host core"}
+
+
+def cpu_baseline_all_cores(wl, eff, seconds):
+    """The same oracle loop, the indexed rows split over the host's cores.
+
+    One thread per core (at most 16), each applying its share of the rows
+    again and again until `seconds` pass; the C loop releases the GIL, so
+    the threads run in parallel.  Bytes per processed row are the
+    workload's effective bytes over its rows.
+    """
+    import threading
+
+    import numpy as np
+
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    parts = [p for p in np.array_split(np.asarray(wl.indices), threads) if p.size]
+    x = wl.logits.copy()
+    done = [0] * len(parts)
+    t0 = time.perf_counter()
+    stop = t0 + seconds
+
+    def work(k):
+        rows = list(parts[k])
+        while time.perf_counter() < stop:
+            oracle.apply_inplace(x, wl.mask, wl.dtype, wl.vocab_size, rows, wl.fill_value)
+            done[k] += len(rows)
+
+    pool = [threading.Thread(target=work, args=(k,)) for k in range(len(parts))]
+    for th in pool:
+        th.start()
+    for th in pool:
+        th.join()
+    el = time.perf_counter() - t0
+    per_row = eff / len(wl.indices)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(sum(done) * per_row / el / 1e9, 3), "unit": "GB/s", "cores": len(parts),
+            "kind": "oracle", "cpu_model": model,
+            "sample": f"{sum(done)} row applications of the same workload's indexed rows, split over "
+                      f"{len(parts)} threads, in {el:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -265,3 +265,38 @@ def test_rows_without_candidates_draw_minus_one(T, k, p, m):
     say(f"[gpu] sampler empty rows T={T} k={k} p={p} m={m}")
     tok = check_rows(x.view(np.uint32), "float32", mask, None, T, k, p, m, seed=2, offset=5, min_exact=1.0)
     assert tok[3] == -1 and tok[7] == -1 and tok[11] == 500
+
+
+def test_graph_replay_matches_eager():
+    """The sampler captured in a HIP graph (several offsets, a per-row
+    temperature array) replays to the eager tokens, replay after replay,
+    with other GPU work and synchronisations in between."""
+    rng = np.random.default_rng(10)
+    R, cols = 64, 5000
+    bits = random_logits(rng, "bfloat16", R, cols)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.3, (cols + 31) // 32, rng)
+    dl = dev_logits(bits, "bfloat16")
+    dm = torch.from_numpy(mask).to("cuda")
+    temp = torch.from_numpy(rng.uniform(0.5, 1.5, R).astype(np.float32)).to("cuda")
+    modes = [dict(top_k=20), dict(top_p=0.8), dict(min_p=0.05), dict()]
+    outs = [torch.empty(R, dtype=torch.int64, device="cuda") for _ in modes]
+    want = [mb.mi_apply_bitmask_sample(dl, dm, 4990, temperature=temp, seed=5, offset=k, **kw).cpu()
+            for k, kw in enumerate(modes)]
+    say("[gpu] sampler graph capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for k, kw in enumerate(modes):
+                mb.mi_apply_bitmask_sample(dl, dm, 4990, temperature=temp, seed=5, offset=k, out=outs[k], **kw)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(len(modes)):
+            assert torch.equal(outs[k].cpu(), want[k]), (rep, modes[k])
+        (dl.float() * 2).sum().item()     # unrelated eager work between replays
+    del g
