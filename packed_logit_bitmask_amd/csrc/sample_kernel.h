@@ -26,9 +26,9 @@
 //   top-p    the same radix search summing softmax mass instead of counts:
 //            the largest key whose tokens at or above it hold at least p * Z
 //            (Z is the total of the first pass's mass histogram).  Masses
-//            are fixed-point integers (2^31 * exp(z - z_max)), so the sums do
-//            not depend on the order of the atomic adds: the cut is
-//            deterministic.  Both searches share the passes, one per 8-bit
+//            are fixed-point integers (2^31 * exp(z - z_max), the exponential
+//            by the hardware base-2 instruction), so the sums do not depend
+//            on the order of the atomic adds: the cut is deterministic.  Both searches share the passes, one per 8-bit
 //            digit: 4 for fp32, 3 for fp16, 2 for bf16 (the low digits of a
 //            16-bit type's key are the same for every token of a prefix);
 //   min-p    z - z_max >= ln(min_p), no pass of its own;
@@ -439,9 +439,14 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
             const uint32_t key = order_key(x[q]);
             const uint32_t d = (key >> shift) & 255u;
             if (use_k && (key & pmask) == pk) atomicAdd(&hist_n[wave][d], 1u);
-            if (use_p && (key & pmask) == pp)
-              atomicAdd(&hist_m[wave][d],
-                        static_cast<unsigned long long>(expf(x[q] * inv_t - zmax) * 2147483648.0f));
+            if (use_p && (key & pmask) == pp) {
+              // 2^31 exp(z - z_max) in [0, 2^31]: the hardware base-2
+              // exponential, converted through u32 (exact in that range); a
+              // mass that truncates to 0 adds nothing
+              const uint32_t m = static_cast<uint32_t>(
+                  __builtin_amdgcn_exp2f((x[q] * inv_t - zmax) * 1.4426950408889634f) * 2147483648.0f);
+              if (m) atomicAdd(&hist_m[wave][d], static_cast<unsigned long long>(m));
+            }
           }
         }
       });

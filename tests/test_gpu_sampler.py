@@ -300,3 +300,22 @@ def test_graph_replay_matches_eager():
             assert torch.equal(outs[k].cpu(), want[k]), (rep, modes[k])
         (dl.float() * 2).sum().item()     # unrelated eager work between replays
     del g
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_many_rows_variant(dtype):
+    """More than 256 rows selects the 256-thread variant; per-row parameters,
+    a ragged vocab tail and a few rows with nothing allowed."""
+    rng = np.random.default_rng(11)
+    R, cols, V = 300, 2051, 2045
+    bits = random_logits(rng, dtype, R, cols)
+    allowed = rng.random((R, cols)) < rng.uniform(0.02, 0.8, (R, 1))
+    allowed[[4, 150, 299]] = False
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    T = rng.choice([0.0, 0.6, 1.0, 1.4], R).astype(np.float32)
+    k = rng.choice([0, 1, 10, 300], R).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.5], R).astype(np.float32)
+    m = rng.choice([0.0, 0.02], R).astype(np.float32)
+    say(f"[gpu] sampler 300 rows {dtype}")
+    tok = check_rows(bits, dtype, mask, V, T, k, p, m, seed=13, offset=77)
+    assert tok[4] == -1 and tok[150] == -1 and tok[299] == -1
