@@ -263,7 +263,7 @@ def main():
             t = timed(var, args.steps, 10, rotate=True)
             per[var] = {"ms_per_step": t, "GBps": eff / (t * 1e-3) / 1e9}
         extras["variants_cold"] = per
-        extras["ceiling_cold"] = ceilings(torch, dev, eff, nsets, args.steps, stream)
+        extras["ceiling_cold"] = ceilings(torch, dev, eff, nsets, args.steps, stream, rmw_bytes=R * V * 2)
         extras["gated_rows_cold"] = gated_rows(torch, dev, mb, workloads, args.steps, stream)
         extras["host_path"] = host_path(torch, mb, wl, eff)
         extras["mask_upload_overlap"] = upload_overlap(torch, dev, mb, wl)
@@ -311,16 +311,27 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def ceilings(torch, dev, eff, nsets, steps, stream):
-    """Plain fill and copy over the same byte count, same rotation."""
+def ceilings(torch, dev, eff, nsets, steps, stream, rmw_bytes=0):
+    """Plain fill and copy over the same byte count, same rotation.
+
+    With rmw_bytes, also a plain copy of rmw_bytes (read rmw_bytes, write
+    rmw_bytes): the physical traffic of an in-place apply that must read
+    every line it writes, without any of the apply's work.
+    """
     n = eff // 2
     nsets = max(2, math.ceil(2 * INFINITY_CACHE / eff))
     bufs = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(nsets)]
     half = [torch.empty(n // 2, dtype=torch.int16, device=dev) for _ in range(2 * nsets)]
+    cases = [("fill", eff, lambda k: bufs[k % nsets].fill_(-128)),
+             ("copy", eff, lambda k: half[(2 * k) % (2 * nsets)].copy_(half[(2 * k + 1) % (2 * nsets)]))]
+    if rmw_bytes:
+        rsets = max(2, math.ceil(INFINITY_CACHE / rmw_bytes))
+        src = [torch.empty(rmw_bytes // 2, dtype=torch.int16, device=dev) for _ in range(rsets)]
+        dst = [torch.empty(rmw_bytes // 2, dtype=torch.int16, device=dev) for _ in range(rsets)]
+        cases.append(("copy_same_physical_bytes", 2 * rmw_bytes, lambda k: dst[k % rsets].copy_(src[k % rsets])))
     torch.cuda.synchronize()
     out = {}
-    for name, fn in (("fill", lambda k: bufs[k % nsets].fill_(-128)),
-                     ("copy", lambda k: half[(2 * k) % (2 * nsets)].copy_(half[(2 * k + 1) % (2 * nsets)]))):
+    for name, nbytes, fn in cases:
         with torch.cuda.stream(stream):
             for k in range(10):
                 fn(k)
@@ -339,7 +350,7 @@ def ceilings(torch, dev, eff, nsets, steps, stream):
         e.record(stream)
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / steps
-        out[name] = {"bytes_per_step": eff, "ms_per_step": ms, "GBps": eff / (ms * 1e-3) / 1e9}
+        out[name] = {"bytes_per_step": nbytes, "ms_per_step": ms, "GBps": nbytes / (ms * 1e-3) / 1e9}
         del g
     return out
 
