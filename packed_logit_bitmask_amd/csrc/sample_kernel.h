@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "apply_kernels.h"  // raw buffer resources (Rsrc, make_rsrc, load_word, load16, kSkip)
 
 namespace mi {
@@ -341,6 +343,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   __shared__ int32_t s_besti[kWaves];
   __shared__ uint32_t s_count[kWaves];
   __shared__ SelectState s_sel;
+  __shared__ unsigned long long s_bin[256];  // last radix pass: best (key, token) per digit of the bucket
   // per-wave histograms in dynamic LDS (present only when a filter may run)
   extern __shared__ unsigned long long s_dyn[];
   auto hist_m = reinterpret_cast<unsigned long long(*)[256]>(s_dyn);
@@ -412,32 +415,94 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   const float zmax = best * inv_t;  // used only when the first pass ran
   const bool use_k = top_k > 0 && (!first_pass || static_cast<uint32_t>(top_k) < count);
   const bool use_p = top_p < 1.0f;
-  uint32_t cut = 0;  // keep tokens with order_key(x) >= cut
+  const bool use_min_p = min_p > 0.f;
+  const float ln_min_p = use_min_p ? logf(min_p) : 0.f;
 
-  // ---- top-k and top-p cuts: 4 radix passes (8-bit digits, high to low),
-  // both searches in the same passes.  The first mass histogram covers every
-  // candidate, so its total is the softmax mass Z.
+  // Gumbel-max over the kept tokens: key = z - ln(-ln u) for each kept token
+  // of a group, u from the token's Philox word; sink(q, key) receives them.
+  const auto gumbel_group = [&](int32_t i0, const float* x, uint32_t kept, auto&& sink) {
+    uint32_t c0[4] = {static_cast<uint32_t>(i0 >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo, a.offset_hi};
+    uint32_t c1[4] = {static_cast<uint32_t>(i0 >> 2) + 1u, static_cast<uint32_t>(row_base + r), a.offset_lo,
+                      a.offset_hi};
+    if (kept & 0x0Fu) philox4x32_10(c0, a.seed_lo, a.seed_hi);
+    if (kept & 0xF0u) philox4x32_10(c1, a.seed_lo, a.seed_hi);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if ((kept >> q) & 1u) {
+        // -ln(-ln u) through the hardware base-2 logarithm: -ln u =
+        // -log2(u) ln 2, then -ln(that) = -log2(that) ln 2; clamped so an
+        // overflowed z (a tiny temperature) still draws a token
+        const float u = unit_uniform(q < 4 ? c0[q] : c1[q - 4]);
+        const float e = -__log2f(u) * 0.6931471805599453f;
+        sink(q, fmaxf(x[q] * inv_t - __log2f(e) * 0.6931471805599453f, -__FLT_MAX__));
+      }
+    }
+  };
+  const auto min_p_keep = [&](const float* x, uint32_t bits) {
+    if (use_min_p) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (x[q] * inv_t - zmax < ln_min_p) bits &= ~(1u << q);
+    }
+    return bits;
+  };
+
+  float bk = -__builtin_inff();  // this thread's best Gumbel key so far, and its token
+  int32_t bi = 0x7FFFFFFF;
+  const auto offer = [&](float key, int32_t i) {
+    if (key > bk || (key == bk && i < bi)) {
+      bk = key;
+      bi = i;
+    }
+  };
+
   if (use_k || use_p) {
+    // ---- top-k and top-p cuts: radix passes over 8-bit digits of the key,
+    // high to low, both searches in the same passes.  The first mass
+    // histogram covers every candidate, so its total is the softmax mass Z.
+    //
+    // For fp16 and fp32 the last pass also draws.  Before it, every token
+    // whose key is above the bucket of the higher of the two prefixes is
+    // kept whatever the last digit turns out to be, and every token below
+    // that bucket is cut; the final cut lies inside the bucket.  So that
+    // pass computes the Gumbel key of each token above or in the bucket: a
+    // token above goes to the thread's running best, a token in the bucket
+    // to a per-digit best in LDS; once the digit is known, the bins at or
+    // above it join the draw.
     if (t == 0) s_sel = SelectState{0u, static_cast<uint32_t>(top_k), 0ull, 0u};
     // Digits below kLastShift lie in the type's always-zero low bits: every
     // token of a prefix shares them (all 0 under a positive prefix, all 1
     // under a negative one, the key complementing negatives), so they are
     // filled in after the passes instead of counted.
     constexpr int kLastShift = (D::kZeroLowBits / 8) * 8;
-    uint32_t pmask = 0;
-    for (int shift = 24; shift >= kLastShift; shift -= 8) {
+    // The draw rides on the last pass only when that pass's bucket is narrow
+    // (a 16-bit prefix or finer: fp16 and fp32).  For bf16 the last pass is
+    // the second digit and its bucket a whole binade, often thousands of
+    // tokens, which would all pay for the generator; a separate draw pass
+    // over the kept tokens alone is cheaper there.
+    constexpr bool kFuseDraw = kLastShift < 16;
+    // one radix pass; `last` (a compile-time flag) also draws, with half as
+    // many bytes in flight to leave registers for the generator
+    const auto radix_pass = [&](int shift, uint32_t pmask, auto last_tag) {
+      constexpr bool last = decltype(last_tag)::value;
       for (int b = t; b < kWaves * 256; b += THREADS) {
         (&hist_n[0][0])[b] = 0u;
         (&hist_m[0][0])[b] = 0ull;
       }
+      if constexpr (last)
+        for (int b = t; b < 256; b += THREADS) s_bin[b] = 0ull;
       __syncthreads();
       const uint32_t pk = s_sel.prefix_k, pp = s_sel.prefix_p;
-      walk_row<BYTES, THREADS>(rv, [&](int32_t, const float* x, uint32_t ok) {
+      const uint32_t phi = max(use_k ? pk : 0u, use_p ? pp : 0u);
+      walk_row<last ? BYTES / 2 : BYTES, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+        uint32_t above = 0, inside = 0;
+        uint32_t digit[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
+          const uint32_t key = order_key(x[q]);
+          const uint32_t d = (key >> shift) & 255u;
+          digit[q] = d;
           if ((ok >> q) & 1u) {
-            const uint32_t key = order_key(x[q]);
-            const uint32_t d = (key >> shift) & 255u;
             if (use_k && (key & pmask) == pk) atomicAdd(&hist_n[wave][d], 1u);
             if (use_p && (key & pmask) == pp) {
               // 2^31 exp(z - z_max) in [0, 2^31]: the hardware base-2
@@ -447,8 +512,25 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
                   __builtin_amdgcn_exp2f((x[q] * inv_t - zmax) * 1.4426950408889634f) * 2147483648.0f);
               if (m) atomicAdd(&hist_m[wave][d], static_cast<unsigned long long>(m));
             }
+            if constexpr (last) {
+              if ((key & pmask) > phi) above |= 1u << q;
+              else if ((key & pmask) == phi) inside |= 1u << q;
+            }
           }
         }
+        if constexpr (!last) return;
+        const uint32_t kept = min_p_keep(x, above | inside);
+        if (!kept) return;
+        gumbel_group(i0, x, kept, [&](int q, float key) {
+          if ((above >> q) & 1u) {
+            offer(key, i0 + q);
+          } else {
+            // larger key first, then the lower token index
+            const unsigned long long packed = (static_cast<unsigned long long>(order_key(key)) << 32) |
+                                              static_cast<uint32_t>(~static_cast<uint32_t>(i0 + q));
+            atomicMax(&s_bin[digit[q]], packed);
+          }
+        });
       });
       __syncthreads();
       // fold the per-wave histograms into row 0
@@ -468,11 +550,11 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       if (use_k && wave == 0) {
         const WaveSuffix<uint32_t> ws(&hist_n[0][0]);
         int d;
-        uint32_t above;
-        ws.pick(s_sel.need_k, &d, &above);
+        uint32_t ab;
+        ws.pick(s_sel.need_k, &d, &ab);
         if (lane_id() == 0) {
           s_sel.prefix_k |= static_cast<uint32_t>(d) << shift;
-          s_sel.need_k -= above;
+          s_sel.need_k -= ab;
         }
       }
       if (use_p && wave == 1) {
@@ -484,55 +566,67 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           need = target ? target : 1ull;
         }
         int d;
-        unsigned long long above;
-        ws.pick(need, &d, &above);
+        unsigned long long ab;
+        ws.pick(need, &d, &ab);
         if (lane_id() == 0) {
           s_sel.prefix_p |= static_cast<uint32_t>(d) << shift;
-          s_sel.need_p = need - above;
+          s_sel.need_p = need - ab;
         }
       }
       __syncthreads();
+    };
+    uint32_t pmask = 0;
+    for (int shift = 24; shift > kLastShift; shift -= 8) {
+      radix_pass(shift, pmask, std::false_type{});
       pmask |= 255u << shift;
     }
+    radix_pass(kLastShift, pmask, std::integral_constant<bool, kFuseDraw>{});
     constexpr uint32_t kLow = (1u << kLastShift) - 1u;
     const auto complete = [&](uint32_t prefix) { return prefix | ((prefix & 0x80000000u) ? 0u : kLow); };
+    uint32_t cut = 0;  // keep tokens with order_key(x) >= cut
     if (use_k) cut = max(cut, complete(s_sel.prefix_k));
     if (use_p) cut = max(cut, complete(s_sel.prefix_p));
-  }
-  const bool use_min_p = min_p > 0.f;
-  const float ln_min_p = use_min_p ? logf(min_p) : 0.f;
-
-  // ---- draw: Gumbel-max over the kept tokens
-  float bk = -__builtin_inff();
-  int32_t bi = 0x7FFFFFFF;
-  walk_row<BYTES / 2, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
-    uint32_t kept = 0;
+    if constexpr (kFuseDraw) {
+      // the bucket's tokens at or above the cut's last digit are kept
+      const uint32_t dcut = (cut >> kLastShift) & 255u;
+      for (int b = t; b < 256; b += THREADS) {
+        const unsigned long long packed = s_bin[b];
+        if (static_cast<uint32_t>(b) >= dcut && packed) {
+          const uint32_t k = static_cast<uint32_t>(packed >> 32);
+          offer(__uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k),
+                static_cast<int32_t>(~static_cast<uint32_t>(packed)));
+        }
+      }
+    } else {
+      // ---- draw: Gumbel-max over the tokens at or above the cut
+      walk_row<BYTES / 2, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+        uint32_t at_or_above = 0;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (((ok >> q) & 1u) && order_key(x[q]) >= cut && (!use_min_p || x[q] * inv_t - zmax >= ln_min_p))
-        kept |= 1u << q;
-    if (!kept) return;
-    uint32_t c0[4] = {static_cast<uint32_t>(i0 >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo, a.offset_hi};
-    uint32_t c1[4] = {static_cast<uint32_t>(i0 >> 2) + 1u, static_cast<uint32_t>(row_base + r), a.offset_lo,
-                      a.offset_hi};
-    if (kept & 0x0Fu) philox4x32_10(c0, a.seed_lo, a.seed_hi);
-    if (kept & 0xF0u) philox4x32_10(c1, a.seed_lo, a.seed_hi);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if ((kept >> q) & 1u) {
-        // Gumbel variate -ln(-ln u) through the hardware base-2 logarithm:
-        // -ln u = -log2(u) * ln 2, then -ln(that) = -log2(that) * ln 2
-        const float u = unit_uniform(q < 4 ? c0[q] : c1[q - 4]);
-        const float e = -__log2f(u) * 0.6931471805599453f;
-        // clamped so an overflowed z (a tiny temperature) still draws a token
-        const float key = fmaxf(x[q] * inv_t - __log2f(e) * 0.6931471805599453f, -__FLT_MAX__);
-        if (key > bk) {
+        for (int q = 0; q < 8; ++q)
+          if (((ok >> q) & 1u) && order_key(x[q]) >= cut) at_or_above |= 1u << q;
+        const uint32_t kept = min_p_keep(x, at_or_above);
+        if (!kept) return;
+        gumbel_group(i0, x, kept, [&](int q, float key) {
+          if (key > bk) {  // strictly greater: each thread sees its tokens in order
+            bk = key;
+            bi = i0 + q;
+          }
+        });
+      });
+    }
+  } else {
+    // ---- draw: Gumbel-max over every candidate (min-p aside)
+    walk_row<BYTES / 2, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+      const uint32_t kept = min_p_keep(x, ok);
+      if (!kept) return;
+      gumbel_group(i0, x, kept, [&](int q, float key) {
+        if (key > bk) {  // strictly greater: each thread sees its tokens in order
           bk = key;
           bi = i0 + q;
         }
-      }
-    }
-  });
+      });
+    });
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ob = __shfl_xor(bk, o);
