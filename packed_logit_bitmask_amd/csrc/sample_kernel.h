@@ -11,10 +11,10 @@
 // finite -- so a masked token is never drawn.  The logits are only read.
 //
 // One block per row (1024 threads when each compute unit holds one row, 256
-// when many rows share one).  Each pass walks the row
-// in groups of 8 consecutive tokens per thread (16-byte vector loads when
-// the row start is aligned; four groups in flight per thread); trip counts
-// are uniform across the block.
+// when many rows share one).  Each pass walks the row in groups of 8
+// consecutive tokens per thread through raw buffer loads (16-byte vectors
+// when the row start is aligned), several groups in flight per thread; trip
+// counts are uniform across the block.
 //
 //   pass 1   max logit and its (lowest) index, count of candidate tokens
 //            -> greedy rows and rows with no candidate end here; skipped
@@ -26,17 +26,21 @@
 //   top-p    the same radix search summing softmax mass instead of counts:
 //            the largest key whose tokens at or above it hold at least p * Z
 //            (Z is the total of the first pass's mass histogram).  Masses
-//            are fixed-point integers (2^31 * exp(z - z_max), the exponential
-//            by the hardware base-2 instruction), so the sums do not depend
-//            on the order of the atomic adds: the cut is deterministic.  Both searches share the passes, one per 8-bit
+//            are fixed-point integers (2^31 * exp(z - z_max), the
+//            exponential by the hardware base-2 instruction), so the sums do
+//            not depend on the order of the atomic adds: the cut is
+//            deterministic.  Both searches share the passes, one per 8-bit
 //            digit: 4 for fp32, 3 for fp16, 2 for bf16 (the low digits of a
 //            16-bit type's key are the same for every token of a prefix);
+//            each digit is picked by a wave-parallel suffix scan;
 //   min-p    z - z_max >= ln(min_p), no pass of its own;
 //   draw     Gumbel-max over the kept tokens: key = z - ln(-ln u) (logarithms
 //            by the hardware log2 instruction, rescaled), u from
 //            Philox4x32-10 (counter (i / 4, row, offset lo, offset hi), key
 //            (seed lo, seed hi), word i % 4; u = (floor(x / 2^9) + 1/2) / 2^23),
-//            ties to the lowest index.
+//            ties to the lowest index.  A pass of its own, except for fp16
+//            and fp32 rows with top-k or top-p, where the last radix pass
+//            draws as it counts.
 //
 // Histograms are private to each wave (LDS), folded after every pass.
 #pragma once
