@@ -45,23 +45,33 @@ constexpr int64_t kMaxBytes = int64_t(1) << 56;
 constexpr int64_t kMaxBlocksPerLaunch = (int64_t(1) << 24) - 1;  // blocks * 256 < 2^32
 
 // Shape of the 16-byte-vector kernels: vectors per lane (unroll) and the
-// store cache policy.  Picked from measurements on MI355X, cold from HBM:
-// below ~48 MB of writes a device-scope write-through store with two
-// vectors per lane is fastest (the output then streams out during the
-// kernel instead of in one end-of-kernel L2 writeback); above it adding the
-// non-temporal hint wins, with one vector per lane for 16-bit data and four
-// for 32-bit data.  Out of place, two vectors per lane with write-through
-// non-temporal stores was best at every size measured.
+// store cache policy.  Picked from measurements on MI355X, cold from HBM,
+// in place:
+//  - below 48 MB of writes, two vectors per lane with device-scope
+//    write-through stores (the output streams out during the kernel instead
+//    of in one end-of-kernel L2 writeback);
+//  - from 48 MB to 1 GB, two vectors per lane with write-through
+//    non-temporal stores: 3-5 % ahead of one vector per lane up to 128 MB
+//    and 14-25 % ahead on rows of mixed kinds (all-ones, sparse, empty), at
+//    most 4 % behind one vector per lane on 256-512 MB of uniform density;
+//  - from 1 GB, four vectors per lane, non-temporal: 1-4 % ahead on the
+//    large mixed-kind workloads.  One vector per lane is never used: it
+//    launches 4x the blocks, which cost 36-40 % on rows that need little
+//    work.
+// Out of place, two vectors per lane with write-through non-temporal stores
+// was best at every size measured.
 struct VecShape {
   int unroll;
   int policy;
 };
 
 constexpr int64_t kSmallWriteBytes = int64_t(48) << 20;
+constexpr int64_t kLargeWriteBytes = int64_t(1) << 30;
 
-VecShape inplace_shape(int esize, int64_t write_bytes) {
+VecShape inplace_shape(int64_t write_bytes) {
   if (write_bytes < kSmallWriteBytes) return {2, mi::kStoreDevice};
-  return esize == 2 ? VecShape{1, mi::kStoreDeviceStream} : VecShape{4, mi::kStoreDeviceStream};
+  if (write_bytes < kLargeWriteBytes) return {2, mi::kStoreDeviceStream};
+  return {4, mi::kStoreDeviceStream};
 }
 
 constexpr VecShape kOutShape{2, mi::kStoreDeviceStream};
@@ -255,15 +265,16 @@ mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64
     }
     case MI_VARIANT_VEC: {
       constexpr int VW = mi::Bits16B<T>::VW;
-      const VecShape shape = inplace_shape(sizeof(T), p.R * p.V * static_cast<int64_t>(sizeof(T)));
+      const VecShape shape = inplace_shape(p.R * p.V * static_cast<int64_t>(sizeof(T)));
       const int64_t per = int64_t(mi::kBlock) * shape.unroll;
       const int64_t chunks = std::max<int64_t>(1, (p.V / VW + per - 1) / per);
       launch_slots(p.R, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t nrep) {
 #define MI_INPLACE_VEC(UNROLL, POLICY)                                                            \
   mi::inplace_vec<T, UNROLL, POLICY><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, W, map, s0, \
                                                                         ch, fill, any_out, nrep)
-        if (shape.unroll == 2) MI_INPLACE_VEC(2, mi::kStoreDevice);
-        else if (shape.unroll == 1) MI_INPLACE_VEC(1, mi::kStoreDeviceStream);
+        // exactly the shapes inplace_shape returns
+        if (shape.unroll == 2 && shape.policy == mi::kStoreDevice) MI_INPLACE_VEC(2, mi::kStoreDevice);
+        else if (shape.unroll == 2) MI_INPLACE_VEC(2, mi::kStoreDeviceStream);
         else MI_INPLACE_VEC(4, mi::kStoreDeviceStream);
 #undef MI_INPLACE_VEC
       }, any_out != nullptr);
