@@ -462,3 +462,33 @@ def test_staged_decode_loop(depth):
         src = before.view(torch.int16).cpu().numpy().view(np.uint16)
         want = oracle.apply_inplace(src.copy(), mask_np, "float16", V)
         assert np.array_equal(after.view(torch.int16).cpu().numpy().view(np.uint16), want), step
+
+
+def test_grids_split_over_several_launches():
+    """More row slots than one launch holds (2^24 - 1 blocks of one chunk):
+    the host splits the grid, and every row is still applied exactly once.
+    Also the gated apply with its report, whose extra block per row halves
+    the slots a launch takes."""
+    rng = np.random.default_rng(12)
+    R, cols = (1 << 24) + 3, 8                   # 268 MB of bf16; one 16-byte vector per row
+    bits = rng.integers(0, 1 << 16, size=(R, cols), dtype=np.uint16)
+    mask = rng.integers(-(1 << 31), 1 << 31, size=(R, 1), dtype=np.int64).astype(np.int32)
+    say(f"[gpu] {R} rows of 8 bf16 tokens, in place")
+    x = to_device(bits, "bfloat16")
+    m = torch.from_numpy(mask).to("cuda")
+    mb.mi_apply_bitmask_inplace(x, m)
+    want = oracle.apply_inplace(bits.copy(), mask, "bfloat16")
+    got = to_host(x, "bfloat16")
+    assert np.array_equal(got, want)
+    del x, got, want
+
+    R2 = (1 << 23) + 3
+    b2 = bits[:R2].copy()
+    gate = (rng.random(R2) < 0.7).astype(np.int8)
+    gate[-1] = 1
+    say(f"[gpu] {R2} rows, gated with the report")
+    x = to_device(b2, "bfloat16")
+    rep = mb.mi_apply_bitmask_rows(x, m[:R2], torch.from_numpy(gate).to("cuda"), report=True)
+    want, want_any = oracle.apply_rows(b2.copy(), mask[:R2], "bfloat16", None, gate)
+    assert np.array_equal(to_host(x, "bfloat16"), want)
+    assert np.array_equal(rep.cpu().numpy(), want_any)

@@ -319,3 +319,17 @@ def test_many_rows_variant(dtype):
     say(f"[gpu] sampler 300 rows {dtype}")
     tok = check_rows(bits, dtype, mask, V, T, k, p, m, seed=13, offset=77)
     assert tok[4] == -1 and tok[150] == -1 and tok[299] == -1
+
+
+def test_rows_split_over_launches():
+    """More than 2^20 rows go out in several launches: the generator's row
+    counter and the per-row parameter arrays continue across the split."""
+    rng = np.random.default_rng(13)
+    R, cols = (1 << 20) + 5, 8
+    bits = random_logits(rng, "float32", R, cols)
+    mask = rng.integers(1, 256, size=(R, 1)).astype(np.int32)
+    T = rng.uniform(0.5, 1.5, R).astype(np.float32)
+    k = rng.choice([0, 3], R).astype(np.int32)
+    rows = [0, 1, (1 << 20) - 2, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, R - 1]
+    say(f"[gpu] sampler over {R} rows")
+    check_rows(bits, "float32", mask, None, T, k, 1.0, 0.0, seed=17, offset=3, rows=rows, min_exact=1.0)
