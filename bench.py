@@ -54,7 +54,9 @@ def parse():
     return ap.parse_args()
 
 
+# the sources that define the apply kernels, their shapes and launches
 KERNEL_SOURCES = [ROOT / "packed_logit_bitmask_amd" / "csrc" / "apply_kernels.h",
+                  ROOT / "packed_logit_bitmask_amd" / "csrc" / "host_checks.h",
                   ROOT / "packed_logit_bitmask_amd" / "csrc" / "mi_bitmask.hip"]
 PMC_SUMMARY = ROOT / "profiles" / "inplace_vec_mixed_bf16_pmc.md"
 

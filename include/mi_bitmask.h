@@ -259,6 +259,15 @@ const char *mi_status_string(mi_status_t status);
 /* Detail of this thread's last non-OK return ("" if none yet). */
 const char *mi_last_error_message(void);
 
+/*
+ * Which loop the host-memory entry points run, fixed for the process:
+ * "avx512" (one masked vector store per mask word, on x86 with AVX-512 F and
+ * BW) or "portable" (one store per masked token).  The environment variable
+ * MI_BITMASK_HOST_ISA=portable, read at the first host call, selects the
+ * portable loop.  Static text; never NULL.
+ */
+const char *mi_host_isa(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     MI_DTYPE,
     VARIANT,
     fill_value_bits,
+    host_isa,
     load_library,
     mi_apply_bitmask_inplace,
     mi_apply_bitmask_inplace_host,
@@ -36,7 +37,7 @@ from .xgrammar_api import (  # noqa: F401
 )
 
 __all__ = [
-    "BitmaskError", "EXPORTS", "MI_DTYPE", "VARIANT", "fill_value_bits", "load_library",
+    "BitmaskError", "EXPORTS", "MI_DTYPE", "VARIANT", "fill_value_bits", "host_isa", "load_library",
     "mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_host",
     "mi_apply_bitmask_out_host", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample", "resolve_vocab_size",
     "allocate_token_bitmask", "apply_token_bitmask_inplace", "bitmask_dtype", "get_bitmask_shape",

@@ -25,7 +25,8 @@ VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3, "vec_resident": 4}
 EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",
            "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample",
            "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
-           "mi_resolve_vocab_size", "mi_fill_value_bits", "mi_status_string", "mi_last_error_message"]
+           "mi_resolve_vocab_size", "mi_fill_value_bits", "mi_status_string", "mi_last_error_message",
+           "mi_host_isa"]
 
 _i64, _p, _dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
 _INPLACE = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _dbl]
@@ -81,6 +82,8 @@ def load_library(path: Union[str, pathlib.Path, None] = None) -> ctypes.CDLL:
     lib.mi_status_string.restype = ctypes.c_char_p
     lib.mi_last_error_message.argtypes = []
     lib.mi_last_error_message.restype = ctypes.c_char_p
+    lib.mi_host_isa.argtypes = []
+    lib.mi_host_isa.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
@@ -101,6 +104,11 @@ def resolve_vocab_size(cols: int, mask_cols: int, vocab_size: Optional[int] = No
     check(load_library().mi_resolve_vocab_size(cols, mask_cols, -1 if vocab_size is None else vocab_size,
                                                ctypes.byref(out)))
     return out.value
+
+
+def host_isa() -> str:
+    """The loop the host-memory entry points run: "avx512" or "portable"."""
+    return load_library().mi_host_isa().decode()
 
 
 def fill_value_bits(fill_value: float, dtype: str) -> int:

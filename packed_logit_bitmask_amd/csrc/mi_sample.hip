@@ -1,0 +1,116 @@
+// Host side of the fused apply + sampler: argument checks and the launch of
+// mi::sample_rows (sample_kernel.h).  Declared in include/mi_bitmask.h.
+
+#include "mi_bitmask.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "host_checks.h"
+#include "sample_kernel.h"
+
+using namespace mi_abi;
+
+namespace {
+
+constexpr int64_t kMaxSampleVocab = int64_t(1) << 28;
+
+// Checks for a call without a mask: every token below V takes part, and V
+// defaults to cols.
+mi_status_t check_logits_only(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t ls,
+                              int64_t vocab_size, Plan* p) {
+  if (!logits && rows > 0 && cols > 0) return fail(MI_ERR_NULL_POINTER, "logits is NULL");
+  if (!valid_dtype(static_cast<int>(dtype))) return fail(MI_ERR_BAD_DTYPE, "unknown dtype %d", (int)dtype);
+  if (rows < 0 || cols < 0) return fail(MI_ERR_BAD_SHAPE, "negative size (rows %lld, cols %lld)", (long long)rows,
+                                        (long long)cols);
+  if (rows > kMaxRows || cols > kMaxCols) return fail(MI_ERR_BAD_SHAPE, "size above the limits");
+  if (ls < cols || ls > kMaxPitch)
+    return fail(MI_ERR_BAD_SHAPE, "logits_row_stride %lld must be in [cols %lld, 2^40]", (long long)ls, (long long)cols);
+  if (vocab_size < -1 || vocab_size > cols)
+    return fail(MI_ERR_BAD_VOCAB, "vocab_size %lld outside [0, cols %lld] (or -1)", (long long)vocab_size,
+                (long long)cols);
+  p->V = vocab_size == -1 ? cols : vocab_size;
+  p->W = (p->V + 31) / 32;
+  p->R = rows;
+  p->row_limit = rows;
+  p->esize = elem_bytes(dtype);
+  if (reinterpret_cast<uintptr_t>(logits) % p->esize)
+    return fail(MI_ERR_MISALIGNED, "logits not aligned to its %d-byte elements", p->esize);
+  if (!extent(logits, rows, cols, ls, p->esize, &p->logits)) return fail(MI_ERR_BAD_SHAPE, "buffer extent overflows");
+  return MI_OK;
+}
+
+}  // namespace
+
+MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                                           int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
+                                           int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
+                                           const mi_sample_params_t* params, int64_t* tokens, hipStream_t stream) {
+  if (!params) return fail(MI_ERR_NULL_POINTER, "params is NULL");
+  if (!tokens && rows > 0) return fail(MI_ERR_NULL_POINTER, "tokens is NULL");
+  Plan p;
+  mi_status_t st;
+  if (mask) {
+    st = check_common(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
+                      vocab_size, nullptr, 0, 0.0, &p);
+  } else {
+    st = check_logits_only(logits, dtype, rows, cols, logits_row_stride, vocab_size, &p);
+  }
+  if (st != MI_OK) return st;
+  // the kernel addresses a row through 32-bit byte offsets
+  if (p.V > kMaxSampleVocab) return fail(MI_ERR_BAD_SHAPE, "vocab size above 2^28 (the sampler's limit)");
+  ByteRange tb;
+  if (!extent(tokens, tokens ? 1 : 0, rows, rows, 8, &tb)) return fail(MI_ERR_BAD_SHAPE, "tokens extent overflows");
+  if (reinterpret_cast<uintptr_t>(tokens) % 8) return fail(MI_ERR_MISALIGNED, "tokens not 8-byte aligned");
+  if (overlaps(tb, p.logits) || overlaps(tb, p.mask)) return fail(MI_ERR_ALIAS, "tokens overlap an input");
+  for (const void* q : {static_cast<const void*>(params->temperature), static_cast<const void*>(params->top_k),
+                        static_cast<const void*>(params->top_p), static_cast<const void*>(params->min_p)})
+    if (reinterpret_cast<uintptr_t>(q) % 4) return fail(MI_ERR_MISALIGNED, "a per-row parameter array is not 4-byte aligned");
+  if (rows == 0) return MI_OK;
+
+  mi::SampleArgs a{params->temperature, params->top_k, params->top_p, params->min_p,
+                   params->temperature_all, params->top_k_all, params->top_p_all, params->min_p_all,
+                   static_cast<uint32_t>(params->seed), static_cast<uint32_t>(params->seed >> 32),
+                   static_cast<uint32_t>(params->offset), static_cast<uint32_t>(params->offset >> 32)};
+  const uint32_t* m = reinterpret_cast<const uint32_t*>(mask);
+  const int32_t V = static_cast<int32_t>(p.V);
+  (void)hipGetLastError();
+  constexpr int64_t kRowsPerLaunch = int64_t(1) << 20;   // blocks * threads < 2^32
+  for (int64_t r0 = 0; r0 < rows; r0 += kRowsPerLaunch) {
+    const uint32_t n = static_cast<uint32_t>(std::min(kRowsPerLaunch, rows - r0));
+    const int64_t mr0 = m ? r0 * mask_row_stride : 0;
+    // per-row parameter arrays and the row counter of the generator start at r0
+    mi::SampleArgs ar = a;
+    if (ar.temperature) ar.temperature += r0;
+    if (ar.top_k) ar.top_k += r0;
+    if (ar.top_p) ar.top_p += r0;
+    if (ar.min_p) ar.min_p += r0;
+    const auto* lg = static_cast<const char*>(logits) + r0 * logits_row_stride * p.esize;
+    const uint32_t* mk = m ? m + mr0 : nullptr;
+    // Histogram LDS only when some row may filter; deep load pipeline when a
+    // compute unit holds one row at a time (rows <= 256), shallow otherwise.
+    const bool may_filter = ar.top_k || ar.top_p || ar.top_k_all > 0 || ar.top_p_all < 1.0f;
+    const bool deep = n <= 256;
+    const int threads = deep ? 1024 : 256;
+    const size_t lds = may_filter ? mi::sample_hist_bytes(threads) : 0;
+#define MI_SAMPLE(TAG, BITS, BYTES, THREADS)                                                                   \
+  mi::sample_rows<TAG, BYTES, THREADS><<<n, THREADS, lds, stream>>>(reinterpret_cast<const BITS*>(lg),          \
+                                                                    logits_row_stride, mk, mask_row_stride, V,   \
+                                                                    ar, r0, tokens + r0)
+    switch (dtype) {
+      case MI_DTYPE_F32:
+        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 64, 256);
+        break;
+      case MI_DTYPE_F16:
+        if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::F16Bits, uint16_t, 64, 256);
+        break;
+      default:
+        if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 64, 256);
+    }
+#undef MI_SAMPLE
+  }
+  return after_launch("sample_rows");
+}
+

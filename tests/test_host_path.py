@@ -124,3 +124,22 @@ def test_xgrammar_apply_on_cpu_tensors(dtype):
     x2 = as_tensor(np.array(wl.logits), dtype)
     mb.apply_token_bitmask_inplace(x2, mb.allocate_token_bitmask(5, 333))
     assert np.array_equal(bits_of(x2, dtype), np.array(wl.logits))
+
+
+def test_host_loop_choice_and_the_portable_loop():
+    """The host entry points run the AVX-512 loop where the CPU has it; the
+    portable loop (forced through the environment, in a fresh process since
+    the choice is made once) passes the same tests."""
+    import os
+    import subprocess
+    import sys
+
+    isa = mb.host_isa()
+    assert isa in ("avx512", "portable")
+    if os.environ.get("MI_BITMASK_HOST_ISA") == "portable":
+        assert isa == "portable"
+        return
+    env = dict(os.environ, MI_BITMASK_HOST_ISA="portable")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", __file__],
+                         env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-2000:]
