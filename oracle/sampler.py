@@ -25,7 +25,7 @@ What it follows (logits-processor page, "Ops: sample" and "How it works"):
   no part, so a masked token is never drawn (logits-processor page,
   Correctness: a bitmask followed by sample never draws a disallowed token).
 
-Readings where the page is silent (each also stated in the design doc):
+Readings where the page is silent:
 
 * generator: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random
   Numbers: As Easy as 1, 2, 3", SC 2011), written here from its definition:
