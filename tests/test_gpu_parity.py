@@ -492,3 +492,21 @@ def test_grids_split_over_several_launches():
     want, want_any = oracle.apply_rows(b2.copy(), mask[:R2], "bfloat16", None, gate)
     assert np.array_equal(to_host(x, "bfloat16"), want)
     assert np.array_equal(rep.cpu().numpy(), want_any)
+
+
+def test_longest_row():
+    """One row at the column limit: 2^30 - 5 bf16 tokens (2 GB), a mask of
+    2^25 words with garbage past V, applied in place (the buffer resources
+    and chunk offsets of a single row at its largest)."""
+    rng = np.random.default_rng(14)
+    cols = (1 << 30) - 5
+    bits = rng.integers(0, 1 << 16, size=(1, cols), dtype=np.uint16)
+    mask = rng.integers(-(1 << 31), 1 << 31, size=(1, 1 << 25), dtype=np.int64).astype(np.int32)
+    say(f"[gpu] one row of {cols} bf16 tokens")
+    x = to_device(bits, "bfloat16")
+    m = torch.from_numpy(mask).to("cuda")
+    mb.mi_apply_bitmask_inplace(x, m)
+    got = to_host(x, "bfloat16")
+    del x
+    oracle.apply_inplace(bits, mask, "bfloat16")
+    assert np.array_equal(got, bits)

@@ -333,3 +333,15 @@ def test_rows_split_over_launches():
     rows = [0, 1, (1 << 20) - 2, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, R - 1]
     say(f"[gpu] sampler over {R} rows")
     check_rows(bits, "float32", mask, None, T, k, 1.0, 0.0, seed=17, offset=3, rows=rows, min_exact=1.0)
+
+
+def test_long_rows():
+    """Rows of 2^24 + 3 fp32 tokens (64 MB each): greedy on both and an
+    unfiltered draw on one, against the oracle."""
+    rng = np.random.default_rng(15)
+    R, cols = 2, (1 << 24) + 3
+    bits = random_logits(rng, "float32", R, cols)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.5, (cols + 31) // 32, rng)
+    say(f"[gpu] sampler on {R} rows of {cols} fp32 tokens")
+    check_rows(bits, "float32", mask, None, 0.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
+    check_rows(bits, "float32", mask, None, 1.0, 0, 1.0, 0.0, seed=1, offset=1, rows=[1], min_exact=1.0)
