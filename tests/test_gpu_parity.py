@@ -193,9 +193,10 @@ def test_named_large_fp32(large, variant):
 
 
 @pytest.mark.parametrize("dtype,rows,cols,vocab", [
-    ("bfloat16", 800, 40001, 39999),   # > 48 MB of 16-bit writes: one vector per lane, streaming stores
+    ("bfloat16", 800, 40001, 39999),   # 48 MB - 1 GB of writes: two vectors per lane, streaming stores
     ("float16", 700, 50003, None),
-    ("float32", 500, 30001, 29990),    # > 48 MB of 32-bit writes: four vectors per lane
+    ("float32", 500, 30001, 29990),
+    ("float32", 4500, 60001, None),    # >= 1 GB of writes: four vectors per lane
 ])
 def test_large_shapes_misaligned(dtype, rows, cols, vocab):
     rng = np.random.default_rng(rows)
