@@ -16,10 +16,9 @@
 // when the row start is aligned), several groups in flight per thread; trip
 // counts are uniform across the block.
 //
-//   pass 1   max logit and its (lowest) index, count of candidate tokens
-//            -> greedy rows and rows with no candidate end here; skipped
-//            when the row uses neither top-p nor min-p (nothing else needs
-//            it);
+//   pass 1   max logit over the candidates and its (lowest) index -> greedy
+//            rows and rows with no candidate end here; skipped when the row
+//            uses neither top-p nor min-p (nothing else needs it);
 //   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
@@ -210,6 +209,23 @@ struct RowView {
     return full ? ok : 0u;
   }
 
+  // Group g's values with every position that is not a candidate by the
+  // mask (bit clear, or past the full groups) set to -inf.  Non-finite
+  // logits pass through: a caller taking maxima sees them in the result.
+  __device__ __forceinline__ void gated(const Raw& r, int32_t g, bool full, float xv[8]) const {
+    const uint32_t bits = full ? (has_mask ? (r.w >> ((g & 3) * 8)) & 0xFFu : 0xFFu) : 0u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t u;
+      if constexpr (sizeof(Bits) == 2)
+        u = __float_as_uint(D::value(static_cast<Bits>(q & 1 ? r.v[q >> 1] >> 16 : r.v[q >> 1] & 0xFFFFu)));
+      else
+        u = r.v[q];
+      const uint32_t m = 0u - ((bits >> q) & 1u);  // all ones for a candidate
+      xv[q] = __uint_as_float((u & m) | (0xFF800000u & ~m));
+    }
+  }
+
   // The last, partial group (tokens 8 * (V / 8) .. V - 1), by plain loads.
   __device__ __forceinline__ uint32_t load_tail(float x[8]) const {
     const int32_t i0 = V & ~7;
@@ -228,9 +244,12 @@ struct RowView {
 };
 
 template <int BYTES, int THREADS, bool VEC, typename D, typename F>
-__device__ __forceinline__ void walk_groups(const RowView<D>& rv, F& f) {
+__device__ __forceinline__ void walk_groups_raw(const RowView<D>& rv, F& f) {
   // groups in flight per thread: BYTES of logits (the misaligned path, with
-  // one load per token, keeps at most 4)
+  // one load per token, keeps at most 4).  All of a batch's loads are
+  // issued before its first group is used.  (Double-buffering half batches,
+  // so the next batch's loads overlap this batch's arithmetic, measured a
+  // few percent slower in every mode.)
   constexpr int kFull = BYTES / (8 * static_cast<int>(sizeof(typename D::Bits)));
   constexpr int kInFlight = VEC ? kFull : (kFull < 4 ? kFull : 4);
   const int32_t nfull = rv.V >> 3;
@@ -245,11 +264,20 @@ __device__ __forceinline__ void walk_groups(const RowView<D>& rv, F& f) {
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
       const int32_t g = base + j * THREADS + t;
-      float x[8];
-      const uint32_t ok = rv.decode(raw[j], g, g < nfull, x);
-      f(8 * g, x, ok);
+      f(g, raw[j], g < nfull);
     }
   }
+}
+
+// Walk the full 8-token groups of the row as loaded: f(g, raw, full) for
+// group g (full: the whole group lies below V; groups past the row come
+// with full == false).  The partial last group, if any, is the caller's.
+template <int BYTES, int THREADS, typename D, typename F>
+__device__ __forceinline__ void walk_row_raw(const RowView<D>& rv, F&& f) {
+  if (rv.aligned)
+    walk_groups_raw<BYTES, THREADS, true>(rv, f);
+  else
+    walk_groups_raw<BYTES, THREADS, false>(rv, f);
 }
 
 // Walk the row: f(i0, x[8], ok) for every 8-token group, BYTES of logits
@@ -259,10 +287,11 @@ __device__ __forceinline__ void walk_groups(const RowView<D>& rv, F& f) {
 // with ok == 0), so f may hold block-uniform control flow.
 template <int BYTES, int THREADS, typename D, typename F>
 __device__ __forceinline__ void walk_row(const RowView<D>& rv, F&& f) {
-  if (rv.aligned)
-    walk_groups<BYTES, THREADS, true>(rv, f);
-  else
-    walk_groups<BYTES, THREADS, false>(rv, f);
+  walk_row_raw<BYTES, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+    float x[8];
+    const uint32_t ok = rv.decode(raw, g, full, x);
+    f(8 * g, x, ok);
+  });
   if (rv.V & 7) {
     float x[8] = {};
     const uint32_t ok = threadIdx.x == 0 ? rv.load_tail(x) : 0u;
@@ -345,7 +374,6 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   constexpr int kWaves = THREADS / 64;
   __shared__ float s_best[kWaves];
   __shared__ int32_t s_besti[kWaves];
-  __shared__ uint32_t s_count[kWaves];
   __shared__ SelectState s_sel;
   __shared__ unsigned long long s_bin[256];  // last radix pass: best (key, token) per digit of the bucket
   // per-wave histograms in dynamic LDS (present only when a filter may run)
@@ -364,25 +392,73 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   const float top_p = a.top_p ? a.top_p[r] : a.top_p_all;
   const float min_p = a.min_p ? a.min_p[r] : a.min_p_all;
 
-  // ---- pass 1: max, argmax (lowest index), candidate count.  Greedy rows
-  // need the argmax, top-p and min-p need the max logit (their masses and
-  // cutoffs are relative to it); without those the pass is skipped: the
-  // Gumbel keys need no max, and top-k needs no count (a k at or above the
-  // number of candidates comes out of the radix search as "keep all").
+  // ---- pass 1: max and argmax (lowest index) over the candidates.  Greedy
+  // rows need the argmax, top-p and min-p need the max logit (their masses
+  // and cutoffs are relative to it); without those the pass is skipped: the
+  // Gumbel keys need no max, and top-k needs no count of candidates (a k at
+  // or above it comes out of the radix search as "keep all").
+  //
+  // Fast form: each group's tokens are gated by their mask bits (others
+  // -inf) and reduced by a max tree; a thread keeps its best value and the
+  // words of the group holding it, and decodes that one group at the end
+  // for the lowest index with that value.  A group maximum that is NaN or +inf (possible
+  // only for rows holding such logits, which are not candidates) sends the
+  // whole block through the exact per-token form instead.
   const bool first_pass = !(temp > 0.f) || top_p < 1.0f || min_p > 0.f;
   float best = -__builtin_inff();
-  uint32_t count = 0;
   if (first_pass) {
     int32_t besti = 0x7FFFFFFF;
-    walk_row<BYTES, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
-      count += __builtin_popcount(ok);
+    int32_t bestg = -1;
+    typename RowView<D>::Raw braw{};  // the best group's words, kept so it need not be read again
+    bool odd = false;
+    walk_row_raw<BYTES, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+      float xv[8];
+      rv.gated(raw, g, full, xv);
+      const float gm = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
+                             fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
+      odd |= !(gm < __builtin_inff()) && gm != -__builtin_inff();  // NaN or +inf
+      if (gm > best) {  // strictly greater: each thread sees its groups in order
+        best = gm;
+        bestg = g;
+        braw = raw;
+      }
+    });
+    const int32_t tail_g = rv.V >> 3;  // the partial last group, if V % 8 != 0 (thread 0's)
+    float tx[8] = {};
+    const uint32_t tok = (rv.V & 7) && t == 0 ? rv.load_tail(tx) : 0u;
+    if (tok) {
+      float gm = -__builtin_inff();
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (((ok >> q) & 1u) && x[q] > best) {  // strictly greater: each thread sees its tokens in order
-          best = x[q];
-          besti = i0 + q;
-        }
-    });
+        if ((tok >> q) & 1u) gm = fmaxf(gm, tx[q]);
+      if (gm > best) {
+        best = gm;
+        bestg = tail_g;
+      }
+    }
+    if (__syncthreads_or(odd)) {
+      best = -__builtin_inff();
+      walk_row<BYTES, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (((ok >> q) & 1u) && x[q] > best) {
+            best = x[q];
+            besti = i0 + q;
+          }
+      });
+    } else if (bestg >= 0) {
+      float x[8];
+      uint32_t ok;
+      if (bestg == tail_g && (rv.V & 7)) {
+        ok = tok;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = tx[q];
+      } else {
+        ok = rv.decode(braw, bestg, true, x);
+      }
+      for (int q = 7; q >= 0; --q)  // the lowest index holding the best value
+        if (((ok >> q) & 1u) && x[q] == best) besti = 8 * bestg + q;
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const float ob = __shfl_xor(best, o);
@@ -391,33 +467,31 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         best = ob;
         besti = oi;
       }
-      count += __shfl_xor(count, o);
     }
     if (lane_id() == 0) {
       s_best[wave] = best;
       s_besti[wave] = besti;
-      s_count[wave] = count;
     }
     __syncthreads();
     best = s_best[0];
     besti = s_besti[0];
-    count = s_count[0];
     for (int w = 1; w < kWaves; ++w) {
       if (s_best[w] > best || (s_best[w] == best && s_besti[w] < besti)) {
         best = s_best[w];
         besti = s_besti[w];
       }
-      count += s_count[w];
     }
-    if (count == 0 || !(temp > 0.f)) {  // no candidate, or greedy
-      if (t == 0) out[r] = count == 0 ? -1 : besti;
+    // candidates are finite, so the max is -inf only when there is none
+    const bool none = best == -__builtin_inff();
+    if (none || !(temp > 0.f)) {  // no candidate, or greedy
+      if (t == 0) out[r] = none ? -1 : besti;
       return;
     }
   }
 
   const float inv_t = 1.0f / temp;
   const float zmax = best * inv_t;  // used only when the first pass ran
-  const bool use_k = top_k > 0 && (!first_pass || static_cast<uint32_t>(top_k) < count);
+  const bool use_k = top_k > 0;
   const bool use_p = top_p < 1.0f;
   const bool use_min_p = min_p > 0.f;
   const float ln_min_p = use_min_p ? logf(min_p) : 0.f;

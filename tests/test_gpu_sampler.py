@@ -345,3 +345,31 @@ def test_long_rows():
     say(f"[gpu] sampler on {R} rows of {cols} fp32 tokens")
     check_rows(bits, "float32", mask, None, 0.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
     check_rows(bits, "float32", mask, None, 1.0, 0, 1.0, 0.0, seed=1, offset=1, rows=[1], min_exact=1.0)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_non_finite_logits_are_not_candidates(dtype):
+    """NaN (quiet and signalling patterns), +inf and -inf logits never count
+    as candidates: rows with only NaNs take the first pass's fast form, rows
+    with +inf its exact form; greedy and top-p agree with the oracle."""
+    rng = np.random.default_rng(16)
+    R, cols = 32, 1000
+    bits = random_logits(rng, dtype, R, cols)
+    if dtype == "float32":
+        pos_inf, neg_inf, qnan, snan = 0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001
+    elif dtype == "float16":
+        pos_inf, neg_inf, qnan, snan = 0x7C00, 0xFC00, 0x7E00, 0x7C01
+    else:
+        pos_inf, neg_inf, qnan, snan = 0x7F80, 0xFF80, 0x7FC0, 0x7F81
+    for r in range(R):
+        idx = rng.choice(cols, 40, replace=False)
+        kinds = [qnan, snan, neg_inf] + ([pos_inf] if r % 2 else [])   # odd rows also hold +inf
+        for j, i in enumerate(idx):
+            bits[r, i] = kinds[j % len(kinds)]
+    bits[3, :] = snan                                                  # nothing finite at all
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.6, (cols + 31) // 32, rng)
+    say(f"[gpu] sampler non-finite logits {dtype}")
+    with np.errstate(invalid="ignore"):            # numpy notes the signalling NaNs it converts
+        tok = check_rows(bits, dtype, mask, None, 0.0, 0, 1.0, 0.0, seed=3, offset=0, min_exact=1.0)
+        assert tok[3] == -1
+        check_rows(bits, dtype, mask, None, 1.0, 0, 0.8, 0.0, seed=3, offset=1)
