@@ -401,9 +401,9 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // Fast form: each group's tokens are gated by their mask bits (others
   // -inf) and reduced by a max tree; a thread keeps its best value and the
   // words of the group holding it, and decodes that one group at the end
-  // for the lowest index with that value.  A group maximum that is NaN or +inf (possible
-  // only for rows holding such logits, which are not candidates) sends the
-  // whole block through the exact per-token form instead.
+  // for the lowest index with that value.  A group maximum that is NaN or
+  // +inf (possible only for rows holding such logits, which are not
+  // candidates) sends the whole block through the exact per-token form.
   const bool first_pass = !(temp > 0.f) || top_p < 1.0f || min_p > 0.f;
   float best = -__builtin_inff();
   if (first_pass) {
