@@ -186,8 +186,8 @@ def main():
         all_configs()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the apply has no cross-GPU step, and this build runs on a "
-              "single GPU only (--gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU (--gpus 1): the apply has no cross-GPU step, and each GPU of a "
+              "larger job would run the same calls on its own rows.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
