@@ -274,6 +274,7 @@ def main():
     cpu = cpu_baseline(wl, eff, args.cpu_seconds)
     if not args.no_extras:
         extras["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl, eff, args.cpu_seconds / 2)
+        extras["cpu_baseline_python_small"] = cpu_baseline_python()
 
     line = {
         "metric": METRIC,
@@ -632,6 +633,28 @@ def cpu_baseline_all_cores(wl, eff, seconds):
             "kind": "oracle", "cpu_model": model,
             "sample": f"{sum(done)} row applications of the same workload's indexed rows, split over "
                       f"{len(parts)} threads, in {el:.1f} s"}
+
+
+def cpu_baseline_python():
+    """The oracle's pure-Python loop on the two small workloads, one pass each.
+
+    The tiny fp32 [1, 32000] case and the bf16 [8, 50257] case with its
+    garbage tail: the Python list version of the page's double loop, timed
+    whole (conversion to and from lists included).
+    """
+    import oracle
+    from packed_logit_bitmask_amd import workloads
+
+    out = {}
+    for wl in (workloads.tiny(), workloads.tail_bf16()):
+        rows, cols = wl.logits.shape
+        V = wl.vocab_size if wl.vocab_size is not None else min(cols, 32 * wl.mask.shape[1])
+        eff = effective_bytes(rows, V, wl.logits.dtype.itemsize)
+        t0 = time.perf_counter()
+        oracle.apply_inplace_py(wl.logits, wl.mask, wl.dtype, wl.vocab_size, None, wl.fill_value)
+        el = time.perf_counter() - t0
+        out[wl.name] = {"seconds": round(el, 3), "GBps": round(eff / el / 1e9, 5), "cores": 1}
+    return out
 
 
 if __name__ == "__main__":
