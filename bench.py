@@ -267,6 +267,7 @@ def main():
         extras["variants_cold"] = per
         extras["ceiling_cold"] = ceilings(torch, dev, eff, nsets, args.steps, stream, rmw_bytes=R * V * 2)
         extras["gated_rows_cold"] = gated_rows(torch, dev, mb, workloads, args.steps, stream)
+        extras["vocab_shard_tp8_cold"] = vocab_shard(torch, dev, mb, wl, args.steps, stream)
         extras["host_path"] = host_path(torch, mb, wl, eff)
         extras["mask_upload_overlap"] = upload_overlap(torch, dev, mb, wl)
         extras["fused_sampler_cold"] = sampler_times(torch, dev, mb, workloads, stream)
@@ -379,6 +380,35 @@ def graph_ms(torch, fn, steps, stream, warmup=10):
     ms = s.elapsed_time(e) / steps
     del g
     return ms
+
+
+def vocab_shard(torch, dev, mb, wl, steps, stream, shards=8):
+    """One GPU's share of the headline under an 8-way vocabulary split.
+
+    Shard 0 of the [256, 128256] bf16 logits: its own [256, 16032] buffer
+    (16032 = 128256 / 8 = 501 mask words), the mask read in place through a
+    strided view of the full [256, 4008] mask (row stride 4008 words), the
+    same 128 indexed rows; cold rotation over buffer sets.
+    """
+    import numpy as np
+
+    cols = wl.logits.shape[1] // shards
+    words = cols // 32
+    R = len(wl.indices)
+    eff = effective_bytes(R, cols, 2)
+    set_bytes = wl.logits.shape[0] * cols * 2 + wl.mask.nbytes
+    nsets = max(2, math.ceil(2 * INFINITY_CACHE / set_bytes))
+    shard = np.ascontiguousarray(wl.logits[:, :cols])
+    sets = [(torch.from_numpy(shard.view(np.int16)).to(dev).view(torch.bfloat16),
+             torch.from_numpy(wl.mask).to(dev)[:, :words],
+             torch.from_numpy(wl.indices).to(dev)) for _ in range(nsets)]
+    ms = graph_ms(torch, lambda k: mb.mi_apply_bitmask_inplace(sets[k % nsets][0], sets[k % nsets][1], cols,
+                                                               sets[k % nsets][2]), steps, stream)
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": f"bf16 [256, {cols}] (vocab shard 0 of {shards}), mask view [256, {words}] with row stride "
+                        f"{wl.mask.shape[1]} words, {R} indexed rows",
+            "effective_bytes": eff, "ms_per_step": ms, "GBps": eff / (ms * 1e-3) / 1e9}
 
 
 def gated_rows(torch, dev, mb, workloads, steps, stream):
