@@ -511,3 +511,27 @@ def test_longest_row():
     del x
     oracle.apply_inplace(bits, mask, "bfloat16")
     assert np.array_equal(got, bits)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_out_onto_its_own_input_is_the_inplace_apply(dtype):
+    """out == logits with the same row pitch is the in-place apply (the
+    out-of-place entry's documented alias rule): whole-buffer equality with
+    the oracle's in-place result, with and without an index list, on an odd
+    row pitch."""
+    rng = np.random.default_rng(17)
+    rows, cols = 40, 3001
+    for n_idx in (None, 17):
+        wl, _, _ = workloads.random_case(rng, dtype, rows, cols, vocab_size=2990, n_indices=n_idx, density=0.4,
+                                         fill_value=-1e4)
+        P = Placed(rng, wl.logits, wl.dtype, cols + 5, 3)
+        hmask, dmask = place_mask(rng, wl.mask, wl.mask.shape[1], 3)
+        want = P.host.copy()
+        oracle.apply_inplace(P.view(want), hmask, wl.dtype, wl.vocab_size,
+                             None if wl.indices is None else list(wl.indices), wl.fill_value)
+        dl = P.device()
+        ind = None if wl.indices is None else torch.from_numpy(np.asarray(wl.indices, np.int32)).to("cuda")
+        say(f"[gpu] out onto its own input {dtype} indices={n_idx}")
+        mb.mi_apply_bitmask_out(dl, dmask, dl, wl.vocab_size, ind, wl.fill_value)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(P.dev, wl.dtype), want)
