@@ -175,7 +175,9 @@ mi_status_t mi_apply_bitmask_out_ex(
  * (k <= 0, p >= 1, m <= 0 disable them; ties at a cutoff are kept) and the
  * kept set is their intersection; one token is drawn from it with
  * probability proportional to its softmax probability (Gumbel-max).
- * temperature <= 0 takes the argmax (lowest index on ties).
+ * A temperature that is not positive (<= 0, or NaN) takes the argmax
+ * (lowest index on ties).  top_p <= 0 keeps only the largest value and its
+ * ties.
  *
  * Candidates are the tokens v < V whose logit is finite and, when mask is
  * not NULL, whose bit v % 32 of word mask[row, v / 32] is set -- the apply

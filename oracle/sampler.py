@@ -35,6 +35,9 @@ Readings where the page is silent:
   0 < u < 1 and u is exact in binary32 (24 significant bits);
 * Gumbel variate: g = -ln(-ln(u));
 * greedy and Gumbel-max ties go to the lowest token index;
+* a temperature that is not positive -- NaN included -- is greedy; top-p
+  with p <= 0 keeps only the largest value and its ties (any mass reaches
+  p), as p = 0 does;
 * a row with no allowed token draws -1; a logit that is not finite (-inf
   from an earlier mask, +inf, NaN) counts as not allowed.
 
@@ -130,7 +133,7 @@ def sample_row(logits: np.ndarray, allowed: np.ndarray, temperature: float, top_
     allowed = allowed & np.isfinite(logits)
     if not allowed.any():
         return -1, {"keep": np.zeros(V, bool), "candidates": {-1}}
-    if temperature <= 0.0:
+    if not temperature > 0.0:  # T <= 0, or NaN: greedy
         best = np.max(logits[allowed])
         token = int(np.flatnonzero(allowed & (logits == best))[0])
         return token, {"keep": allowed & (logits == best), "candidates": {token}}
@@ -162,7 +165,7 @@ def filtered_probs(logits: np.ndarray, allowed: np.ndarray, temperature: float, 
     out = np.zeros(logits.size)
     if not allowed.any():
         return out
-    if temperature <= 0.0:
+    if not temperature > 0.0:  # T <= 0, or NaN: greedy
         best = np.max(logits[allowed])
         out[int(np.flatnonzero(allowed & (logits == best))[0])] = 1.0
         return out

@@ -639,8 +639,9 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         const WaveSuffix<unsigned long long> ws(&hist_m[0][0]);
         unsigned long long need = s_sel.need_p;
         if (shift == 24) {  // every candidate is in this histogram: its total is Z
-          const unsigned long long target =
-              static_cast<unsigned long long>(ceil(static_cast<double>(top_p) * static_cast<double>(ws.total())));
+          // p <= 0 keeps just the largest value, as p = 0 does: any mass reaches it
+          const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(ws.total());
+          const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
           need = target ? target : 1ull;
         }
         int d;

@@ -112,7 +112,11 @@ def test_greedy_exact_with_ties_and_masks(dtype):
 
 @pytest.mark.parametrize("T,k,p,m", [(1.0, 0, 1.0, 0.0), (0.7, 40, 1.0, 0.0), (1.2, 0, 0.9, 0.0),
                                       (1.0, 0, 1.0, 0.02), (0.8, 100, 0.95, 0.01), (1.5, 1, 1.0, 0.0),
-                                      (1.0, 5000, 0.3, 0.0)])
+                                      (1.0, 5000, 0.3, 0.0),
+                                      # edges: p = 0 and p < 0 keep only the max (and its ties); min_p = 1
+                                      # likewise; k above the vocab keeps everything; a tiny temperature
+                                      (1.0, 0, 0.0, 0.0), (1.0, 0, -0.5, 0.0), (1.0, 0, 1.0, 1.0),
+                                      (1.0, 100000, 1.0, 0.0), (1e-3, 0, 1.0, 0.0), (math.nan, 0, 0.9, 0.0)])
 def test_draws_match_oracle(T, k, p, m):
     rng = np.random.default_rng(2)
     R, cols = 48, 4100

@@ -128,3 +128,23 @@ def test_planted_gumbel_mistakes_fail_distribution(name, monkeypatch):
     assert chi_square_ok(draws(z, a, 1.0, 0, 1.0, 0.0, 6000), probs)
     monkeypatch.setattr(S, "gumbel", MUTANT_GUMBELS[name])
     assert not chi_square_ok(draws(z, a, 1.0, 0, 1.0, 0.0, 6000), probs)
+
+
+def test_non_positive_temperature_and_top_p_edges():
+    """Readings where the page is silent, pinned against direct definitions:
+    a temperature that is not positive (0, negative, NaN) is the argmax of
+    the allowed finite logits (lowest index on ties); top-p with p <= 0 keeps
+    exactly the tokens equal to the largest allowed logit."""
+    rng = np.random.default_rng(31)
+    x = np.round(rng.standard_normal(200) * 2, 1)            # many ties
+    allowed = rng.random(200) < 0.5
+    best = np.max(x[allowed])
+    argmax = int(np.flatnonzero(allowed & (x == best))[0])
+    for T in (0.0, -1.0, float("nan")):
+        tok, _ = S.sample_row(x, allowed, T, 0, 1.0, 0.0, 1, 2, 0)
+        assert tok == argmax
+    for p in (0.0, -0.5, -math.inf):
+        cut = S.keep_threshold(x, allowed, 0, p, 0.0)
+        assert cut == best
+        keep = allowed & (x >= cut)
+        assert np.array_equal(keep, allowed & (x == best))
