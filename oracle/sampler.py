@@ -37,7 +37,8 @@ Readings where the page is silent:
 * greedy and Gumbel-max ties go to the lowest token index;
 * a temperature that is not positive -- NaN included -- is greedy; top-p
   with p <= 0 keeps only the largest value and its ties (any mass reaches
-  p), as p = 0 does;
+  p), as p = 0 does, and so does min-p with m >= 1 (no filter empties a set
+  that has a candidate);
 * a row with no allowed token draws -1; a logit that is not finite (-inf
   from an earlier mask, +inf, NaN) counts as not allowed.
 
@@ -115,7 +116,8 @@ def keep_threshold(z: np.ndarray, allowed: np.ndarray, top_k: int, top_p: float,
         reach = np.flatnonzero(mass_at_or_above >= top_p)
         cut = max(cut, values[reach[0]] if reach.size else values[-1])
     if min_p > 0.0:
-        cut = max(cut, zmax + math.log(min_p))
+        # the cut never passes the largest value: min_p >= 1 keeps it and its ties
+        cut = max(cut, zmax + min(math.log(min_p), 0.0))
     return cut
 
 

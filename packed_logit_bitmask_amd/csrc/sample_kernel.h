@@ -491,10 +491,13 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
 
   const float inv_t = 1.0f / temp;
   const float zmax = best * inv_t;  // used only when the first pass ran
-  const bool use_k = top_k > 0;
-  const bool use_p = top_p < 1.0f;
+  // An infinite temperature makes every z equal: each filter then keeps all
+  // candidates (ties are kept), so top-k and top-p have nothing to do.
+  const bool use_k = top_k > 0 && inv_t > 0.f;
+  const bool use_p = top_p < 1.0f && inv_t > 0.f;
   const bool use_min_p = min_p > 0.f;
-  const float ln_min_p = use_min_p ? logf(min_p) : 0.f;
+  // min_p >= 1 keeps just the largest value and its ties (the cut never passes z_max)
+  const float ln_min_p = use_min_p ? fminf(logf(min_p), 0.f) : 0.f;
 
   // Gumbel-max over the kept tokens: key = z - ln(-ln u) for each kept token
   // of a group, u from the token's Philox word; sink(q, key) receives them.

@@ -116,7 +116,9 @@ def test_greedy_exact_with_ties_and_masks(dtype):
                                       # edges: p = 0 and p < 0 keep only the max (and its ties); min_p = 1
                                       # likewise; k above the vocab keeps everything; a tiny temperature
                                       (1.0, 0, 0.0, 0.0), (1.0, 0, -0.5, 0.0), (1.0, 0, 1.0, 1.0),
-                                      (1.0, 100000, 1.0, 0.0), (1e-3, 0, 1.0, 0.0), (math.nan, 0, 0.9, 0.0)])
+                                      (1.0, 100000, 1.0, 0.0), (1e-3, 0, 1.0, 0.0), (math.nan, 0, 0.9, 0.0),
+                                      # min_p above 1 keeps the max; an infinite temperature keeps everything
+                                      (1.0, 0, 1.0, 1.5), (math.inf, 5, 0.5, 0.2)])
 def test_draws_match_oracle(T, k, p, m):
     rng = np.random.default_rng(2)
     R, cols = 48, 4100

@@ -148,3 +148,23 @@ def test_non_positive_temperature_and_top_p_edges():
         assert cut == best
         keep = allowed & (x >= cut)
         assert np.array_equal(keep, allowed & (x == best))
+
+
+def test_min_p_at_or_above_one_and_infinite_temperature():
+    """min_p >= 1 keeps exactly the tokens equal to the largest allowed logit
+    (no filter empties a set that has a candidate); an infinite temperature
+    makes every z equal, so top-k, top-p and min-p keep every allowed token
+    and the draw is the argmax of the Gumbel variates alone."""
+    rng = np.random.default_rng(32)
+    x = np.round(rng.standard_normal(300) * 2, 1)
+    allowed = rng.random(300) < 0.5
+    best = np.max(x[allowed])
+    for m in (1.0, 1.5, math.inf):
+        cut = S.keep_threshold(x, allowed, 0, 1.0, m)
+        assert np.array_equal(allowed & (x >= cut), allowed & (x == best))
+    z = x / math.inf
+    cut = S.keep_threshold(z, allowed, 3, 0.5, 0.9)
+    assert np.array_equal(allowed & (z >= cut), allowed)
+    tok, _ = S.sample_row(x, allowed, math.inf, 3, 0.5, 0.9, 4, 5, 6)
+    g = S.gumbel(S.uniforms(4, 5, 6, 300))
+    assert tok == int(np.flatnonzero(allowed)[np.argmax(g[allowed])])
