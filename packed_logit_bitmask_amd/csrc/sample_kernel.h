@@ -92,6 +92,11 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Whether an order key belongs to a finite value: keys of finite floats run
+// from that of -FLT_MAX (0x00800000) to that of +FLT_MAX (0xFF7FFFFF); the
+// infinities and NaNs lie outside.
+__device__ __forceinline__ bool finite_key(uint32_t key) { return key - 0x00800000u < 0xFF000000u; }
+
 __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
@@ -186,6 +191,25 @@ struct RowView {
       }
     }
     return r;
+  }
+
+  // Group g's mask bits (token q in bit q); 0 for a group past the full ones.
+  __device__ __forceinline__ uint32_t mask_bits(const Raw& r, int32_t g, bool full) const {
+    return full ? (has_mask ? (r.w >> ((g & 3) * 8)) & 0xFFu : 0xFFu) : 0u;
+  }
+
+  // Group values only.
+  __device__ __forceinline__ void values(const Raw& r, float x[8]) const {
+    if constexpr (sizeof(Bits) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * q] = D::value(static_cast<Bits>(r.v[q] & 0xFFFFu));
+        x[2 * q + 1] = D::value(static_cast<Bits>(r.v[q] >> 16));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = D::value(r.v[q]);
+    }
   }
 
   // Group g's values and a bit per token that is a candidate (mask bit set,
@@ -575,7 +599,9 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       __syncthreads();
       const uint32_t pk = s_sel.prefix_k, pp = s_sel.prefix_p;
       const uint32_t phi = max(use_k ? pk : 0u, use_p ? pp : 0u);
-      walk_row<last ? BYTES / 2 : BYTES, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+      // One group: `bits` are its mask bits; a token is a candidate when its
+      // bit is set and its key is that of a finite value.
+      const auto group = [&](int32_t i0, const float* x, uint32_t bits) {
         uint32_t above = 0, inside = 0;
         uint32_t digit[8];
 #pragma unroll
@@ -583,7 +609,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           const uint32_t key = order_key(x[q]);
           const uint32_t d = (key >> shift) & 255u;
           digit[q] = d;
-          if ((ok >> q) & 1u) {
+          if (((bits >> q) & 1u) && finite_key(key)) {
             if (use_k && (key & pmask) == pk) atomicAdd(&hist_n[wave][d], 1u);
             if (use_p && (key & pmask) == pp) {
               // 2^31 exp(z - z_max) in [0, 2^31]: the hardware base-2
@@ -612,7 +638,18 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
             atomicMax(&s_bin[digit[q]], packed);
           }
         });
-      });
+      };
+      walk_row_raw<last ? BYTES / 2 : BYTES, THREADS>(
+          rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+            float x[8];
+            rv.values(raw, x);
+            group(8 * g, x, rv.mask_bits(raw, g, full));
+          });
+      if (rv.V & 7) {  // the partial last group: exact candidate bits from the plain loads
+        float x[8] = {};
+        const uint32_t ok = t == 0 ? rv.load_tail(x) : 0u;
+        group(rv.V & ~7, x, ok);
+      }
       __syncthreads();
       // fold the per-wave histograms into row 0
       for (int b = t; b < 256; b += THREADS) {
