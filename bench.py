@@ -13,11 +13,19 @@ Timing: inputs sit in HBM; the timed region rotates over enough independent
 buffer sets (> 2 x the 256 MB Infinity Cache) that no step finds its data in
 a cache.  The K launches are captured once in a HIP graph and replayed, so
 the host's launch rate does not pace the GPU; HIP events on the launch
-stream bracket the replay.  A warm figure (one buffer set, cache-resident,
-not HBM) is reported beside it.  The CPU baseline is the oracle's plain C
-loop on one host core over repeated passes of the same workload.
+stream bracket the replay.  The CPU baseline is the oracle's plain C loop
+on one host core over repeated passes of the same workload.
+
+Besides the headline, the one JSON line carries: a warm figure (one buffer
+set, cache-resident, not HBM), each kernel variant cold, fill and copy
+ceilings (one of them moving the apply's physical bytes), the gated apply
+with its report, one GPU's share under a vocabulary split, the host-memory
+path, mask upload behind a forward pass, the fused sampler against a
+stock-torch sampler, and the oracle on all host cores and in pure Python.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto]
+       python bench.py --all-configs       (every workload, next to a plain fill)
+       python bench.py --copy-calibration  (plain copies, for scaling HBM counters)
 """
 
 from __future__ import annotations
