@@ -221,11 +221,13 @@ mi_status_t mi_apply_bitmask_sample(
  * "Bitmask Operations", Notes: Device: CPU tensors get a CPU
  * implementation).  Same arguments, rules and results as the device entry
  * points, except that every pointer is HOST memory, the call runs
- * synchronously on the calling thread plus up to `num_threads` worker
- * threads (<= 0: half the hardware threads; inputs below 2^20 elements run
- * on one thread), and -- since the host can read the index list -- an index
- * outside [0, min(rows, mask_rows)) is MI_ERR_BAD_INDICES before anything is
- * written.  These never touch a GPU and are never used for device memory.
+ * synchronously on up to `num_threads` threads, the calling thread among
+ * them (<= 0: half the hardware threads; at most 256; inputs below 2^20
+ * elements run on the calling thread alone; rows a worker thread could not
+ * be started for run on the calling thread), and -- since the host can read
+ * the index list -- an index outside [0, min(rows, mask_rows)) is
+ * MI_ERR_BAD_INDICES before anything is written.  They allocate nothing,
+ * never touch a GPU and are never used for device memory.
  */
 mi_status_t mi_apply_bitmask_inplace_host(
     void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,

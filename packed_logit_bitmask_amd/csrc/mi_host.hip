@@ -5,8 +5,8 @@
 #include "mi_bitmask.h"
 
 #include <cstdint>
+#include <cstring>
 #include <thread>
-#include <vector>
 
 #include "host_apply.h"
 #include "host_checks.h"
@@ -22,34 +22,26 @@ int resolve_threads(int threads, int64_t elements) {
   return hc > 1 ? static_cast<int>(hc / 2) : 1;
 }
 
-mi_status_t host_rows(const Plan& p, int64_t rows, const int32_t* indices, std::vector<int64_t>* out) {
-  out->clear();
-  if (!indices) {
-    out->resize(rows);
-    for (int64_t i = 0; i < rows; ++i) (*out)[i] = i;
-    return MI_OK;
-  }
-  out->reserve(p.R);
-  for (int64_t i = 0; i < p.R; ++i) {  // host memory: the values can be checked
+// Host memory can be read, so an index list is checked value by value
+// before anything is written.
+mi_status_t check_host_indices(const Plan& p, const int32_t* indices) {
+  for (int64_t i = 0; indices && i < p.R; ++i) {
     const int64_t r = indices[i];
     if (r < 0 || r >= p.row_limit)
       return fail(MI_ERR_BAD_INDICES, "index %lld outside [0, %lld)", (long long)r, (long long)p.row_limit);
-    out->push_back(r);
   }
   return MI_OK;
 }
 
 template <typename T>
-void host_apply(void* logits, int64_t ls, const int32_t* mask, int64_t ms, const Plan& p,
-                const std::vector<int64_t>& rows, int threads) {
+void host_apply(void* logits, int64_t ls, const int32_t* mask, int64_t ms, const Plan& p, const int32_t* indices,
+                int threads) {
   const uint32_t* m = reinterpret_cast<const uint32_t*>(mask);
-  const int nt = resolve_threads(threads, static_cast<int64_t>(rows.size()) * p.V);
+  const int nt = resolve_threads(threads, p.R * p.V);
   if constexpr (sizeof(T) == 4)
-    mi_host::apply_u32(static_cast<uint32_t*>(logits), ls, m, ms, p.V, rows.data(),
-                       static_cast<int64_t>(rows.size()), static_cast<uint32_t>(p.fill), nt);
+    mi_host::apply_u32(static_cast<uint32_t*>(logits), ls, m, ms, p.V, indices, p.R, static_cast<uint32_t>(p.fill), nt);
   else
-    mi_host::apply_u16(static_cast<uint16_t*>(logits), ls, m, ms, p.V, rows.data(),
-                       static_cast<int64_t>(rows.size()), static_cast<uint16_t>(p.fill), nt);
+    mi_host::apply_u16(static_cast<uint16_t*>(logits), ls, m, ms, p.V, indices, p.R, static_cast<uint16_t>(p.fill), nt);
 }
 }  // namespace
 
@@ -65,11 +57,10 @@ MI_API mi_status_t mi_apply_bitmask_inplace_host(void* logits, mi_dtype_t dtype,
   if (overlaps(p.mask, p.logits)) return fail(MI_ERR_ALIAS, "mask overlaps logits");
   if (overlaps(p.indices, p.logits)) return fail(MI_ERR_ALIAS, "indices overlap logits");
   if (p.V == 0 || p.R == 0) return MI_OK;
-  std::vector<int64_t> rs;
-  st = host_rows(p, rows, indices, &rs);
+  st = check_host_indices(p, indices);
   if (st != MI_OK) return st;
-  if (p.esize == 4) host_apply<uint32_t>(logits, logits_row_stride, mask, mask_row_stride, p, rs, num_threads);
-  else host_apply<uint16_t>(logits, logits_row_stride, mask, mask_row_stride, p, rs, num_threads);
+  if (p.esize == 4) host_apply<uint32_t>(logits, logits_row_stride, mask, mask_row_stride, p, indices, num_threads);
+  else host_apply<uint16_t>(logits, logits_row_stride, mask, mask_row_stride, p, indices, num_threads);
   return MI_OK;
 }
 
@@ -96,15 +87,14 @@ MI_API mi_status_t mi_apply_bitmask_out_host(void* out, int64_t out_row_stride, 
   if (overlaps(ob, p.logits)) return fail(MI_ERR_ALIAS, "out overlaps logits");
   if (overlaps(ob, p.mask)) return fail(MI_ERR_ALIAS, "out overlaps mask");
   if (overlaps(ob, p.indices)) return fail(MI_ERR_ALIAS, "out overlaps indices");
-  std::vector<int64_t> rs;
-  st = host_rows(p, rows, indices, &rs);  // check the index list before writing anything
+  st = check_host_indices(p, indices);  // before anything is written
   if (st != MI_OK) return st;
   for (int64_t r = 0; r < rows; ++r)
     std::memcpy(static_cast<char*>(out) + r * out_row_stride * p.esize,
                 static_cast<const char*>(logits) + r * logits_row_stride * p.esize, static_cast<size_t>(cols) * p.esize);
   if (p.V == 0 || p.R == 0) return MI_OK;
-  if (p.esize == 4) host_apply<uint32_t>(out, out_row_stride, mask, mask_row_stride, p, rs, num_threads);
-  else host_apply<uint16_t>(out, out_row_stride, mask, mask_row_stride, p, rs, num_threads);
+  if (p.esize == 4) host_apply<uint32_t>(out, out_row_stride, mask, mask_row_stride, p, indices, num_threads);
+  else host_apply<uint16_t>(out, out_row_stride, mask, mask_row_stride, p, indices, num_threads);
   return MI_OK;
 }
 

@@ -90,6 +90,19 @@ def test_threaded_rows_match():
         assert np.array_equal(bits_of(x, wl.dtype), want), threads
 
 
+def test_threaded_rows_without_an_index_list():
+    # every row, split over threads: each thread's rows start past row 0
+    wl = workloads.mixed_bf16(rows=40, n_indices=8)
+    want = oracle.apply_inplace(wl.logits.copy(), wl.mask, wl.dtype, wl.vocab_size, None, wl.fill_value)
+    for threads in (2, 7, 40, 300):
+        x = as_tensor(wl.logits.copy(), wl.dtype)
+        mb.mi_apply_bitmask_inplace_host(x, torch.from_numpy(wl.mask), wl.vocab_size, None, num_threads=threads)
+        assert np.array_equal(bits_of(x, wl.dtype), want), threads
+        out = mb.mi_apply_bitmask_out_host(as_tensor(wl.logits.copy(), wl.dtype), torch.from_numpy(wl.mask),
+                                           vocab_size=wl.vocab_size, fill_value=wl.fill_value, num_threads=threads)
+        assert np.array_equal(bits_of(out, wl.dtype), want), threads
+
+
 def test_host_checks_index_values():
     x = torch.zeros(4, 64, dtype=torch.float32)
     m = torch.zeros(3, 2, dtype=torch.int32)
