@@ -303,8 +303,9 @@ def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None,
     prm.offset = int(offset) & 0xFFFFFFFFFFFFFFFF
     if out is None:
         out = torch.empty(rows, dtype=torch.int64, device=logits.device)
-    if out.dtype != torch.int64 or out.numel() != rows or not out.is_contiguous():
-        raise ValueError("out must be a contiguous int64 tensor with one entry per row")
+    if (out.dtype != torch.int64 or out.numel() != rows or not out.is_contiguous()
+            or out.device != logits.device):
+        raise ValueError("out must be a contiguous int64 tensor with one entry per row, on the logits' GPU")
     if mask is not None:
         M = _check_mask(mask, logits.device)
         mp, mr, mc, ms = M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M)
@@ -355,6 +356,13 @@ def mi_apply_bitmask_out(logits, mask, out=None, vocab_size: Optional[int] = Non
 # host-memory (CPU tensor) entry points
 # ----------------------------------------------------------------------------
 
+def _check_host_mask(mask):
+    torch = _torch()
+    if not isinstance(mask, torch.Tensor) or mask.dtype != torch.int32:
+        raise TypeError("bitmask must be an int32 tensor")
+    return _as_rows(mask, "bitmask")
+
+
 def _host_indices(indices):
     torch = _torch()
     if indices is None:
@@ -371,7 +379,7 @@ def mi_apply_bitmask_inplace_host(logits, mask, vocab_size: Optional[int] = None
         raise ValueError("the host entry point takes CPU tensors only")
     lib = load_library()
     L = _as_rows(logits, "logits")
-    M = _as_rows(mask, "bitmask")
+    M = _check_host_mask(mask)
     ip, n, keep = _host_indices(indices)
     check(lib.mi_apply_bitmask_inplace_host(
         L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
@@ -390,9 +398,11 @@ def mi_apply_bitmask_out_host(logits, mask, out=None, vocab_size: Optional[int] 
     lib = load_library()
     if out is None:
         out = torch.empty_like(logits, memory_format=torch.contiguous_format)
+    if out.dtype != logits.dtype or out.shape != logits.shape:
+        raise ValueError("out must match logits in dtype and shape")
     L = _as_rows(logits, "logits")
     O = _as_rows(out, "out")
-    M = _as_rows(mask, "bitmask")
+    M = _check_host_mask(mask)
     ip, n, keep = _host_indices(indices)
     check(lib.mi_apply_bitmask_out_host(
         O.data_ptr(), _row_stride(O), L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1],

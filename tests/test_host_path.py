@@ -112,6 +112,17 @@ def test_host_checks_index_values():
     assert torch.count_nonzero(x) == 0        # nothing written before the check
 
 
+def test_host_binding_rejects_mismatched_tensors():
+    x = torch.zeros(2, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        mb.mi_apply_bitmask_inplace_host(x, torch.zeros(2, 2, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        mb.mi_apply_bitmask_out_host(x, torch.zeros(2, 2, dtype=torch.int32), out=torch.zeros(2, 64))
+    with pytest.raises(ValueError):
+        mb.mi_apply_bitmask_out_host(x, torch.zeros(2, 2, dtype=torch.int32),
+                                     out=torch.zeros(2, 32, dtype=torch.bfloat16))
+
+
 def test_xgrammar_surface_shapes_and_reset():
     assert mb.bitmask_dtype == torch.int32
     assert mb.get_bitmask_shape(8, 50257) == (8, 1571)
