@@ -91,10 +91,15 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     const uint32_t* mk = m ? m + mr0 : nullptr;
     // Histogram LDS only when some row may filter; deep load pipeline when a
     // compute unit holds one row at a time (rows <= 256), shallow otherwise.
+    // Filtered 16-bit rows always take 1024-thread blocks: those search the
+    // full 16-bit key histogram, which fills most of a compute unit's LDS
+    // (the radix histograms of the fallback share its space).
     const bool may_filter = ar.top_k || ar.top_p || ar.top_k_all > 0 || ar.top_p_all < 1.0f;
-    const bool deep = n <= 256;
+    const bool fine = may_filter && dtype != MI_DTYPE_F32;
+    const bool deep = n <= 256 || fine;
     const int threads = deep ? 1024 : 256;
-    const size_t lds = may_filter ? mi::sample_hist_bytes(threads) : 0;
+    const size_t lds = fine ? std::max(mi::sample_fine_bytes(), mi::sample_hist_bytes(threads))
+                            : (may_filter ? mi::sample_hist_bytes(threads) : 0);
 #define MI_SAMPLE(TAG, BITS, BYTES, THREADS)                                                                   \
   mi::sample_rows<TAG, BYTES, THREADS><<<n, THREADS, lds, stream>>>(reinterpret_cast<const BITS*>(lg),          \
                                                                     logits_row_stride, mk, mask_row_stride, V,   \

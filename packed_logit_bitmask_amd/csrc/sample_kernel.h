@@ -19,6 +19,11 @@
 //   pass 1   max logit over the candidates and its (lowest) index -> greedy
 //            rows and rows with no candidate end here; skipped when the row
 //            uses neither top-p nor min-p (nothing else needs it);
+//   16-bit   bf16 and fp16 rows with top-k or top-p, in 1024-thread blocks:
+//            one pass counts the candidates under each of the 65536 16-bit
+//            keys (LDS) and finds the maximum; both cuts follow from the
+//            counts (fine_search).  The radix passes below remain for fp32
+//            and for a row where one key holds 65536 tokens or more;
 //   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
@@ -76,11 +81,13 @@ struct F32Bits {
 struct BF16Bits {
   using Bits = uint16_t;
   static constexpr int kZeroLowBits = 16;
+  static constexpr uint32_t kKey16Lo = 0x0080u, kKey16Hi = 0xFF7Fu;  // order_key16 of -max, +max
   static __device__ __forceinline__ float value(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 };
 struct F16Bits {
   using Bits = uint16_t;
   static constexpr int kZeroLowBits = 13;
+  static constexpr uint32_t kKey16Lo = 0x0400u, kKey16Hi = 0xFBFFu;  // order_key16 of -max, +max
   static __device__ __forceinline__ float value(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
 };
 
@@ -90,6 +97,25 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t b = __float_as_uint(x);
   b = b == 0x80000000u ? 0u : b;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// The same order on the raw pattern of a 16-bit float (bf16, fp16), as a
+// 16-bit key; -0 takes the key of +0.  bits_of_key16 inverts it (giving +0
+// for the key of zero).
+__device__ __forceinline__ uint32_t order_key16(uint32_t h) {
+  h = h == 0x8000u ? 0u : h;
+  return (h & 0x8000u) ? (h ^ 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ uint32_t bits_of_key16(uint32_t k) {
+  return (k & 0x8000u) ? (k & 0x7FFFu) : (k ^ 0xFFFFu);
+}
+
+// Softmax mass of a token in fixed point, 2^31 exp(z - z_max) with z = x / T,
+// in [0, 2^31] for x at or below the maximum: the hardware base-2
+// exponential, converted through u32 (exact in that range).  Every top-p
+// search sums these, so equal inputs always give equal sums.
+__device__ __forceinline__ uint32_t fixed_mass(float x, float inv_t, float zmax) {
+  return static_cast<uint32_t>(__builtin_amdgcn_exp2f((x * inv_t - zmax) * 1.4426950408889634f) * 2147483648.0f);
 }
 
 // Whether an order key belongs to a finite value: keys of finite floats run
@@ -385,6 +411,245 @@ constexpr size_t sample_hist_bytes(int threads) {
   return static_cast<size_t>(threads / 64) * 256 * (sizeof(uint32_t) + sizeof(unsigned long long));
 }
 
+// The full-resolution histogram of a 16-bit type's keys: 65536 counts of 16
+// bits, two per word, plus one spare word per lane that non-candidates add
+// to (so the add needs no branch and spreads over the banks).
+constexpr int kFineWords = 32768;
+constexpr size_t sample_fine_bytes() { return static_cast<size_t>(kFineWords + 64) * sizeof(uint32_t); }
+
+// Whether a block shape searches 16-bit keys through the full histogram
+// (it needs most of a compute unit's LDS, so one 1024-thread block per unit).
+template <typename D, int THREADS>
+constexpr bool kFineSearch = sizeof(typename D::Bits) == 2 && THREADS == 1024;
+
+// Two 16-bit order keys at once, from a word holding two raw 16-bit floats
+// (low token in the low half): a negative value's bits are inverted, a
+// positive one's sign bit set.  Unlike order_key16, -0 keeps a key of its
+// own, one below +0's (callers that need them equal handle it).
+__device__ __forceinline__ uint32_t order_key16x2(uint32_t two) {
+  typedef short short2_t __attribute__((ext_vector_type(2)));
+  const short2_t sign = __builtin_bit_cast(short2_t, two) >> static_cast<short>(15);  // per half: 0 or all ones
+  return two ^ (__builtin_bit_cast(uint32_t, sign) | 0x80008000u);
+}
+
+// Top-k and top-p cuts of a 16-bit row from one pass over it.  Each finite
+// bf16 or fp16 value has a 16-bit key of its own, and the tokens under one
+// key share their value, so a count per key answers both searches exactly:
+// top-k counts down from the largest key; top-p sums count x mass per key,
+// the mass being the fixed-point one the radix search sums token by token,
+// so the cut is the same.  The pass counts every token the mask allows,
+// finite or not, under its key; the keys of the finite values form
+// [D::kKey16Lo, D::kKey16Hi], and only those count as candidates.  -0 and +0
+// have adjacent keys: a cut on either is the value zero, which keeps both.
+// The largest candidate (*best; -inf when the row has none) is the highest
+// finite key with a count.  The counts are 16 bits wide, so a key holding
+// 65536 tokens or more would wrap: the counts then fall short of the tokens
+// counted, and the function returns false for the radix search to take
+// over (no thread reads `fine` after the barrier that decides it).  On
+// success *cut is the order key (of the widened value) at and above which
+// tokens are kept, 0 to keep every candidate.
+template <typename D, int BYTES, int THREADS>
+__device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine, float inv_t, bool use_k,
+                                            int32_t top_k, bool use_p, float top_p, float* best, uint32_t* cut) {
+  using Bits = typename D::Bits;
+  constexpr int kWaves = THREADS / 64;
+  constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
+  __shared__ uint32_t s_n[kWaves], s_kmax[kWaves], s_all[kWaves], s_c[kWaves], s_cut[2];
+  __shared__ unsigned long long s_m[kWaves];
+  const int t = static_cast<int>(threadIdx.x);
+  const int lane = lane_id(), wave = t >> 6;
+
+  uint4* f4 = reinterpret_cast<uint4*>(fine);
+  for (int i = t; i < (kFineWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (t < 2) s_cut[t] = 0u;
+  __syncthreads();
+
+  // ---- the pass: the 16-bit count of key k is half k & 1 of word k / 2; a
+  // token the mask rules out adds to this lane's spare word instead, so the
+  // add needs no branch and spreads over the banks
+  uint32_t allowed = 0;  // tokens the mask allows below V
+  const uint32_t spare = 2u * (kFineWords + static_cast<uint32_t>(lane));
+  const auto add = [&](uint32_t k, uint32_t bit) {
+    const uint32_t kk = bit ? k : spare;
+    atomicAdd(&fine[kk >> 1], 1u << ((kk & 1u) << 4));
+  };
+  const auto group = [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+    const uint32_t bits = rv.mask_bits(raw, g, full);
+    allowed += __builtin_popcount(bits);
+#pragma unroll
+    for (int p2 = 0; p2 < 4; ++p2) {
+      const uint32_t k2 = order_key16x2(raw.v[p2]);
+      add(k2 & 0xFFFFu, (bits >> (2 * p2)) & 1u);
+      add(k2 >> 16, (bits >> (2 * p2 + 1)) & 1u);
+    }
+  };
+  // short rows keep half as many bytes in flight, so fewer loads fall past V
+  if (rv.V <= 4 * 8 * THREADS)
+    walk_row_raw<BYTES / 2, THREADS>(rv, group);
+  else
+    walk_row_raw<BYTES, THREADS>(rv, group);
+  if ((rv.V & 7) && t == 0) {  // the partial last group, by plain loads
+    for (int32_t i = rv.V & ~7; i < rv.V; ++i) {
+      const uint32_t bit = rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u;
+      allowed += bit;
+      add(order_key16x2(rv.row[i]) & 0xFFFFu, bit);
+    }
+  }
+  __syncthreads();
+
+  // ---- sums: thread t holds keys [64t, 64t + 64) (words [32t, 32t + 32),
+  // read in a rotated order so a wave's lanes hit different banks).  Only
+  // the threads at the two ends of the key range hold keys of non-finite
+  // values; the others count every key.
+  const uint32_t k0 = 64u * static_cast<uint32_t>(t);
+  const auto in_range = [](uint32_t k) { return k - D::kKey16Lo <= kSpan; };
+  const bool inside = in_range(k0) && in_range(k0 + 63);
+  uint32_t c = 0, all = 0, ktop = 0;  // candidates, every count, highest candidate key + 1
+  uint32_t nz = 0;                    // bit j: word 32t + j counts a candidate
+  if (inside) {
+    for (int j = 0; j < 32; ++j) {
+      const int jj = (j + t) & 31;
+      const uint32_t w = fine[32 * t + jj];
+      all += (w & 0xFFFFu) + (w >> 16);
+      nz |= (w ? 1u : 0u) << jj;
+    }
+    c = all;
+    if (nz) {
+      const int jt = 31 - __builtin_clz(nz);
+      ktop = k0 + 2 * jt + ((fine[32 * t + jt] >> 16) ? 2 : 1);
+    }
+  } else {
+    for (int j = 0; j < 32; ++j) {
+      const int jj = (j + t) & 31;
+      const uint32_t w = fine[32 * t + jj];
+      const uint32_t ka = k0 + 2 * jj, lo = w & 0xFFFFu, hi = w >> 16;
+      all += lo + hi;
+      if (in_range(ka) && lo) {
+        c += lo;
+        ktop = max(ktop, ka + 1);
+        nz |= 1u << jj;
+      }
+      if (in_range(ka + 1) && hi) {
+        c += hi;
+        ktop = max(ktop, ka + 2);
+        nz |= 1u << jj;
+      }
+    }
+  }
+  // block totals (every count, highest key) and suffix totals of c, high keys first
+  uint32_t sc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t vc = static_cast<uint32_t>(__shfl_down(static_cast<int>(sc), o));
+    if (lane + o < 64) sc += vc;
+    ktop = max(ktop, static_cast<uint32_t>(__shfl_xor(static_cast<int>(ktop), o)));
+    allowed += static_cast<uint32_t>(__shfl_xor(static_cast<int>(allowed), o));
+    all += static_cast<uint32_t>(__shfl_xor(static_cast<int>(all), o));
+  }
+  if (lane == 0) {
+    s_c[wave] = sc;
+    s_kmax[wave] = ktop;
+    s_n[wave] = allowed;
+    s_all[wave] = all;
+  }
+  __syncthreads();
+  uint32_t tot_c = 0, tot_allowed = 0, tot_all = 0;
+  ktop = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    tot_c += s_c[w];
+    tot_allowed += s_n[w];
+    tot_all += s_all[w];
+    ktop = max(ktop, s_kmax[w]);
+    if (w > wave) sc += s_c[w];
+  }
+  if (tot_all != tot_allowed) return false;  // a count wrapped
+  if (tot_c == 0) {
+    *best = -__builtin_inff();
+    return true;
+  }
+  *best = D::value(static_cast<Bits>(bits_of_key16(ktop - 1)));
+  const float zmax = *best * inv_t;
+  const auto mass = [&](uint32_t k) { return fixed_mass(D::value(static_cast<Bits>(bits_of_key16(k))), inv_t, zmax); };
+  const auto cut_of = [](uint32_t k) { return order_key(D::value(static_cast<Bits>(bits_of_key16(k)))); };
+
+  // ---- top-p masses per thread, then their suffix totals
+  unsigned long long m = 0, sm = 0, tot_m = 0;
+  if (use_p) {
+    for (uint32_t b = nz; b; b &= b - 1u) {  // only the words that count a candidate
+      const int j = __builtin_ctz(b);
+      const uint32_t w = fine[32 * t + j];
+      const uint32_t ka = k0 + 2 * j;
+      if ((w & 0xFFFFu) && in_range(ka)) m += static_cast<unsigned long long>(w & 0xFFFFu) * mass(ka);
+      if ((w >> 16) && in_range(ka + 1)) m += static_cast<unsigned long long>(w >> 16) * mass(ka + 1);
+    }
+    sm = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long vm = __shfl_down(sm, o);
+      if (lane + o < 64) sm += vm;
+    }
+    if (lane == 0) s_m[wave] = sm;
+    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+      tot_m += s_m[w];
+      if (w > wave) sm += s_m[w];
+    }
+  }
+
+  // ---- each search: the one thread whose keys hold the crossing walks them
+  // from the top; the cut is the largest key whose suffix reaches the need
+  if (use_k) {
+    const uint32_t need = static_cast<uint32_t>(top_k);  // more than the candidates: keep all
+    if (need <= tot_c && sc >= need && sc - c < need) {
+      uint32_t run = sc - c;
+      for (int j = 31; j >= 0; --j) {
+        const uint32_t w = fine[32 * t + j];
+        const uint32_t ka = k0 + 2 * j;
+        if (in_range(ka + 1)) run += w >> 16;
+        if (run >= need) {
+          s_cut[0] = cut_of(ka + 1);
+          break;
+        }
+        if (in_range(ka)) run += w & 0xFFFFu;
+        if (run >= need) {
+          s_cut[0] = cut_of(ka);
+          break;
+        }
+      }
+    }
+  }
+  if (use_p) {
+    // p <= 0 keeps just the largest value, as p = 0 does: any mass reaches it
+    const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(tot_m);
+    const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
+    const unsigned long long need = target ? target : 1ull;
+    if (need <= tot_m && sm >= need && sm - m < need) {
+      unsigned long long run = sm - m;
+      for (int j = 31; j >= 0; --j) {
+        const uint32_t w = fine[32 * t + j];
+        const uint32_t ka = k0 + 2 * j;
+        if ((w >> 16) && in_range(ka + 1)) {
+          run += static_cast<unsigned long long>(w >> 16) * mass(ka + 1);
+          if (run >= need) {
+            s_cut[1] = cut_of(ka + 1);
+            break;
+          }
+        }
+        if ((w & 0xFFFFu) && in_range(ka)) {
+          run += static_cast<unsigned long long>(w & 0xFFFFu) * mass(ka);
+          if (run >= need) {
+            s_cut[1] = cut_of(ka);
+            break;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  *cut = max(s_cut[0], s_cut[1]);
+  return true;
+}
+
 // One block of THREADS threads per row.  1024 threads with 128 bytes of
 // logits in flight per thread when each compute unit holds one row at a
 // time; 256 threads with 64 bytes so several rows share a compute unit when
@@ -429,8 +694,30 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // +inf (possible only for rows holding such logits, which are not
   // candidates) sends the whole block through the exact per-token form.
   const bool first_pass = !(temp > 0.f) || top_p < 1.0f || min_p > 0.f;
+  const float inv_t = 1.0f / temp;  // used only when temp > 0
+  // An infinite temperature makes every z equal: each filter then keeps all
+  // candidates (ties are kept), so top-k and top-p have nothing to do.
+  const bool use_k = temp > 0.f && top_k > 0 && inv_t > 0.f;
+  const bool use_p = temp > 0.f && top_p < 1.0f && inv_t > 0.f;
   float best = -__builtin_inff();
-  if (first_pass) {
+  bool have_best = false;  // the largest candidate is known
+  bool have_cut = false;   // the top-k / top-p cut is known
+  uint32_t cut = 0;        // keep tokens with order_key(x) >= cut
+  if constexpr (kFineSearch<D, THREADS>) {
+    // 16-bit rows with a filter: one pass gives the maximum and both cuts
+    if (use_k || use_p) {
+      have_cut = fine_search<D, BYTES, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p,
+                                                top_p, &best, &cut);
+      if (have_cut) {  // else the radix search below, after the first pass if the row needs the maximum
+        have_best = true;
+        if (best == -__builtin_inff()) {  // no candidate
+          if (t == 0) out[r] = -1;
+          return;
+        }
+      }
+    }
+  }
+  if (first_pass && !have_best) {
     int32_t besti = 0x7FFFFFFF;
     int32_t bestg = -1;
     typename RowView<D>::Raw braw{};  // the best group's words, kept so it need not be read again
@@ -513,12 +800,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     }
   }
 
-  const float inv_t = 1.0f / temp;
-  const float zmax = best * inv_t;  // used only when the first pass ran
-  // An infinite temperature makes every z equal: each filter then keeps all
-  // candidates (ties are kept), so top-k and top-p have nothing to do.
-  const bool use_k = top_k > 0 && inv_t > 0.f;
-  const bool use_p = top_p < 1.0f && inv_t > 0.f;
+  const float zmax = best * inv_t;  // used only when the maximum is known
   const bool use_min_p = min_p > 0.f;
   // min_p >= 1 keeps just the largest value and its ties (the cut never passes z_max)
   const float ln_min_p = use_min_p ? fminf(logf(min_p), 0.f) : 0.f;
@@ -561,7 +843,9 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     }
   };
 
-  if (use_k || use_p) {
+  // Before the last radix pass fuses the draw (fp16, fp32): its decision.
+  constexpr bool kFuseDraw = (D::kZeroLowBits / 8) * 8 < 16;
+  if ((use_k || use_p) && !have_cut) {
     // ---- top-k and top-p cuts: radix passes over 8-bit digits of the key,
     // high to low, both searches in the same passes.  The first mass
     // histogram covers every candidate, so its total is the softmax mass Z.
@@ -585,7 +869,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     // the second digit and its bucket a whole binade, often thousands of
     // tokens, which would all pay for the generator; a separate draw pass
     // over the kept tokens alone is cheaper there.
-    constexpr bool kFuseDraw = kLastShift < 16;
+    static_assert(kFuseDraw == (kLastShift < 16), "draw fusion follows the last digit");
     // one radix pass; `last` (a compile-time flag) also draws, with half as
     // many bytes in flight to leave registers for the generator
     const auto radix_pass = [&](int shift, uint32_t pmask, auto last_tag) {
@@ -612,11 +896,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           if (((bits >> q) & 1u) && finite_key(key)) {
             if (use_k && (key & pmask) == pk) atomicAdd(&hist_n[wave][d], 1u);
             if (use_p && (key & pmask) == pp) {
-              // 2^31 exp(z - z_max) in [0, 2^31]: the hardware base-2
-              // exponential, converted through u32 (exact in that range); a
-              // mass that truncates to 0 adds nothing
-              const uint32_t m = static_cast<uint32_t>(
-                  __builtin_amdgcn_exp2f((x[q] * inv_t - zmax) * 1.4426950408889634f) * 2147483648.0f);
+              const uint32_t m = fixed_mass(x[q], inv_t, zmax);  // one that truncates to 0 adds nothing
               if (m) atomicAdd(&hist_m[wave][d], static_cast<unsigned long long>(m));
             }
             if constexpr (last) {
@@ -702,7 +982,6 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     radix_pass(kLastShift, pmask, std::integral_constant<bool, kFuseDraw>{});
     constexpr uint32_t kLow = (1u << kLastShift) - 1u;
     const auto complete = [&](uint32_t prefix) { return prefix | ((prefix & 0x80000000u) ? 0u : kLow); };
-    uint32_t cut = 0;  // keep tokens with order_key(x) >= cut
     if (use_k) cut = max(cut, complete(s_sel.prefix_k));
     if (use_p) cut = max(cut, complete(s_sel.prefix_p));
     if constexpr (kFuseDraw) {
@@ -716,7 +995,10 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
                 static_cast<int32_t>(~static_cast<uint32_t>(packed)));
         }
       }
-    } else {
+    }
+  }
+  if (use_k || use_p) {
+    if (have_cut || !kFuseDraw) {
       // ---- draw: Gumbel-max over the tokens at or above the cut
       walk_row<BYTES / 2, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
         uint32_t at_or_above = 0;

@@ -56,6 +56,8 @@ class MaskStager:
     def upload(self) -> None:
         """Enqueue the host -> device copy of the current slot on the side stream."""
         k = self.k
+        if k < 0:
+            raise RuntimeError("upload() before host(): fill the buffer host() returns first")
         with torch.cuda.stream(self.copy_stream):
             if self.consumed[k] is not None:
                 self.copy_stream.wait_event(self.consumed[k])   # do not overwrite a mask still being applied
@@ -66,6 +68,8 @@ class MaskStager:
 
     def _consume(self, stream):
         k = self.k
+        if k < 0 or self.copied[k] is None:
+            raise RuntimeError("apply before upload(): the current slot holds no mask yet")
         s = stream or torch.cuda.current_stream(self.device)
         s.wait_event(self.copied[k])          # device-side wait for this slot's upload
         return k, s

@@ -308,10 +308,12 @@ def test_graph_replay_matches_eager():
     del g
 
 
-@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
-def test_many_rows_variant(dtype):
-    """More than 256 rows selects the 256-thread variant; per-row parameters,
-    a ragged vocab tail and a few rows with nothing allowed."""
+@pytest.mark.parametrize("dtype,filters", [("float32", True), ("bfloat16", True), ("float16", False)])
+def test_many_rows_variant(dtype, filters):
+    """More than 256 rows: fp32 rows, and 16-bit rows without top-k or top-p,
+    take the 256-thread variant; 16-bit rows that may filter keep 1024-thread
+    blocks (the full key histogram).  Per-row parameters, a ragged vocab tail
+    and a few rows with nothing allowed."""
     rng = np.random.default_rng(11)
     R, cols, V = 300, 2051, 2045
     bits = random_logits(rng, dtype, R, cols)
@@ -319,12 +321,31 @@ def test_many_rows_variant(dtype):
     allowed[[4, 150, 299]] = False
     mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
     T = rng.choice([0.0, 0.6, 1.0, 1.4], R).astype(np.float32)
-    k = rng.choice([0, 1, 10, 300], R).astype(np.int32)
-    p = rng.choice([1.0, 0.95, 0.5], R).astype(np.float32)
+    k = rng.choice([0, 1, 10, 300] if filters else [0], R).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.5] if filters else [1.0], R).astype(np.float32)
     m = rng.choice([0.0, 0.02], R).astype(np.float32)
-    say(f"[gpu] sampler 300 rows {dtype}")
+    say(f"[gpu] sampler 300 rows {dtype} filters={filters}")
     tok = check_rows(bits, dtype, mask, V, T, k, p, m, seed=13, offset=77)
     assert tok[4] == -1 and tok[150] == -1 and tok[299] == -1
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_key_holding_65536_tokens(dtype):
+    """16-bit rows count their tokens per key in 16 bits; a key holding 65536
+    or more candidates would wrap, and the row then takes the radix search.
+    Rows with 65535 (no wrap), 65536 and 66000 copies of one value among
+    random logits, and a row without copies, under top-k (a cut above the
+    copies, and one that keeps them all) and top-p."""
+    rng = np.random.default_rng(19)
+    R, cols = 4, 70003
+    bits = random_logits(rng, dtype, R, cols)
+    one = {"float16": 0x3400, "bfloat16": 0x3E80}[dtype]          # 0.25
+    bits[bits == one] = one + 1                                   # only the planted copies hold 0.25
+    for r, copies in enumerate((65535, 65536, 66000, 0)):
+        bits[r, rng.choice(cols, copies, replace=False)] = one
+    say(f"[gpu] sampler keys holding 65536 tokens {dtype}")
+    for (T, k, p, seed) in ((1.0, 10, 1.0, 1), (1.0, 2000, 1.0, 2), (0.9, 0, 0.6, 3), (1.0, 50, 0.9, 4)):
+        check_rows(bits, dtype, None, None, T, k, p, 0.0, seed=seed, offset=0, min_exact=0.75)
 
 
 def test_rows_split_over_launches():
