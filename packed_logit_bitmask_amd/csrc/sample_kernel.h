@@ -454,14 +454,17 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   using Bits = typename D::Bits;
   constexpr int kWaves = THREADS / 64;
   constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
-  __shared__ uint32_t s_n[kWaves], s_kmax[kWaves], s_all[kWaves], s_c[kWaves], s_cut[2];
-  __shared__ unsigned long long s_m[kWaves];
+  __shared__ uint32_t s_n[kWaves], s_kmax[kWaves], s_all[kWaves], s_c[kWaves], s_cut[2], s_cross[2];
+  __shared__ unsigned long long s_m[kWaves], s_above[2];
   const int t = static_cast<int>(threadIdx.x);
   const int lane = lane_id(), wave = t >> 6;
 
   uint4* f4 = reinterpret_cast<uint4*>(fine);
   for (int i = t; i < (kFineWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (t < 2) s_cut[t] = 0u;
+  if (t < 2) {
+    s_cut[t] = 0u;
+    s_cross[t] = ~0u;  // no crossing: keep every candidate
+  }
   __syncthreads();
 
   // ---- the pass: the 16-bit count of key k is half k & 1 of word k / 2; a
@@ -575,12 +578,15 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   // ---- top-p masses per thread, then their suffix totals
   unsigned long long m = 0, sm = 0, tot_m = 0;
   if (use_p) {
-    for (uint32_t b = nz; b; b &= b - 1u) {  // only the words that count a candidate
-      const int j = __builtin_ctz(b);
-      const uint32_t w = fine[32 * t + j];
-      const uint32_t ka = k0 + 2 * j;
-      if ((w & 0xFFFFu) && in_range(ka)) m += static_cast<unsigned long long>(w & 0xFFFFu) * mass(ka);
-      if ((w >> 16) && in_range(ka + 1)) m += static_cast<unsigned long long>(w >> 16) * mass(ka + 1);
+#pragma unroll 4
+    for (int j = 0; j < 32; ++j) {
+      const int jj = (j + t) & 31;
+      const uint32_t w = fine[32 * t + jj];
+      if ((nz >> jj) & 1u) {  // a word that counts a candidate
+        const uint32_t ka = k0 + 2 * jj;
+        if ((w & 0xFFFFu) && in_range(ka)) m += static_cast<unsigned long long>(w & 0xFFFFu) * mass(ka);
+        if ((w >> 16) && in_range(ka + 1)) m += static_cast<unsigned long long>(w >> 16) * mass(ka + 1);
+      }
     }
     sm = m;
 #pragma unroll
@@ -596,54 +602,36 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
     }
   }
 
-  // ---- each search: the one thread whose keys hold the crossing walks them
-  // from the top; the cut is the largest key whose suffix reaches the need
-  if (use_k) {
-    const uint32_t need = static_cast<uint32_t>(top_k);  // more than the candidates: keep all
-    if (need <= tot_c && sc >= need && sc - c < need) {
-      uint32_t run = sc - c;
-      for (int j = 31; j >= 0; --j) {
-        const uint32_t w = fine[32 * t + j];
-        const uint32_t ka = k0 + 2 * j;
-        if (in_range(ka + 1)) run += w >> 16;
-        if (run >= need) {
-          s_cut[0] = cut_of(ka + 1);
-          break;
-        }
-        if (in_range(ka)) run += w & 0xFFFFu;
-        if (run >= need) {
-          s_cut[0] = cut_of(ka);
-          break;
-        }
-      }
-    }
+  // ---- each search: the thread whose 64 keys hold the crossing posts its
+  // number and the total above them; then one wave per search takes those
+  // keys, one per lane, and a suffix scan finds the largest key whose
+  // suffix reaches the need (top-k on wave 0, top-p on wave 1)
+  const uint32_t need_k = static_cast<uint32_t>(top_k);  // more than the candidates: keep all
+  const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(tot_m);
+  const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
+  const unsigned long long need_p = target ? target : 1ull;  // p <= 0 keeps just the largest value
+  if (use_k && need_k <= tot_c && sc >= need_k && sc - c < need_k) {
+    s_cross[0] = static_cast<uint32_t>(t);
+    s_above[0] = sc - c;
   }
-  if (use_p) {
-    // p <= 0 keeps just the largest value, as p = 0 does: any mass reaches it
-    const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(tot_m);
-    const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
-    const unsigned long long need = target ? target : 1ull;
-    if (need <= tot_m && sm >= need && sm - m < need) {
-      unsigned long long run = sm - m;
-      for (int j = 31; j >= 0; --j) {
-        const uint32_t w = fine[32 * t + j];
-        const uint32_t ka = k0 + 2 * j;
-        if ((w >> 16) && in_range(ka + 1)) {
-          run += static_cast<unsigned long long>(w >> 16) * mass(ka + 1);
-          if (run >= need) {
-            s_cut[1] = cut_of(ka + 1);
-            break;
-          }
-        }
-        if ((w & 0xFFFFu) && in_range(ka)) {
-          run += static_cast<unsigned long long>(w & 0xFFFFu) * mass(ka);
-          if (run >= need) {
-            s_cut[1] = cut_of(ka);
-            break;
-          }
-        }
-      }
+  if (use_p && need_p <= tot_m && sm >= need_p && sm - m < need_p) {
+    s_cross[1] = static_cast<uint32_t>(t);
+    s_above[1] = sm - m;
+  }
+  __syncthreads();
+  const int which = wave;  // 0: top-k, 1: top-p
+  if (which < 2 && (which == 0 ? use_k : use_p) && s_cross[which] != ~0u) {
+    const uint32_t kx = 64u * s_cross[which] + static_cast<uint32_t>(lane);
+    const uint32_t n = in_range(kx) ? (fine[kx >> 1] >> ((kx & 1u) << 4)) & 0xFFFFu : 0u;
+    unsigned long long v = which == 0 ? n : (n ? static_cast<unsigned long long>(n) * mass(kx) : 0ull);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long u = __shfl_down(v, o);
+      if (lane + o < 64) v += u;
     }
+    const unsigned long long total = v + s_above[which];  // the candidates' total at and above kx
+    const uint64_t hit = __ballot(total >= (which == 0 ? static_cast<unsigned long long>(need_k) : need_p));
+    if (lane == 0) s_cut[which] = cut_of(64u * s_cross[which] + (63u - static_cast<uint32_t>(__clzll(hit))));
   }
   __syncthreads();
   *cut = max(s_cut[0], s_cut[1]);
