@@ -447,14 +447,17 @@ __device__ __forceinline__ uint32_t order_key16x2(uint32_t two) {
 // counted, and the function returns false for the radix search to take
 // over (no thread reads `fine` after the barrier that decides it).  On
 // success *cut is the order key (of the widened value) at and above which
-// tokens are kept, 0 to keep every candidate.
+// tokens are kept, 0 to keep every candidate; *cut16 the same cut as a
+// 16-bit key (0 to keep all), and *kept the number of candidates it keeps.
 template <typename D, int BYTES, int THREADS>
 __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine, float inv_t, bool use_k,
-                                            int32_t top_k, bool use_p, float top_p, float* best, uint32_t* cut) {
+                                            int32_t top_k, bool use_p, float top_p, float* best, uint32_t* cut,
+                                            uint32_t* cut16, uint32_t* kept) {
   using Bits = typename D::Bits;
   constexpr int kWaves = THREADS / 64;
   constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
   __shared__ uint32_t s_n[kWaves], s_kmax[kWaves], s_all[kWaves], s_c[kWaves], s_cut[2], s_cross[2];
+  __shared__ uint32_t s_above_n[2], s_kept[2];
   __shared__ unsigned long long s_m[kWaves], s_above[2];
   const int t = static_cast<int>(threadIdx.x);
   const int lane = lane_id(), wave = t >> 6;
@@ -610,13 +613,16 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(tot_m);
   const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
   const unsigned long long need_p = target ? target : 1ull;  // p <= 0 keeps just the largest value
+  if (t == 0) s_kept[0] = s_kept[1] = tot_c;  // a search without a crossing keeps every candidate
   if (use_k && need_k <= tot_c && sc >= need_k && sc - c < need_k) {
     s_cross[0] = static_cast<uint32_t>(t);
     s_above[0] = sc - c;
+    s_above_n[0] = sc - c;
   }
   if (use_p && need_p <= tot_m && sm >= need_p && sm - m < need_p) {
     s_cross[1] = static_cast<uint32_t>(t);
     s_above[1] = sm - m;
+    s_above_n[1] = sc - c;
   }
   __syncthreads();
   const int which = wave;  // 0: top-k, 1: top-p
@@ -624,17 +630,29 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
     const uint32_t kx = 64u * s_cross[which] + static_cast<uint32_t>(lane);
     const uint32_t n = in_range(kx) ? (fine[kx >> 1] >> ((kx & 1u) << 4)) & 0xFFFFu : 0u;
     unsigned long long v = which == 0 ? n : (n ? static_cast<unsigned long long>(n) * mass(kx) : 0ull);
+    uint32_t vn = n;  // and the candidates at and above kx
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const unsigned long long u = __shfl_down(v, o);
-      if (lane + o < 64) v += u;
+      const uint32_t un = static_cast<uint32_t>(__shfl_down(static_cast<int>(vn), o));
+      if (lane + o < 64) {
+        v += u;
+        vn += un;
+      }
     }
-    const unsigned long long total = v + s_above[which];  // the candidates' total at and above kx
+    const unsigned long long total = v + s_above[which];  // the searched total at and above kx
     const uint64_t hit = __ballot(total >= (which == 0 ? static_cast<unsigned long long>(need_k) : need_p));
-    if (lane == 0) s_cut[which] = cut_of(64u * s_cross[which] + (63u - static_cast<uint32_t>(__clzll(hit))));
+    const int L = 63 - __clzll(static_cast<long long>(hit));
+    const uint32_t at_cut = static_cast<uint32_t>(__shfl(static_cast<int>(vn), L)) + s_above_n[which];
+    if (lane == 0) {
+      s_cut[which] = 64u * s_cross[which] + static_cast<uint32_t>(L);  // a key: 0 (non-finite) keeps all
+      s_kept[which] = at_cut;
+    }
   }
   __syncthreads();
-  *cut = max(s_cut[0], s_cut[1]);
+  *cut16 = max(s_cut[0], s_cut[1]);
+  *cut = *cut16 ? cut_of(*cut16) : 0u;
+  *kept = min(use_k ? s_kept[0] : tot_c, use_p ? s_kept[1] : tot_c);  // the tighter cut keeps fewer
   return true;
 }
 
@@ -691,11 +709,13 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   bool have_best = false;  // the largest candidate is known
   bool have_cut = false;   // the top-k / top-p cut is known
   uint32_t cut = 0;        // keep tokens with order_key(x) >= cut
+  uint32_t n_kept = 0;     // with the cut from the 16-bit search: candidates at or above it
+  uint32_t cut16 = 0;      // and that cut as a 16-bit key (0: keep all)
   if constexpr (kFineSearch<D, THREADS>) {
     // 16-bit rows with a filter: one pass gives the maximum and both cuts
     if (use_k || use_p) {
       have_cut = fine_search<D, BYTES, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p,
-                                                top_p, &best, &cut);
+                                                top_p, &best, &cut, &cut16, &n_kept);
       if (have_cut) {  // else the radix search below, after the first pass if the row needs the maximum
         have_best = true;
         if (best == -__builtin_inff()) {  // no candidate
@@ -795,6 +815,13 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
 
   // Gumbel-max over the kept tokens: key = z - ln(-ln u) for each kept token
   // of a group, u from the token's Philox word; sink(q, key) receives them.
+  // -ln(-ln u) through the hardware base-2 logarithm: -ln u = -log2(u) ln 2,
+  // then -ln(that) = -log2(that) ln 2; clamped so an overflowed z (a tiny
+  // temperature) still draws a token
+  const auto gumbel_key = [&](float x, uint32_t word) {
+    const float e = -__log2f(unit_uniform(word)) * 0.6931471805599453f;
+    return fmaxf(x * inv_t - __log2f(e) * 0.6931471805599453f, -__FLT_MAX__);
+  };
   const auto gumbel_group = [&](int32_t i0, const float* x, uint32_t kept, auto&& sink) {
     uint32_t c0[4] = {static_cast<uint32_t>(i0 >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo, a.offset_hi};
     uint32_t c1[4] = {static_cast<uint32_t>(i0 >> 2) + 1u, static_cast<uint32_t>(row_base + r), a.offset_lo,
@@ -802,16 +829,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     if (kept & 0x0Fu) philox4x32_10(c0, a.seed_lo, a.seed_hi);
     if (kept & 0xF0u) philox4x32_10(c1, a.seed_lo, a.seed_hi);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      if ((kept >> q) & 1u) {
-        // -ln(-ln u) through the hardware base-2 logarithm: -ln u =
-        // -log2(u) ln 2, then -ln(that) = -log2(that) ln 2; clamped so an
-        // overflowed z (a tiny temperature) still draws a token
-        const float u = unit_uniform(q < 4 ? c0[q] : c1[q - 4]);
-        const float e = -__log2f(u) * 0.6931471805599453f;
-        sink(q, fmaxf(x[q] * inv_t - __log2f(e) * 0.6931471805599453f, -__FLT_MAX__));
-      }
-    }
+    for (int q = 0; q < 8; ++q)
+      if ((kept >> q) & 1u) sink(q, gumbel_key(x[q], q < 4 ? c0[q] : c1[q - 4]));
   };
   const auto min_p_keep = [&](const float* x, uint32_t bits) {
     if (use_min_p) {
@@ -985,7 +1004,117 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       }
     }
   }
-  if (use_k || use_p) {
+  // ---- draw after the 16-bit search
+  constexpr uint32_t kListPerWave = static_cast<uint32_t>(kFineWords) / (THREADS / 64);
+  bool drawn = false;
+  if constexpr (kFineSearch<D, THREADS>) {
+    if (have_cut) {
+      // The kept test on 16-bit keys of the raw words, two per operation:
+      // a candidate (mask bit set, finite value) at or above the cut.  The
+      // keys of -0 and +0 differ by one; a cut at +0 keeps -0 too.
+      const uint32_t lo16 = cut16 == 0u ? D::kKey16Lo : (cut16 == 0x8000u ? 0x7FFFu : cut16);
+      const uint32_t span16 = D::kKey16Hi - lo16;
+      const auto keep_of = [&](const typename RowView<D>::Raw& raw, uint32_t bits, float x[8]) {
+        uint32_t keep = 0;
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+          const uint32_t k2 = order_key16x2(raw.v[p2]);
+          keep |= ((k2 & 0xFFFFu) - lo16 <= span16 ? 1u : 0u) << (2 * p2);
+          keep |= ((k2 >> 16) - lo16 <= span16 ? 1u : 0u) << (2 * p2 + 1);
+        }
+        keep &= bits;
+        if (keep) {
+          rv.values(raw, x);
+          keep = min_p_keep(x, keep);
+        }
+        return keep;
+      };
+      // every group of the row, the partial last one included (its words
+      // loaded by thread 0 alone), through f(i0, raw, mask bits)
+      const auto walk16 = [&](auto&& f) {
+        walk_row_raw<BYTES / 2, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+          f(8 * g, raw, rv.mask_bits(raw, g, full));
+        });
+        if (rv.V & 7) {
+          typename RowView<D>::Raw raw{};
+          uint32_t bits = 0;
+          const int32_t i0 = rv.V & ~7;
+          if (t == 0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int32_t i = i0 + q;
+              if (i < rv.V) {
+                raw.v[q >> 1] |= static_cast<uint32_t>(row[i]) << (16 * (q & 1));
+                bits |= (rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u) << q;
+              }
+            }
+          }
+          f(i0, raw, bits);
+        }
+      };
+      if (n_kept >= 1024u && n_kept <= static_cast<uint32_t>(kFineWords) / 2) {
+        // Many kept tokens (the search counted them): list them first (LDS,
+        // where the histogram was, one region per wave), then run the
+        // generator on the list alone, every lane busy; a walk would run it
+        // for every group in which any lane of the wave keeps a token.
+        // With fewer, most waves keep none, and the walk skips those.
+        uint32_t* list = reinterpret_cast<uint32_t*>(s_dyn) + wave * kListPerWave;
+        uint32_t nw = 0;  // the same in every lane of the wave
+        walk16([&](int32_t i0, const typename RowView<D>::Raw& raw, uint32_t bits) {
+          float x[8];
+          const uint32_t keep = keep_of(raw, bits, x);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint64_t b = __ballot((keep >> q) & 1u);
+            if (b) {
+              const uint32_t pos = nw + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
+              if (((keep >> q) & 1u) && pos < kListPerWave) list[pos] = static_cast<uint32_t>(i0 + q);
+              nw += static_cast<uint32_t>(__popcll(b));
+            }
+          }
+        });
+        // a wave whose region filled up sends the row through the walk below
+        drawn = !__syncthreads_or(nw > kListPerWave);
+        if (drawn) {
+          // four entries per lane at a time, their logits loaded together
+          for (uint32_t e0 = static_cast<uint32_t>(lane_id()); e0 < nw; e0 += 4u * 64u) {
+            int32_t idx[4];
+            uint32_t h[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t e = e0 + 64u * u;
+              idx[u] = e < nw ? static_cast<int32_t>(list[e]) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              h[u] = __builtin_amdgcn_raw_buffer_load_b16(rv.rl, idx[u] >= 0 ? idx[u] * 2 : kSkip, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (idx[u] < 0) continue;
+              const int32_t i = idx[u];
+              uint32_t c4[4] = {static_cast<uint32_t>(i >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo,
+                                a.offset_hi};
+              philox4x32_10(c4, a.seed_lo, a.seed_hi);
+              const uint32_t word = (i & 3) == 0 ? c4[0] : (i & 3) == 1 ? c4[1] : (i & 3) == 2 ? c4[2] : c4[3];
+              offer(gumbel_key(D::value(static_cast<typename D::Bits>(h[u])), word), i);
+            }
+          }
+        }
+      }
+      if (!drawn) {
+        // ---- draw: Gumbel-max over the tokens at or above the cut, by a walk
+        walk16([&](int32_t i0, const typename RowView<D>::Raw& raw, uint32_t bits) {
+          float x[8];
+          const uint32_t keep = keep_of(raw, bits, x);
+          if (!keep) return;
+          gumbel_group(i0, x, keep, [&](int q, float key) { offer(key, i0 + q); });
+        });
+        drawn = true;
+      }
+    }
+  }
+  if ((use_k || use_p) && !drawn) {
     if (have_cut || !kFuseDraw) {
       // ---- draw: Gumbel-max over the tokens at or above the cut
       walk_row<BYTES / 2, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
@@ -1003,7 +1132,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         });
       });
     }
-  } else {
+  } else if (!drawn) {
     // ---- draw: Gumbel-max over every candidate (min-p aside)
     walk_row<BYTES / 2, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
       const uint32_t kept = min_p_keep(x, ok);
