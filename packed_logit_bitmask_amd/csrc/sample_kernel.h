@@ -1052,12 +1052,17 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           f(i0, raw, bits);
         }
       };
-      if (n_kept >= 1024u && n_kept <= static_cast<uint32_t>(kFineWords) / 2) {
+      if (n_kept >= 256u && n_kept <= static_cast<uint32_t>(rv.V) / 6u &&
+          n_kept <= static_cast<uint32_t>(kFineWords) - 4096u) {
         // Many kept tokens (the search counted them): list them first (LDS,
         // where the histogram was, one region per wave), then run the
         // generator on the list alone, every lane busy; a walk would run it
         // for every group in which any lane of the wave keeps a token.
-        // With fewer, most waves keep none, and the walk skips those.
+        // With fewer than 256, most waves keep none, and the walk skips
+        // those.  The list pays one generator call per kept token, the walk
+        // one per 4 tokens of every group it runs it for, so the list is
+        // taken for at most V / 6 kept tokens; and at most 28672, which
+        // leaves each wave's region room for its share plus 256.
         uint32_t* list = reinterpret_cast<uint32_t*>(s_dyn) + wave * kListPerWave;
         uint32_t nw = 0;  // the same in every lane of the wave
         walk16([&](int32_t i0, const typename RowView<D>::Raw& raw, uint32_t bits) {
