@@ -348,6 +348,24 @@ def test_key_holding_65536_tokens(dtype):
         check_rows(bits, dtype, None, None, T, k, p, 0.0, seed=seed, offset=0, min_exact=0.75)
 
 
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_short_rows_with_filters(dtype):
+    """16-bit rows shorter than one 8-token group, or with a ragged last
+    group, under top-k, top-p and min-p: the histogram pass reads such tokens
+    one at a time."""
+    rng = np.random.default_rng(23)
+    for V in (1, 3, 7, 9, 15, 17):
+        R = 24
+        bits = random_logits(rng, dtype, R, V)
+        allowed = rng.random((R, V)) < 0.7
+        allowed[0] = False
+        mask = workloads.pack_allowed(allowed, (V + 31) // 32, rng)
+        say(f"[gpu] sampler short rows V={V} {dtype}")
+        for (T, k, p, m, seed) in ((1.0, 2, 1.0, 0.0, 1), (0.8, 0, 0.5, 0.0, 2), (1.0, 3, 0.9, 0.1, 3)):
+            tok = check_rows(bits, dtype, mask, None, T, k, p, m, seed=seed, offset=V, min_exact=0.9)
+            assert tok[0] == -1
+
+
 def test_rows_split_over_launches():
     """More than 2^20 rows go out in several launches: the generator's row
     counter and the per-row parameter arrays continue across the split."""
