@@ -366,6 +366,28 @@ def test_short_rows_with_filters(dtype):
             assert tok[0] == -1
 
 
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_fuzz_filtered_16bit(dtype):
+    """Seeded random shapes, masks, value spreads (including heavy ties) and
+    filter settings on 16-bit rows: the histogram search and both draw forms
+    (walk and list) against the oracle."""
+    rng = np.random.default_rng(29 if dtype == "float16" else 31)
+    for case in range(12):
+        R = int(rng.integers(1, 40))
+        cols = int(rng.integers(1, 6000))
+        ties = bool(rng.integers(0, 2))
+        bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([0.3, 2.0, 8.0])), ties=ties)
+        density = rng.uniform(0.0, 1.0, (R, 1))
+        mask = workloads.pack_allowed(rng.random((R, cols)) < density, (cols + 31) // 32 + int(rng.integers(0, 2)), rng)
+        V = int(rng.integers(1, cols + 1))
+        T = rng.choice([0.5, 1.0, 1.7], R).astype(np.float32)
+        k = rng.choice([0, 1, 5, 50, 400, 10000], R).astype(np.int32)
+        p = rng.choice([1.0, 0.99, 0.9, 0.5, 0.1], R).astype(np.float32)
+        m = rng.choice([0.0, 0.0, 0.05], R).astype(np.float32)
+        say(f"[gpu] sampler fuzz {dtype} case {case}: R={R} cols={cols} V={V} ties={ties}")
+        check_rows(bits, dtype, mask, V, T, k, p, m, seed=100 + case, offset=case, min_exact=0.9)
+
+
 def test_rows_split_over_launches():
     """More than 2^20 rows go out in several launches: the generator's row
     counter and the per-row parameter arrays continue across the split."""
