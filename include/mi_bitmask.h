@@ -196,7 +196,10 @@ mi_status_t mi_apply_bitmask_out_ex(
  * params: HOST struct.  Each per-row array is a device array of `rows`
  * entries, or NULL to use the matching *_all value for every row.
  * tokens: device int64 [rows] output (8-byte aligned; may not overlap logits
- * or mask).  Asynchronous on `stream` like the apply calls.
+ * or mask).  Asynchronous on `stream` like the apply calls.  It uses no
+ * device memory beyond its arguments: its working space is on chip (for
+ * bf16 and fp16 rows with top-k or top-p, a 131 KB LDS histogram per
+ * 1024-thread block, so one block per compute unit).
  */
 typedef struct mi_sample_params {
     const float *temperature;     /* device [rows] or NULL */
