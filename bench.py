@@ -26,6 +26,7 @@ stock-torch sampler, and the oracle on all host cores and in pure Python.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto]
        python bench.py --all-configs       (every workload, next to a plain fill)
        python bench.py --copy-calibration  (plain copies, for scaling HBM counters)
+       python bench.py --sampler-calls N   (N eager sampler calls per mode, for counters)
 """
 
 from __future__ import annotations
@@ -59,6 +60,9 @@ def parse():
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the headline line, print one line timing the apply on each of the five "
                          "workloads (cold) next to a plain fill of the same bytes")
+    ap.add_argument("--sampler-calls", type=int, default=0, metavar="N",
+                    help="only call the fused sampler N times per mode on its two shapes, eagerly (for hardware "
+                         "counters)")
     return ap.parse_args()
 
 
@@ -108,6 +112,31 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "dispatches": 5}}), flush=True)
+
+
+def sampler_calls(n):
+    """N eager calls of the fused sampler per mode on the two shapes the sampler figures use.
+
+    Under rocprofv3 --pmc each call is one dispatch, in the order printed.
+    """
+    import numpy as np
+    import torch
+
+    import packed_logit_bitmask_amd as mb
+    from packed_logit_bitmask_amd import workloads
+
+    dev = torch.device("cuda:0")
+    for label, wl in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0)),
+                      ("B1024_V32000_fp16", workloads.verify_fp16())):
+        tdt = torch.bfloat16 if wl.dtype == "bfloat16" else torch.float16
+        x = torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(tdt)
+        m = torch.from_numpy(wl.mask).to(dev)
+        tok = torch.empty(wl.rows, dtype=torch.int64, device=dev)
+        for mode, kw in SAMPLER_MODES:
+            for k in range(n):
+                mb.mi_apply_bitmask_sample(x, m, wl.vocab_size, seed=1, offset=k, out=tok, **kw)
+            torch.cuda.synchronize()
+            print(json.dumps({"sampler_calls": {"shape": label, "mode": mode, "calls": n}}), flush=True)
 
 
 def all_configs():
@@ -192,6 +221,9 @@ def main():
         return
     if args.all_configs:
         all_configs()
+        return
+    if args.sampler_calls > 0:
+        sampler_calls(args.sampler_calls)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU (--gpus 1): the apply has no cross-GPU step, and each GPU of a "
@@ -500,6 +532,11 @@ def upload_overlap(torch, dev, mb, wl, steps=30):
             **out}
 
 
+SAMPLER_MODES = (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperature=1.0)),
+                 ("top_p_0.9", dict(top_p=0.9)), ("top_k_50", dict(top_k=50)),
+                 ("top_k_50_top_p_0.9_min_p_0.05", dict(top_k=50, top_p=0.9, min_p=0.05)))
+
+
 def sampler_times(torch, dev, mb, workloads, stream, steps=200):
     """The fused apply + sampler at the two batch/vocab shapes the logits-processor page times.
 
@@ -521,9 +558,7 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
                 for _ in range(nsets)]
         tok = torch.empty(R, dtype=torch.int64, device=dev)
         res = {}
-        for mode, kw in (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperature=1.0)),
-                         ("top_p_0.9", dict(top_p=0.9)), ("top_k_50", dict(top_k=50)),
-                         ("top_k_50_top_p_0.9_min_p_0.05", dict(top_k=50, top_p=0.9, min_p=0.05))):
+        for mode, kw in SAMPLER_MODES:
             ms = graph_ms(torch, lambda k, kw=kw: mb.mi_apply_bitmask_sample(
                 sets[k % nsets][0], sets[k % nsets][1], wl.vocab_size, seed=1, offset=k, out=tok, **kw),
                 steps, stream)
