@@ -388,6 +388,27 @@ def test_fuzz_filtered_16bit(dtype):
         check_rows(bits, dtype, mask, V, T, k, p, m, seed=100 + case, offset=case, min_exact=0.9)
 
 
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_kept_tokens_crowding_one_wave(dtype):
+    """The listed draw gives each wave of the block a region of 2048 entries.
+    Here every kept token lies in groups that one wave reads (thread t reads
+    groups t, t + 1024, ...; wave 0 those with t < 64), 8000 of them, so that
+    wave's region overflows and the row must take the walk instead."""
+    rng = np.random.default_rng(37)
+    R, cols = 4, 128000
+    x = rng.standard_normal((R, cols)).astype(np.float32) - np.float32(12.0)
+    group = np.arange(cols) // 8
+    x[:, (group % 1024) < 64] += np.float32(16.0)      # wave 0's groups: 8000 tokens around +4
+    if dtype == "float16":
+        bits = x.astype(np.float16).view(np.uint16)
+    else:
+        b = x.view(np.uint32)
+        bits = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    say(f"[gpu] sampler kept tokens crowding one wave {dtype}")
+    check_rows(bits, dtype, None, None, 1.0, 0, 0.999, 0.0, seed=41, offset=0, min_exact=0.75)
+    check_rows(bits, dtype, None, None, 1.0, 6000, 1.0, 0.0, seed=42, offset=1, min_exact=0.75)
+
+
 def test_rows_split_over_launches():
     """More than 2^20 rows go out in several launches: the generator's row
     counter and the per-row parameter arrays continue across the split."""
