@@ -581,14 +581,20 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   // ---- top-p masses per thread, then their suffix totals
   unsigned long long m = 0, sm = 0, tot_m = 0;
   if (use_p) {
-#pragma unroll 4
-    for (int j = 0; j < 32; ++j) {
-      const int jj = (j + t) & 31;
-      const uint32_t w = fine[32 * t + jj];
-      if ((nz >> jj) & 1u) {  // a word that counts a candidate
-        const uint32_t ka = k0 + 2 * jj;
-        if ((w & 0xFFFFu) && in_range(ka)) m += static_cast<unsigned long long>(w & 0xFFFFu) * mass(ka);
-        if ((w >> 16) && in_range(ka + 1)) m += static_cast<unsigned long long>(w >> 16) * mass(ka + 1);
+    // eight words at a time, in the rotated order (different banks across
+    // the wave), loaded together before any is used
+    const uint32_t rot = static_cast<uint32_t>(t) & 31u;
+    const uint32_t nzr = rot ? (nz >> rot) | (nz << (32u - rot)) : nz;  // bit j: word (j + t) & 31
+    for (int j0 = 0; j0 < 32; j0 += 8) {
+      if (!((nzr >> j0) & 0xFFu)) continue;
+      uint32_t w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[u] = fine[32 * t + ((j0 + u + t) & 31)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t ka = k0 + 2 * static_cast<uint32_t>((j0 + u + t) & 31);
+        if ((w[u] & 0xFFFFu) && in_range(ka)) m += static_cast<unsigned long long>(w[u] & 0xFFFFu) * mass(ka);
+        if ((w[u] >> 16) && in_range(ka + 1)) m += static_cast<unsigned long long>(w[u] >> 16) * mass(ka + 1);
       }
     }
     sm = m;
