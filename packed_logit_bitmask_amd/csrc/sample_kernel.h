@@ -10,8 +10,9 @@
 // "apply_packed_bitmask"), it lies below the vocab size and its logit is
 // finite -- so a masked token is never drawn.  The logits are only read.
 //
-// One block per row (1024 threads when each compute unit holds one row, 256
-// when many rows share one).  Each pass walks the row in groups of 8
+// One block per row (1024 threads when each compute unit holds one row, or
+// when 16-bit rows may filter; 256 when many rows share a unit).  Each pass
+// walks the row in groups of 8
 // consecutive tokens per thread through raw buffer loads (16-byte vectors
 // when the row start is aligned), several groups in flight per thread; trip
 // counts are uniform across the block.
@@ -20,10 +21,10 @@
 //            rows and rows with no candidate end here; skipped when the row
 //            uses neither top-p nor min-p (nothing else needs it);
 //   16-bit   bf16 and fp16 rows with top-k or top-p, in 1024-thread blocks:
-//            one pass counts the candidates under each of the 65536 16-bit
-//            keys (LDS) and finds the maximum; both cuts follow from the
-//            counts (fine_search).  The radix passes below remain for fp32
-//            and for a row where one key holds 65536 tokens or more;
+//            one pass counts the tokens the mask allows under each of the
+//            65536 16-bit keys (LDS); the maximum and both cuts follow from
+//            the counts (fine_search).  The radix passes below remain for
+//            fp32 and for a row where one key holds 65536 tokens or more;
 //   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
@@ -42,11 +43,14 @@
 //            by the hardware log2 instruction, rescaled), u from
 //            Philox4x32-10 (counter (i / 4, row, offset lo, offset hi), key
 //            (seed lo, seed hi), word i % 4; u = (floor(x / 2^9) + 1/2) / 2^23),
-//            ties to the lowest index.  A pass of its own, except for fp16
-//            and fp32 rows with top-k or top-p, where the last radix pass
-//            draws as it counts.
+//            ties to the lowest index.  A pass of its own, except where the
+//            last radix pass (fp16, fp32) draws as it counts.  After the
+//            16-bit search the kept test runs on packed 16-bit keys, and a
+//            sparse kept set is first listed in LDS so the generator runs
+//            on the list alone.
 //
-// Histograms are private to each wave (LDS), folded after every pass.
+// The radix histograms are private to each wave (LDS), folded after every
+// pass.
 #pragma once
 
 #include <hip/hip_runtime.h>
