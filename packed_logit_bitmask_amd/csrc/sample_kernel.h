@@ -453,10 +453,14 @@ __device__ __forceinline__ uint32_t order_key16x2(uint32_t two) {
 // success *cut is the order key (of the widened value) at and above which
 // tokens are kept, 0 to keep every candidate; *cut16 the same cut as a
 // 16-bit key (0 to keep all), and *kept the number of candidates it keeps.
+// A row of at most 4 groups per thread comes already loaded in pre[4] (group
+// j * THREADS + t in pre[j], with `preloaded` set); otherwise the pass reads
+// the row.
 template <typename D, int BYTES, int THREADS>
 __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine, float inv_t, bool use_k,
                                             int32_t top_k, bool use_p, float top_p, float* best, uint32_t* cut,
-                                            uint32_t* cut16, uint32_t* kept) {
+                                            uint32_t* cut16, uint32_t* kept,
+                                            const typename RowView<D>::Raw (&pre)[4], bool preloaded) {
   using Bits = typename D::Bits;
   constexpr int kWaves = THREADS / 64;
   constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
@@ -493,11 +497,16 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
       add(k2 >> 16, (bits >> (2 * p2 + 1)) & 1u);
     }
   };
-  // short rows keep half as many bytes in flight, so fewer loads fall past V
-  if (rv.V <= 4 * 8 * THREADS)
-    walk_row_raw<BYTES / 2, THREADS>(rv, group);
-  else
+  if (preloaded) {  // a short row, already loaded by the caller: group j * THREADS + t in pre[j]
+    const int32_t nfull = rv.V >> 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t g = j * THREADS + t;
+      group(g, pre[j], g < nfull);
+    }
+  } else {
     walk_row_raw<BYTES, THREADS>(rv, group);
+  }
   if ((rv.V & 7) && t == 0) {  // the partial last group, by plain loads
     for (int32_t i = rv.V & ~7; i < rv.V; ++i) {
       const uint32_t bit = rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u;
@@ -721,11 +730,25 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   uint32_t cut = 0;        // keep tokens with order_key(x) >= cut
   uint32_t n_kept = 0;     // with the cut from the 16-bit search: candidates at or above it
   uint32_t cut16 = 0;      // and that cut as a 16-bit key (0: keep all)
+  // A 16-bit row with a filter and at most 4 groups per thread is loaded once
+  // into registers: the histogram pass and the draw both use these words.
+  typename RowView<D>::Raw pre[4] = {};
+  const bool preloaded = kFineSearch<D, THREADS> && (use_k || use_p) && rv.V <= 4 * 8 * THREADS;
   if constexpr (kFineSearch<D, THREADS>) {
+    if (preloaded) {
+      const int32_t nfull = rv.V >> 3;
+      if (rv.aligned) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre[j] = rv.template load_raw<true>(j * THREADS + t, j * THREADS + t < nfull);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre[j] = rv.template load_raw<false>(j * THREADS + t, j * THREADS + t < nfull);
+      }
+    }
     // 16-bit rows with a filter: one pass gives the maximum and both cuts
     if (use_k || use_p) {
       have_cut = fine_search<D, BYTES, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p,
-                                                top_p, &best, &cut, &cut16, &n_kept);
+                                                top_p, &best, &cut, &cut16, &n_kept, pre, preloaded);
       if (have_cut) {  // else the radix search below, after the first pass if the row needs the maximum
         have_best = true;
         if (best == -__builtin_inff()) {  // no candidate
@@ -860,8 +883,11 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     }
   };
 
-  // Before the last radix pass fuses the draw (fp16, fp32): its decision.
-  constexpr bool kFuseDraw = (D::kZeroLowBits / 8) * 8 < 16;
+  // Whether the last radix pass draws as it counts: fp32 only.  A 16-bit row
+  // reaches the radix passes only when a key holds 65536 tokens or more (the
+  // histogram search covers the rest), and a separate draw keeps the
+  // kernel's register count down for the common path.
+  constexpr bool kFuseDraw = sizeof(typename D::Bits) == 4;
   if ((use_k || use_p) && !have_cut) {
     // ---- top-k and top-p cuts: radix passes over 8-bit digits of the key,
     // high to low, both searches in the same passes.  The first mass
@@ -881,12 +907,11 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     // under a negative one, the key complementing negatives), so they are
     // filled in after the passes instead of counted.
     constexpr int kLastShift = (D::kZeroLowBits / 8) * 8;
-    // The draw rides on the last pass only when that pass's bucket is narrow
-    // (a 16-bit prefix or finer: fp16 and fp32).  For bf16 the last pass is
-    // the second digit and its bucket a whole binade, often thousands of
-    // tokens, which would all pay for the generator; a separate draw pass
-    // over the kept tokens alone is cheaper there.
-    static_assert(kFuseDraw == (kLastShift < 16), "draw fusion follows the last digit");
+    // The draw may ride on the last pass only when that pass's bucket is
+    // narrow (a 16-bit prefix or finer).  For bf16 the last pass is the
+    // second digit and its bucket a whole binade, often thousands of tokens,
+    // which would all pay for the generator.
+    static_assert(!kFuseDraw || kLastShift < 16, "a fused draw needs a narrow last bucket");
     // one radix pass; `last` (a compile-time flag) also draws, with half as
     // many bytes in flight to leave registers for the generator
     const auto radix_pass = [&](int shift, uint32_t pmask, auto last_tag) {
@@ -1042,9 +1067,18 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       // every group of the row, the partial last one included (its words
       // loaded by thread 0 alone), through f(i0, raw, mask bits)
       const auto walk16 = [&](auto&& f) {
-        walk_row_raw<BYTES / 2, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
-          f(8 * g, raw, rv.mask_bits(raw, g, full));
-        });
+        if (preloaded) {
+          const int32_t nfull = rv.V >> 3;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int32_t g = j * THREADS + t;
+            f(8 * g, pre[j], rv.mask_bits(pre[j], g, g < nfull));
+          }
+        } else {
+          walk_row_raw<BYTES / 2, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+            f(8 * g, raw, rv.mask_bits(raw, g, full));
+          });
+        }
         if (rv.V & 7) {
           typename RowView<D>::Raw raw{};
           uint32_t bits = 0;
