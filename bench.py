@@ -148,8 +148,9 @@ def all_configs():
     caches), a graph of
     launches cycling through them, HIP events around its second replay on
     the launch stream.  The fill ceiling is torch's fill of a buffer of the
-    workload's effective bytes under the same rotation.  Parity for every
-    workload is in the GPU tests, not here.
+    workload's effective bytes under the same rotation; the copy ceiling a
+    torch copy that moves the same total bytes, half read and half written.
+    Parity for every workload is in the GPU tests, not here.
     """
     import numpy as np
     import torch
@@ -198,13 +199,24 @@ def all_configs():
         fill_ms = graph_ms(torch, lambda k: bufs[k % fsets].fill_(7), steps, stream)
         del bufs
         torch.cuda.empty_cache()
+        # a plain copy that reads half the effective bytes and writes them:
+        # the same total traffic, half of it reads
+        half = max(1, eff // 2)
+        csets = min(64, max(1, math.ceil(2 * INFINITY_CACHE / eff)))
+        cbufs = [(torch.empty(half, dtype=torch.uint8, device=dev).fill_(1),
+                  torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(csets)]
+        copy_ms = graph_ms(torch, lambda k: cbufs[k % csets][1].copy_(cbufs[k % csets][0]), steps, stream)
+        del cbufs
+        torch.cuda.empty_cache()
         gbps = eff / (ms * 1e-3) / 1e9
         fill_gbps = eff / (fill_ms * 1e-3) / 1e9
+        copy_gbps = 2 * half / (copy_ms * 1e-3) / 1e9
         out.append({"workload": wl.name, "op": wl.op, "dtype": wl.dtype, "shape": [rows, cols], "vocab_size": V,
                     "rows_processed": R, "effective_bytes": eff, "buffer_sets": nsets, "launches": steps,
                     "us_per_launch": round(ms * 1e3, 3), "GBps": round(gbps, 1),
                     "frac_of_peak": round(gbps / PEAK_GBPS, 4), "fill_ceiling_GBps": round(fill_gbps, 1),
-                    "frac_of_fill_ceiling": round(gbps / fill_gbps, 4), "variant": "auto"})
+                    "frac_of_fill_ceiling": round(gbps / fill_gbps, 4), "copy_ceiling_GBps": round(copy_gbps, 1),
+                    "frac_of_copy_ceiling": round(gbps / copy_gbps, 4), "variant": "auto"})
         print(f"# {wl.name}: {ms * 1e3:.3f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
     print(json.dumps({"mode": "all_configs", "peak_GBps": PEAK_GBPS, "configs": out}), flush=True)
 
