@@ -85,13 +85,13 @@ struct F32Bits {
 struct BF16Bits {
   using Bits = uint16_t;
   static constexpr int kZeroLowBits = 16;
-  static constexpr uint32_t kKey16Lo = 0x0080u, kKey16Hi = 0xFF7Fu;  // order_key16 of -max, +max
+  static constexpr uint32_t kKey16Lo = 0x0080u, kKey16Hi = 0xFF7Fu;  // 16-bit order keys of -max, +max
   static __device__ __forceinline__ float value(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 };
 struct F16Bits {
   using Bits = uint16_t;
   static constexpr int kZeroLowBits = 13;
-  static constexpr uint32_t kKey16Lo = 0x0400u, kKey16Hi = 0xFBFFu;  // order_key16 of -max, +max
+  static constexpr uint32_t kKey16Lo = 0x0400u, kKey16Hi = 0xFBFFu;  // 16-bit order keys of -max, +max
   static __device__ __forceinline__ float value(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
 };
 
@@ -103,13 +103,9 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// The same order on the raw pattern of a 16-bit float (bf16, fp16), as a
-// 16-bit key; -0 takes the key of +0.  bits_of_key16 inverts it (giving +0
-// for the key of zero).
-__device__ __forceinline__ uint32_t order_key16(uint32_t h) {
-  h = h == 0x8000u ? 0u : h;
-  return (h & 0x8000u) ? (h ^ 0xFFFFu) : (h | 0x8000u);
-}
+// The raw 16-bit float (bf16, fp16) whose 16-bit order key is k: the
+// inverse of order_key16x2 below (a key with the top bit set is a value of
+// sign 0; otherwise the bits were inverted).
 __device__ __forceinline__ uint32_t bits_of_key16(uint32_t k) {
   return (k & 0x8000u) ? (k & 0x7FFFu) : (k ^ 0xFFFFu);
 }
@@ -428,8 +424,9 @@ constexpr bool kFineSearch = sizeof(typename D::Bits) == 2 && THREADS == 1024;
 
 // Two 16-bit order keys at once, from a word holding two raw 16-bit floats
 // (low token in the low half): a negative value's bits are inverted, a
-// positive one's sign bit set.  Unlike order_key16, -0 keeps a key of its
-// own, one below +0's (callers that need them equal handle it).
+// positive one's sign bit set, so unsigned key order is value order.  -0
+// keeps a key of its own, one below +0's (callers that need the two equal
+// handle it).
 __device__ __forceinline__ uint32_t order_key16x2(uint32_t two) {
   typedef short short2_t __attribute__((ext_vector_type(2)));
   const short2_t sign = __builtin_bit_cast(short2_t, two) >> static_cast<short>(15);  // per half: 0 or all ones
