@@ -16,7 +16,8 @@ the host's launch rate does not pace the GPU; HIP events on the launch
 stream bracket the replay.  The CPU baseline is the oracle's plain C loop
 on one host core over repeated passes of the same workload.
 
-Besides the headline, the one JSON line carries: a warm figure (one buffer
+Besides the headline, the one JSON line carries: the same steps' rate in
+HBM traffic (from the committed counter summary), a warm figure (one buffer
 set, cache-resident, not HBM), each kernel variant cold, fill and copy
 ceilings (one of them moving the apply's physical bytes), the gated apply
 with its report, one GPU's share under a vocabulary split, the host-memory
@@ -329,6 +330,7 @@ def main():
         extras["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl, eff, args.cpu_seconds / 2)
         extras["cpu_baseline_python_small"] = cpu_baseline_python()
 
+    traffic = counted_traffic()
     line = {
         "metric": METRIC,
         "value": round(gbps, 1),
@@ -359,10 +361,16 @@ def main():
             "peak": PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gbps / PEAK_GBPS, 4),
-            "traffic": counted_traffic(),
+            "traffic": traffic,
         },
         "cpu_baseline": cpu,
     }
+    if traffic is not None:
+        # the same steps counted in the bytes that cross the HBM interface
+        # (counters from the committed summary) rather than algorithmic bytes
+        phys = traffic / (ms_step * 1e-3) / 1e9
+        line["hbm_traffic_rate"] = {"bytes_per_step": traffic, "GBps": round(phys, 1),
+                                    "frac_of_peak": round(phys / PEAK_GBPS, 4)}
     line.update(extras)
     print(json.dumps(line), flush=True)
 
