@@ -19,7 +19,8 @@ on one host core over repeated passes of the same workload.
 Besides the headline, the one JSON line carries: the same steps' rate in
 HBM traffic (from the committed counter summary), a warm figure (one buffer
 set, cache-resident, not HBM), each kernel variant cold, fill and copy
-ceilings (one of them moving the apply's physical bytes), the gated apply
+ceilings (two of them moving the apply's physical bytes: a torch copy and
+this library's out-of-place apply with an all-allowed mask), the gated apply
 with its report, one GPU's share under a vocabulary split, the host-memory
 path, mask upload behind a forward pass, the fused sampler against a
 stock-torch sampler, and the oracle on all host cores and in pure Python.
@@ -319,6 +320,8 @@ def main():
             per[var] = {"ms_per_step": t, "GBps": eff / (t * 1e-3) / 1e9}
         extras["variants_cold"] = per
         extras["ceiling_cold"] = ceilings(torch, dev, eff, nsets, args.steps, stream, rmw_bytes=R * V * 2)
+        extras["ceiling_cold"]["own_copy_same_rows"] = own_copy(torch, dev, mb, R, wl.logits.shape[1],
+                                                                 wl.mask.shape[1], args.steps, stream)
         extras["gated_rows_cold"] = gated_rows(torch, dev, mb, workloads, args.steps, stream)
         extras["vocab_shard_tp8_cold"] = vocab_shard(torch, dev, mb, wl, args.steps, stream)
         extras["host_path"] = host_path(torch, mb, wl, eff)
@@ -417,6 +420,26 @@ def ceilings(torch, dev, eff, nsets, steps, stream, rmw_bytes=0):
         out[name] = {"bytes_per_step": nbytes, "ms_per_step": ms, "GBps": nbytes / (ms * 1e-3) / 1e9}
         del g
     return out
+
+
+def own_copy(torch, dev, mb, rows, cols, mask_cols, steps, stream):
+    """This library's out-of-place apply with an all-allowed mask over `rows` rows: a plain copy.
+
+    It reads and writes every logit of those rows (and reads their mask
+    words), the physical traffic of the in-place apply of a mask whose
+    lines all mix kept and masked tokens, with the same load, store and
+    launch machinery.  Cold rotation like the headline.
+    """
+    nbytes = 2 * rows * cols * 2 + rows * mask_cols * 4
+    nsets = max(2, math.ceil(2 * INFINITY_CACHE / nbytes))
+    sets = [(torch.empty(rows, cols, dtype=torch.bfloat16, device=dev).normal_(),
+             torch.full((rows, mask_cols), -1, dtype=torch.int32, device=dev),
+             torch.empty(rows, cols, dtype=torch.bfloat16, device=dev)) for _ in range(nsets)]
+    ms = graph_ms(torch, lambda k: mb.mi_apply_bitmask_out(sets[k % nsets][0], sets[k % nsets][1],
+                                                           sets[k % nsets][2]), steps, stream)
+    del sets
+    torch.cuda.empty_cache()
+    return {"bytes_per_step": nbytes, "ms_per_step": ms, "GBps": nbytes / (ms * 1e-3) / 1e9}
 
 
 def graph_ms(torch, fn, steps, stream, warmup=10):
