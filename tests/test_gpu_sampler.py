@@ -147,10 +147,8 @@ def test_per_row_parameters_verify_shape():
 def test_full_size_mixed_bf16_with_mask():
     wl = workloads.mixed_bf16()
     say("[gpu] sampler on the [256, 128256] bf16 shape, vocab 128000, masked")
-    check_rows(wl.logits, "bfloat16", wl.mask, 128000, 0.8, 0, 0.9, 0.0, seed=123, offset=1,
-               rows=list(range(0, 256, 8)))
-    check_rows(wl.logits, "bfloat16", wl.mask, 128000, 1.0, 50, 1.0, 0.0, seed=123, offset=2,
-               rows=list(range(3, 256, 16)))
+    check_rows(wl.logits, "bfloat16", wl.mask, 128000, 0.8, 0, 0.9, 0.0, seed=123, offset=1)   # every row
+    check_rows(wl.logits, "bfloat16", wl.mask, 128000, 1.0, 50, 1.0, 0.0, seed=123, offset=2)
 
 
 def test_large_vocab_fp32():
