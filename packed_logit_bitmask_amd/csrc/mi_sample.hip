@@ -89,8 +89,10 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     if (ar.min_p) ar.min_p += r0;
     const auto* lg = static_cast<const char*>(logits) + r0 * logits_row_stride * p.esize;
     const uint32_t* mk = m ? m + mr0 : nullptr;
-    // Histogram LDS only when some row may filter; deep load pipeline when a
-    // compute unit holds one row at a time (rows <= 256), shallow otherwise.
+    // Histogram LDS only when some row may filter; 1024-thread blocks when a
+    // compute unit holds one row at a time (rows <= 256), 256-thread blocks
+    // otherwise, 128 bytes in flight per thread either way (with 64 bytes
+    // the 256-thread blocks took B=1024 fp16 greedy 7 % longer).
     // Filtered 16-bit rows always take 1024-thread blocks: those search the
     // full 16-bit key histogram, which fills most of a compute unit's LDS
     // (the radix histograms of the fallback share its space).
@@ -106,13 +108,13 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
                                                                     ar, r0, tokens + r0)
     switch (dtype) {
       case MI_DTYPE_F32:
-        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 64, 256);
+        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 128, 256);
         break;
       case MI_DTYPE_F16:
-        if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::F16Bits, uint16_t, 64, 256);
+        if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256);
         break;
       default:
-        if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 64, 256);
+        if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256);
     }
 #undef MI_SAMPLE
   }

@@ -672,11 +672,10 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   return true;
 }
 
-// One block of THREADS threads per row.  1024 threads with 128 bytes of
-// logits in flight per thread when each compute unit holds one row at a
-// time; 256 threads with 64 bytes so several rows share a compute unit when
-// there are many rows.  The draw, whose per-group work is heavy, keeps half
-// as much in flight.
+// One block of THREADS threads per row, 128 bytes of logits in flight per
+// thread: 1024 threads when each compute unit holds one row at a time; 256
+// so several rows share a compute unit when there are many rows.  The draw,
+// whose per-group work is heavy, keeps half as much in flight.
 template <typename D, int BYTES, int THREADS>
 __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
                                                               const uint32_t* __restrict__ mask, int64_t ms,
