@@ -23,7 +23,8 @@ ceilings (two of them moving the apply's physical bytes: a torch copy and
 this library's out-of-place apply with an all-allowed mask), the gated apply
 with its report, one GPU's share under a vocabulary split, the host-memory
 path, mask upload behind a forward pass, the fused sampler against a
-stock-torch sampler, and the oracle on all host cores and in pure Python.
+stock-torch sampler and at small batches, and the oracle on all host cores
+and in pure Python.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto]
        python bench.py --all-configs       (every workload, next to a plain fill)
@@ -327,6 +328,7 @@ def main():
         extras["host_path"] = host_path(torch, mb, wl, eff)
         extras["mask_upload_overlap"] = upload_overlap(torch, dev, mb, wl)
         extras["fused_sampler_cold"] = sampler_times(torch, dev, mb, workloads, stream)
+        extras["fused_sampler_small_batch_cold"] = sampler_small_batch(torch, dev, mb, workloads, stream)
 
     cpu = cpu_baseline(wl, eff, args.cpu_seconds)
     if not args.no_extras:
@@ -612,6 +614,33 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
         out[label] = res
         del sets
         torch.cuda.empty_cache()
+    return out
+
+
+def sampler_small_batch(torch, dev, mb, workloads, stream, steps=200):
+    """Greedy and unfiltered draws on the first B rows of the B=256 bf16 sampler shape, B = 1, 16, 64.
+
+    With few rows and no filter the library splits each row over several
+    blocks; these are the batch sizes where that matters.  Cold rotation.
+    """
+    import numpy as np
+
+    wl = workloads.mixed_bf16(n_indices=0)
+    nsets = max(2, math.ceil(2 * INFINITY_CACHE / (wl.logits.nbytes + wl.mask.nbytes)))
+    sets = [(torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(torch.bfloat16), torch.from_numpy(wl.mask).to(dev))
+            for _ in range(nsets)]
+    out = {}
+    for B in (1, 16, 64):
+        tok = torch.empty(B, dtype=torch.int64, device=dev)
+        res = {}
+        for mode, kw in (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperature=1.0))):
+            ms = graph_ms(torch, lambda k, kw=kw: mb.mi_apply_bitmask_sample(
+                sets[k % nsets][0][:B], sets[k % nsets][1][:B], wl.vocab_size, seed=1, offset=k, out=tok, **kw),
+                steps, stream)
+            res[mode] = {"us_per_call": ms * 1e3}
+        out[f"B{B}_V128000_bf16"] = res
+    del sets
+    torch.cuda.empty_cache()
     return out
 
 

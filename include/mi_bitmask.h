@@ -199,7 +199,10 @@ mi_status_t mi_apply_bitmask_out_ex(
  * or mask).  Asynchronous on `stream` like the apply calls.  It uses no
  * device memory beyond its arguments: its working space is on chip (for
  * bf16 and fp16 rows with top-k or top-p, a 131 KB LDS histogram per
- * 1024-thread block, so one block per compute unit).
+ * 1024-thread block, so one block per compute unit).  With few rows and no
+ * top-k, top-p or min-p it splits each row over several blocks that merge
+ * their answers in `tokens` itself (three kernels on `stream`; `tokens`
+ * holds intermediate values until the last one has run).
  */
 typedef struct mi_sample_params {
     const float *temperature;     /* device [rows] or NULL */

@@ -17,6 +17,14 @@ namespace {
 
 constexpr int64_t kMaxSampleVocab = int64_t(1) << 28;
 
+// Segmented rows (no filter, no min-p): at most this many rows per launch
+// (fewer when every row is greedy), about this many blocks in all, and at
+// most this many segments per row (each posts one atomic to the row's word).
+constexpr int64_t kSplitRows = 128;
+constexpr int64_t kSplitRowsGreedy = 2;
+constexpr int64_t kSplitBlocks = 512;
+constexpr int64_t kMaxSegments = 32;
+
 // Checks for a call without a mask: every token below V takes part, and V
 // defaults to cols.
 mi_status_t check_logits_only(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t ls,
@@ -97,15 +105,29 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     // full 16-bit key histogram, which fills most of a compute unit's LDS
     // (the radix histograms of the fallback share its space).
     const bool may_filter = ar.top_k || ar.top_p || ar.top_k_all > 0 || ar.top_p_all < 1.0f;
+    const bool may_min_p = ar.min_p || ar.min_p_all > 0.f;
     const bool fine = may_filter && dtype != MI_DTYPE_F32;
-    const bool deep = n <= 256 || fine;
+    // Rows with neither a filter nor min-p need no whole-row state: with few
+    // rows they are split into segments, one 256-thread block each, so every
+    // compute unit has work (see sample_rows).
+    // A launch of greedy rows alone gains only at one or two rows: one block
+    // reads a row about as fast as a few blocks that then merge.
+    const bool greedy_only = !ar.temperature && !(ar.temperature_all > 0.f);
+    int32_t nseg = 1, seg_len = V;
+    if (!may_filter && !may_min_p && n <= (greedy_only ? kSplitRowsGreedy : kSplitRows) && V >= 8192) {
+      nseg = static_cast<int32_t>(std::min<int64_t>({(kSplitBlocks + n - 1) / n, kMaxSegments, (V + 4095) / 4096}));
+      seg_len = static_cast<int32_t>(((V + nseg - 1) / nseg + 255) / 256 * 256);
+      nseg = (V + seg_len - 1) / seg_len;
+    }
+    const bool deep = (n <= 256 || fine) && nseg == 1;
     const int threads = deep ? 1024 : 256;
     const size_t lds = fine ? std::max(mi::sample_fine_bytes(), mi::sample_hist_bytes(threads))
                             : (may_filter ? mi::sample_hist_bytes(threads) : 0);
+    if (nseg > 1) mi::clear_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
 #define MI_SAMPLE(TAG, BITS, BYTES, THREADS)                                                                   \
-  mi::sample_rows<TAG, BYTES, THREADS><<<n, THREADS, lds, stream>>>(reinterpret_cast<const BITS*>(lg),          \
-                                                                    logits_row_stride, mk, mask_row_stride, V,   \
-                                                                    ar, r0, tokens + r0)
+  mi::sample_rows<TAG, BYTES, THREADS><<<static_cast<uint32_t>(n) * nseg, THREADS, lds, stream>>>(              \
+      reinterpret_cast<const BITS*>(lg), logits_row_stride, mk, mask_row_stride, V, ar, r0, tokens + r0, nseg,     \
+      seg_len)
     switch (dtype) {
       case MI_DTYPE_F32:
         if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 128, 256);
@@ -117,6 +139,7 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
         if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256);
     }
 #undef MI_SAMPLE
+    if (nseg > 1) mi::finish_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
   }
   return after_launch("sample_rows");
 }

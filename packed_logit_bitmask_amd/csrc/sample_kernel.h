@@ -676,11 +676,20 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
 // thread: 1024 threads when each compute unit holds one row at a time; 256
 // so several rows share a compute unit when there are many rows.  The draw,
 // whose per-group work is heavy, keeps half as much in flight.
+//
+// With nseg > 1 (rows with neither top-k, top-p nor min-p), each row is
+// split into nseg segments of seg_len tokens (a multiple of 256), one block
+// each: a block finds its segment's greedy argmax or Gumbel-max and posts it
+// to out[r] as one 64-bit atomic maximum of (order key of the value or the
+// Gumbel key, inverted token index), so the largest wins and ties go to the
+// lowest index.  out must hold 0 beforehand (clear_tokens) and is turned
+// into token numbers afterwards (finish_tokens).
 template <typename D, int BYTES, int THREADS>
 __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
                                                               const uint32_t* __restrict__ mask, int64_t ms,
                                                               int32_t V, SampleArgs a, int64_t row_base,
-                                                              int64_t* __restrict__ out) {
+                                                              int64_t* __restrict__ out, int32_t nseg,
+                                                              int32_t seg_len) {
   constexpr int kWaves = THREADS / 64;
   __shared__ float s_best[kWaves];
   __shared__ int32_t s_besti[kWaves];
@@ -691,11 +700,20 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   auto hist_m = reinterpret_cast<unsigned long long(*)[256]>(s_dyn);
   auto hist_n = reinterpret_cast<uint32_t(*)[256]>(s_dyn + kWaves * 256);
 
-  const int64_t r = blockIdx.x;
+  const int64_t r = nseg > 1 ? blockIdx.x / nseg : blockIdx.x;
+  const int32_t tok0 = nseg > 1 ? static_cast<int32_t>(blockIdx.x % nseg) * seg_len : 0;  // segment start
+  const bool split = nseg > 1;
   const int t = static_cast<int>(threadIdx.x);
   const int wave = t >> 6;
-  const typename D::Bits* row = logits + r * ls;
-  const RowView<D> rv(row, mask ? mask + r * ms : nullptr, V);
+  const typename D::Bits* row = logits + r * ls + tok0;
+  const RowView<D> rv(row, mask ? mask + r * ms + tok0 / 32 : nullptr, split ? min(seg_len, V - tok0) : V);
+  // one block's answer for row r: its own token (or -1), or a share of the
+  // row's atomic maximum when the row is split
+  const auto post = [&](uint32_t key, int32_t i) {
+    const unsigned long long packed = (static_cast<unsigned long long>(key) << 32) |
+                                      static_cast<uint32_t>(~static_cast<uint32_t>(tok0 + i));
+    atomicMax(reinterpret_cast<unsigned long long*>(out) + r, packed);
+  };
 
   const float temp = a.temperature ? a.temperature[r] : a.temperature_all;
   const int32_t top_k = a.top_k ? a.top_k[r] : a.top_k_all;
@@ -832,7 +850,10 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     // candidates are finite, so the max is -inf only when there is none
     const bool none = best == -__builtin_inff();
     if (none || !(temp > 0.f)) {  // no candidate, or greedy
-      if (t == 0) out[r] = none ? -1 : besti;
+      if (t == 0) {
+        if (!split) out[r] = none ? -1 : besti;
+        else if (!none) post(order_key(best), besti);
+      }
       return;
     }
   }
@@ -852,8 +873,9 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     return fmaxf(x * inv_t - __log2f(e) * 0.6931471805599453f, -__FLT_MAX__);
   };
   const auto gumbel_group = [&](int32_t i0, const float* x, uint32_t kept, auto&& sink) {
-    uint32_t c0[4] = {static_cast<uint32_t>(i0 >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo, a.offset_hi};
-    uint32_t c1[4] = {static_cast<uint32_t>(i0 >> 2) + 1u, static_cast<uint32_t>(row_base + r), a.offset_lo,
+    uint32_t c0[4] = {static_cast<uint32_t>((tok0 + i0) >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo,
+                      a.offset_hi};
+    uint32_t c1[4] = {static_cast<uint32_t>((tok0 + i0) >> 2) + 1u, static_cast<uint32_t>(row_base + r), a.offset_lo,
                       a.offset_hi};
     if (kept & 0x0Fu) philox4x32_10(c0, a.seed_lo, a.seed_hi);
     if (kept & 0xF0u) philox4x32_10(c1, a.seed_lo, a.seed_hi);
@@ -1138,10 +1160,11 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
             for (int u = 0; u < 4; ++u) {
               if (idx[u] < 0) continue;
               const int32_t i = idx[u];
-              uint32_t c4[4] = {static_cast<uint32_t>(i >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo,
+              uint32_t c4[4] = {static_cast<uint32_t>((tok0 + i) >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo,
                                 a.offset_hi};
               philox4x32_10(c4, a.seed_lo, a.seed_hi);
-              const uint32_t word = (i & 3) == 0 ? c4[0] : (i & 3) == 1 ? c4[1] : (i & 3) == 2 ? c4[2] : c4[3];
+              const int32_t w4 = (tok0 + i) & 3;
+              const uint32_t word = w4 == 0 ? c4[0] : w4 == 1 ? c4[1] : w4 == 2 ? c4[2] : c4[3];
               offer(gumbel_key(D::value(static_cast<typename D::Bits>(h[u])), word), i);
             }
           }
@@ -1213,7 +1236,26 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       }
     // every kept token has a key above -inf, and a row with a candidate
     // keeps at least its largest logit: bi is unset only without candidates
-    out[r] = bi == 0x7FFFFFFF ? -1 : bi;
+    if (!split) out[r] = bi == 0x7FFFFFFF ? -1 : bi;
+    else if (bi != 0x7FFFFFFF) post(order_key(bk), bi);
+  }
+}
+
+// Before a split launch: every row's answer word at 0, below any posted
+// (key, index) pair (keys of finite values and of clamped Gumbel keys are at
+// least 0x00800000).  A kernel rather than a memset, so graphs replay it.
+__global__ void clear_tokens(int64_t* __restrict__ out, int64_t rows) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r < rows) out[r] = 0;
+}
+
+// After a split launch: the token number from each row's maximum, -1 where
+// no segment posted one.
+__global__ void finish_tokens(int64_t* __restrict__ out, int64_t rows) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r < rows) {
+    const unsigned long long packed = static_cast<unsigned long long>(out[r]);
+    out[r] = packed ? static_cast<int64_t>(~static_cast<uint32_t>(packed)) : -1;
   }
 }
 

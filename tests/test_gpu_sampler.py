@@ -406,6 +406,76 @@ def test_kept_tokens_crowding_one_wave(dtype):
     check_rows(bits, dtype, None, None, 1.0, 6000, 1.0, 0.0, seed=42, offset=1, min_exact=0.75)
 
 
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_segmented_rows_ties_and_sparse_candidates(dtype):
+    """Few rows without filters are split into segments whose answers merge
+    through one atomic maximum per row: equal maxima in several segments go
+    to the lowest index, a row whose only candidates sit in one segment
+    still finds them, and a row with none gets -1."""
+    rng = np.random.default_rng(43)
+    R, cols = 6, 70001
+    x = rng.standard_normal((R, cols)).astype(np.float32)
+    x[0, [100, 5000, 40000, 69999]] = 9.0          # equal maxima in four segments
+    x[1, [69999, 3]] = 9.0
+    allowed = np.ones((R, cols), bool)
+    allowed[2] = False
+    allowed[2, 50000:50010] = True                 # candidates in one segment only
+    allowed[3] = False                             # none at all
+    allowed[4, ::2] = False
+    if dtype == "float32":
+        bits = x.view(np.uint32)
+    elif dtype == "float16":
+        bits = x.astype(np.float16).view(np.uint16)
+    else:
+        b = x.view(np.uint32)
+        bits = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    say(f"[gpu] sampler segmented rows {dtype}")
+    # greedy through a per-row temperature array (all zero): a launch of scalar
+    # greedy rows is split only at one or two rows, an array makes it split here
+    tok = check_rows(bits, dtype, mask, None, np.zeros(R, np.float32), 0, 1.0, 0.0, seed=1, offset=0,
+                     min_exact=1.0)
+    assert tok[0] == 100 and tok[1] == 3 and 50000 <= tok[2] < 50010 and tok[3] == -1
+    one = check_rows(bits[:1], dtype, mask[:1], None, 0.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
+    assert one[0] == 100
+    tok = check_rows(bits, dtype, mask, None, 1.3, 0, 1.0, 0.0, seed=2, offset=5)
+    assert tok[3] == -1 and 50000 <= tok[2] < 50010
+
+
+def test_segmented_rows_in_a_graph():
+    """The segmented launch (clear, sample, finish: three kernels, no memset)
+    captured in a HIP graph replays to the eager tokens, several times, with
+    other work between replays."""
+    rng = np.random.default_rng(47)
+    R, cols = 8, 40000
+    bits = random_logits(rng, "bfloat16", R, cols)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.4, (cols + 31) // 32, rng)
+    dl = dev_logits(bits, "bfloat16")
+    dm = torch.from_numpy(mask).to("cuda")
+    temp = torch.from_numpy(rng.choice([0.0, 0.8, 1.2], R).astype(np.float32)).to("cuda")
+    want = [mb.mi_apply_bitmask_sample(dl, dm, None, temperature=temp, seed=3, offset=k).cpu() for k in range(3)]
+    say("[gpu] sampler segmented rows in a graph")
+    outs = [torch.empty(R, dtype=torch.int64, device="cuda") for _ in range(3)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for k in range(3):
+                mb.mi_apply_bitmask_sample(dl, dm, None, temperature=temp, seed=3, offset=k, out=outs[k])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(3):
+            assert torch.equal(outs[k].cpu(), want[k]), (rep, k)
+        (dl.float() * 2).sum().item()
+    del g
+    check_rows(bits, "bfloat16", mask, None, temp.cpu().numpy(), 0, 1.0, 0.0, seed=3, offset=0)
+
+
 def test_rows_split_over_launches():
     """More than 2^20 rows go out in several launches: the generator's row
     counter and the per-row parameter arrays continue across the split."""
