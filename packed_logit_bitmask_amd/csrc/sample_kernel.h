@@ -11,8 +11,10 @@
 // finite -- so a masked token is never drawn.  The logits are only read.
 //
 // One block per row (1024 threads when each compute unit holds one row, or
-// when 16-bit rows may filter; 256 when many rows share a unit).  Each pass
-// walks the row in groups of 8
+// when 16-bit rows may filter; 256 when many rows share a unit), or, for a
+// few rows without top-k, top-p or min-p, one 256-thread block per segment
+// of a row, the segments merging by an atomic maximum.  Each pass walks the
+// row in groups of 8
 // consecutive tokens per thread through raw buffer loads (16-byte vectors
 // when the row start is aligned), several groups in flight per thread; trip
 // counts are uniform across the block.
