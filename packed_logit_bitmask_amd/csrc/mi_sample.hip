@@ -25,6 +25,12 @@ constexpr int64_t kSplitRowsGreedy = 2;
 constexpr int64_t kSplitBlocks = 512;
 constexpr int64_t kMaxSegments = 32;
 
+// Filtered 16-bit rows: more rows than this (the compute units) take the
+// 8-bit-counter histogram in 512-thread blocks, two per unit, when a row has
+// at most kFine8Vocab tokens.
+constexpr int64_t kFine16Rows = 256;
+constexpr int64_t kFine8Vocab = 65536;
+
 // Checks for a call without a mask: every token below V takes part, and V
 // defaults to cols.
 mi_status_t check_logits_only(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t ls,
@@ -101,9 +107,13 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     // compute unit holds one row at a time (rows <= 256), 256-thread blocks
     // otherwise, 128 bytes in flight per thread either way (with 64 bytes
     // the 256-thread blocks took B=1024 fp16 greedy 7 % longer).
-    // Filtered 16-bit rows always take 1024-thread blocks: those search the
-    // full 16-bit key histogram, which fills most of a compute unit's LDS
-    // (the radix histograms of the fallback share its space).
+    // Filtered 16-bit rows search the full 16-bit key histogram: in
+    // 1024-thread blocks with 16-bit counters (128 KB, most of a compute
+    // unit's LDS) when there are at most as many rows as compute units, else
+    // in 512-thread blocks with 8-bit counters (64 KB), two to a unit, for
+    // rows of at most 65536 tokens (longer rows would more often hold 256
+    // equal logits, which sends a row to the radix search).  The radix
+    // histograms of that fallback share the space.
     const bool may_filter = ar.top_k || ar.top_p || ar.top_k_all > 0 || ar.top_p_all < 1.0f;
     const bool may_min_p = ar.min_p || ar.min_p_all > 0.f;
     const bool fine = may_filter && dtype != MI_DTYPE_F32;
@@ -119,9 +129,10 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
       seg_len = static_cast<int32_t>(((V + nseg - 1) / nseg + 255) / 256 * 256);
       nseg = (V + seg_len - 1) / seg_len;
     }
+    const bool fine8 = fine && n > kFine16Rows && V <= kFine8Vocab;
     const bool deep = (n <= 256 || fine) && nseg == 1;
-    const int threads = deep ? 1024 : 256;
-    const size_t lds = fine ? std::max(mi::sample_fine_bytes(), mi::sample_hist_bytes(threads))
+    const int threads = fine8 ? 512 : deep ? 1024 : 256;
+    const size_t lds = fine ? std::max(mi::sample_fine_bytes(threads), mi::sample_hist_bytes(threads))
                             : (may_filter ? mi::sample_hist_bytes(threads) : 0);
     if (nseg > 1) mi::clear_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
 #define MI_SAMPLE(TAG, BITS, BYTES, THREADS)                                                                   \
@@ -133,10 +144,14 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
         if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 128, 256);
         break;
       case MI_DTYPE_F16:
-        if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256);
+        if (fine8) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512);
+        else if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024);
+        else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256);
         break;
       default:
-        if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024); else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256);
+        if (fine8) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512);
+        else if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024);
+        else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256);
     }
 #undef MI_SAMPLE
     if (nseg > 1) mi::finish_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);

@@ -10,23 +10,24 @@
 // "apply_packed_bitmask"), it lies below the vocab size and its logit is
 // finite -- so a masked token is never drawn.  The logits are only read.
 //
-// One block per row (1024 threads when each compute unit holds one row, or
-// when 16-bit rows may filter; 256 when many rows share a unit), or, for a
-// few rows without top-k, top-p or min-p, one 256-thread block per segment
-// of a row, the segments merging by an atomic maximum.  Each pass walks the
-// row in groups of 8
-// consecutive tokens per thread through raw buffer loads (16-byte vectors
-// when the row start is aligned), several groups in flight per thread; trip
-// counts are uniform across the block.
+// One block per row (1024 threads when each compute unit holds one row;
+// 256 when many rows share a unit, or 512 for filtered 16-bit rows, two to a
+// unit), or, for a few rows without top-k, top-p or min-p, one 256-thread
+// block per segment of a row, the segments merging by an atomic maximum.
+// Each pass walks the row in groups of 8 consecutive tokens per thread
+// through raw buffer loads (16-byte vectors when the row start is aligned),
+// several groups in flight per thread; trip counts are uniform across the
+// block.
 //
 //   pass 1   max logit over the candidates and its (lowest) index -> greedy
 //            rows and rows with no candidate end here; skipped when the row
 //            uses neither top-p nor min-p (nothing else needs it);
-//   16-bit   bf16 and fp16 rows with top-k or top-p, in 1024-thread blocks:
-//            one pass counts the tokens the mask allows under each of the
-//            65536 16-bit keys (LDS); the maximum and both cuts follow from
-//            the counts (fine_search).  The radix passes below remain for
-//            fp32 and for a row where one key holds 65536 tokens or more;
+//   16-bit   bf16 and fp16 rows with top-k or top-p, in 1024- or 512-thread
+//            blocks: one pass counts the tokens the mask allows under each
+//            of the 65536 16-bit keys (LDS, 16- or 8-bit counters); the
+//            maximum and both cuts follow from the counts (fine_search).
+//            The radix passes below remain for fp32 and for a row where one
+//            key holds more tokens than its counter can (65536 or 256);
 //   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
@@ -413,16 +414,23 @@ constexpr size_t sample_hist_bytes(int threads) {
   return static_cast<size_t>(threads / 64) * 256 * (sizeof(uint32_t) + sizeof(unsigned long long));
 }
 
-// The full-resolution histogram of a 16-bit type's keys: 65536 counts of 16
-// bits, two per word, plus one spare word per lane that non-candidates add
-// to (so the add needs no branch and spreads over the banks).
-constexpr int kFineWords = 32768;
-constexpr size_t sample_fine_bytes() { return static_cast<size_t>(kFineWords + 64) * sizeof(uint32_t); }
+// The full-resolution histogram of a 16-bit type's keys: 65536 counters,
+// several to a word, plus one spare word per lane that non-candidates add to
+// (so the add needs no branch and spreads over the banks).  1024-thread
+// blocks (one per compute unit) count in 16 bits, two per word (128 KB);
+// 512-thread blocks, for batches with more rows than compute units, count
+// in 8 bits, four per word (64 KB), so two blocks share a unit and one's
+// passes overlap the other's searches.  Either way a thread owns 32 words.
+template <int THREADS>
+constexpr int kFineBits = THREADS == 1024 ? 16 : 8;
+constexpr int fine_words(int threads) { return 65536 / (32 / (threads == 1024 ? 16 : 8)); }
+constexpr size_t sample_fine_bytes(int threads) {
+  return static_cast<size_t>(fine_words(threads) + 64) * sizeof(uint32_t);
+}
 
-// Whether a block shape searches 16-bit keys through the full histogram
-// (it needs most of a compute unit's LDS, so one 1024-thread block per unit).
+// Whether a block shape searches 16-bit keys through the full histogram.
 template <typename D, int THREADS>
-constexpr bool kFineSearch = sizeof(typename D::Bits) == 2 && THREADS == 1024;
+constexpr bool kFineSearch = sizeof(typename D::Bits) == 2 && (THREADS == 1024 || THREADS == 512);
 
 // Two 16-bit order keys at once, from a word holding two raw 16-bit floats
 // (low token in the low half): a negative value's bits are inverted, a
@@ -445,16 +453,16 @@ __device__ __forceinline__ uint32_t order_key16x2(uint32_t two) {
 // [D::kKey16Lo, D::kKey16Hi], and only those count as candidates.  -0 and +0
 // have adjacent keys: a cut on either is the value zero, which keeps both.
 // The largest candidate (*best; -inf when the row has none) is the highest
-// finite key with a count.  The counts are 16 bits wide, so a key holding
-// 65536 tokens or more would wrap: the counts then fall short of the tokens
-// counted, and the function returns false for the radix search to take
-// over (no thread reads `fine` after the barrier that decides it).  On
-// success *cut is the order key (of the widened value) at and above which
-// tokens are kept, 0 to keep every candidate; *cut16 the same cut as a
-// 16-bit key (0 to keep all), and *kept the number of candidates it keeps.
-// A row of at most 4 groups per thread comes already loaded in pre[4] (group
-// j * THREADS + t in pre[j], with `preloaded` set); otherwise the pass reads
-// the row.
+// finite key with a count.  A counter is 16 or 8 bits wide (kFineBits), so a
+// key holding 65536 (or 256) tokens or more would wrap into its neighbour:
+// the counts then fall short of the tokens counted, and the function returns
+// false for the radix search to take over (no thread reads `fine` after the
+// barrier that decides it).  On success *cut is the order key (of the
+// widened value) at and above which tokens are kept, 0 to keep every
+// candidate; *cut16 the same cut as a 16-bit key (0 to keep all), and *kept
+// the number of candidates it keeps.  A row of at most 4 groups per thread
+// comes already loaded in pre[4] (group j * THREADS + t in pre[j], with
+// `preloaded` set); otherwise the pass reads the row.
 template <typename D, int BYTES, int THREADS>
 __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine, float inv_t, bool use_k,
                                             int32_t top_k, bool use_p, float top_p, float* best, uint32_t* cut,
@@ -462,29 +470,47 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
                                             const typename RowView<D>::Raw (&pre)[4], bool preloaded) {
   using Bits = typename D::Bits;
   constexpr int kWaves = THREADS / 64;
+  constexpr int CB = kFineBits<THREADS>;        // bits per counter
+  constexpr uint32_t KW = 32 / CB;              // keys per word
+  constexpr uint32_t kWords = 65536 / KW;
+  constexpr uint32_t KPT = 65536 / THREADS;     // keys per thread: 64 or 128
+  static_assert(KPT / KW == 32, "a thread owns 32 words of the histogram");
+  constexpr uint32_t KPL = KPT / 64;            // keys per lane in the final search
+  constexpr uint32_t kCount = (1u << CB) - 1u;  // one counter's bits
   constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
   __shared__ uint32_t s_n[kWaves], s_kmax[kWaves], s_all[kWaves], s_c[kWaves], s_cut[2], s_cross[2];
   __shared__ uint32_t s_above_n[2], s_kept[2];
   __shared__ unsigned long long s_m[kWaves], s_above[2];
   const int t = static_cast<int>(threadIdx.x);
   const int lane = lane_id(), wave = t >> 6;
+  // the count of key k, from the word that holds it
+  const auto count_in = [](uint32_t w, uint32_t k) { return (w >> ((k % KW) * CB)) & kCount; };
+  // every count of a word, summed
+  const auto word_sum = [](uint32_t w) {
+    if constexpr (CB == 16) {
+      return (w & 0xFFFFu) + (w >> 16);
+    } else {
+      const uint32_t s2 = (w & 0x00FF00FFu) + ((w >> 8) & 0x00FF00FFu);
+      return (s2 & 0xFFFFu) + (s2 >> 16);
+    }
+  };
 
   uint4* f4 = reinterpret_cast<uint4*>(fine);
-  for (int i = t; i < (kFineWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = t; i < static_cast<int>(kWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
   if (t < 2) {
     s_cut[t] = 0u;
     s_cross[t] = ~0u;  // no crossing: keep every candidate
   }
   __syncthreads();
 
-  // ---- the pass: the 16-bit count of key k is half k & 1 of word k / 2; a
-  // token the mask rules out adds to this lane's spare word instead, so the
-  // add needs no branch and spreads over the banks
+  // ---- the pass: key k counts in word k / KW; a token the mask rules out
+  // adds to this lane's spare word instead, so the add needs no branch and
+  // spreads over the banks
   uint32_t allowed = 0;  // tokens the mask allows below V
-  const uint32_t spare = 2u * (kFineWords + static_cast<uint32_t>(lane));
+  const uint32_t spare = KW * (kWords + static_cast<uint32_t>(lane));
   const auto add = [&](uint32_t k, uint32_t bit) {
     const uint32_t kk = bit ? k : spare;
-    atomicAdd(&fine[kk >> 1], 1u << ((kk & 1u) << 4));
+    atomicAdd(&fine[kk / KW], 1u << ((kk % KW) * CB));
   };
   const auto group = [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
     const uint32_t bits = rv.mask_bits(raw, g, full);
@@ -515,42 +541,42 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   }
   __syncthreads();
 
-  // ---- sums: thread t holds keys [64t, 64t + 64) (words [32t, 32t + 32),
-  // read in a rotated order so a wave's lanes hit different banks).  Only
+  // ---- sums: thread t holds keys [KPT t, KPT t + KPT), words [32t, 32t + 32),
+  // read in a rotated order so a wave's lanes hit different banks.  Only
   // the threads at the two ends of the key range hold keys of non-finite
   // values; the others count every key.
-  const uint32_t k0 = 64u * static_cast<uint32_t>(t);
+  const uint32_t k0 = KPT * static_cast<uint32_t>(t);
   const auto in_range = [](uint32_t k) { return k - D::kKey16Lo <= kSpan; };
-  const bool inside = in_range(k0) && in_range(k0 + 63);
+  const bool inside = in_range(k0) && in_range(k0 + KPT - 1);
   uint32_t c = 0, all = 0, ktop = 0;  // candidates, every count, highest candidate key + 1
   uint32_t nz = 0;                    // bit j: word 32t + j counts a candidate
   if (inside) {
     for (int j = 0; j < 32; ++j) {
       const int jj = (j + t) & 31;
       const uint32_t w = fine[32 * t + jj];
-      all += (w & 0xFFFFu) + (w >> 16);
+      all += word_sum(w);
       nz |= (w ? 1u : 0u) << jj;
     }
     c = all;
     if (nz) {
       const int jt = 31 - __builtin_clz(nz);
-      ktop = k0 + 2 * jt + ((fine[32 * t + jt] >> 16) ? 2 : 1);
+      const uint32_t w = fine[32 * t + jt];
+      ktop = k0 + KW * jt + static_cast<uint32_t>(31 - __builtin_clz(w)) / CB + 1u;
     }
   } else {
     for (int j = 0; j < 32; ++j) {
       const int jj = (j + t) & 31;
       const uint32_t w = fine[32 * t + jj];
-      const uint32_t ka = k0 + 2 * jj, lo = w & 0xFFFFu, hi = w >> 16;
-      all += lo + hi;
-      if (in_range(ka) && lo) {
-        c += lo;
-        ktop = max(ktop, ka + 1);
-        nz |= 1u << jj;
-      }
-      if (in_range(ka + 1) && hi) {
-        c += hi;
-        ktop = max(ktop, ka + 2);
-        nz |= 1u << jj;
+      const uint32_t ka = k0 + KW * jj;
+#pragma unroll
+      for (uint32_t e = 0; e < KW; ++e) {
+        const uint32_t n = count_in(w, e);
+        all += n;
+        if (in_range(ka + e) && n) {
+          c += n;
+          ktop = max(ktop, ka + e + 1);
+          nz |= 1u << jj;
+        }
       }
     }
   }
@@ -604,9 +630,12 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
       for (int u = 0; u < 8; ++u) w[u] = fine[32 * t + ((j0 + u + t) & 31)];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const uint32_t ka = k0 + 2 * static_cast<uint32_t>((j0 + u + t) & 31);
-        if ((w[u] & 0xFFFFu) && in_range(ka)) m += static_cast<unsigned long long>(w[u] & 0xFFFFu) * mass(ka);
-        if ((w[u] >> 16) && in_range(ka + 1)) m += static_cast<unsigned long long>(w[u] >> 16) * mass(ka + 1);
+        const uint32_t ka = k0 + KW * static_cast<uint32_t>((j0 + u + t) & 31);
+#pragma unroll
+        for (uint32_t e = 0; e < KW; ++e) {
+          const uint32_t n = count_in(w[u], e);
+          if (n && in_range(ka + e)) m += static_cast<unsigned long long>(n) * mass(ka + e);
+        }
       }
     }
     sm = m;
@@ -623,10 +652,10 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
     }
   }
 
-  // ---- each search: the thread whose 64 keys hold the crossing posts its
+  // ---- each search: the thread whose keys hold the crossing posts its
   // number and the total above them; then one wave per search takes those
-  // keys, one per lane, and a suffix scan finds the largest key whose
-  // suffix reaches the need (top-k on wave 0, top-p on wave 1)
+  // keys, KPL consecutive ones per lane, and a suffix scan finds the largest
+  // key whose suffix reaches the need (top-k on wave 0, top-p on wave 1)
   const uint32_t need_k = static_cast<uint32_t>(top_k);  // more than the candidates: keep all
   const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(tot_m);
   const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
@@ -645,10 +674,20 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   __syncthreads();
   const int which = wave;  // 0: top-k, 1: top-p
   if (which < 2 && (which == 0 ? use_k : use_p) && s_cross[which] != ~0u) {
-    const uint32_t kx = 64u * s_cross[which] + static_cast<uint32_t>(lane);
-    const uint32_t n = in_range(kx) ? (fine[kx >> 1] >> ((kx & 1u) << 4)) & 0xFFFFu : 0u;
-    unsigned long long v = which == 0 ? n : (n ? static_cast<unsigned long long>(n) * mass(kx) : 0ull);
-    uint32_t vn = n;  // and the candidates at and above kx
+    const unsigned long long need = which == 0 ? static_cast<unsigned long long>(need_k) : need_p;
+    const uint32_t kb = KPT * s_cross[which] + KPL * static_cast<uint32_t>(lane);  // this lane's first key
+    uint32_t n[KPL];
+    unsigned long long vv[KPL];
+    unsigned long long v = 0;
+    uint32_t vn = 0;  // and the candidates at and above kb
+#pragma unroll
+    for (uint32_t j = 0; j < KPL; ++j) {
+      const uint32_t kx = kb + j;
+      n[j] = in_range(kx) ? count_in(fine[kx / KW], kx) : 0u;
+      vv[j] = which == 0 ? n[j] : (n[j] ? static_cast<unsigned long long>(n[j]) * mass(kx) : 0ull);
+      v += vv[j];
+      vn += n[j];
+    }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const unsigned long long u = __shfl_down(v, o);
@@ -658,12 +697,27 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
         vn += un;
       }
     }
-    const unsigned long long total = v + s_above[which];  // the searched total at and above kx
-    const uint64_t hit = __ballot(total >= (which == 0 ? static_cast<unsigned long long>(need_k) : need_p));
+    const unsigned long long total = v + s_above[which];  // the searched total at and above kb
+    const uint64_t hit = __ballot(total >= need);
     const int L = 63 - __clzll(static_cast<long long>(hit));
-    const uint32_t at_cut = static_cast<uint32_t>(__shfl(static_cast<int>(vn), L)) + s_above_n[which];
+    // within lane L: the largest of its keys whose suffix still reaches the need
+    uint32_t jsel = 0, nsel = vn;
+    unsigned long long acc = total;
+    uint32_t accn = vn;
+#pragma unroll
+    for (uint32_t j = 1; j < KPL; ++j) {
+      acc -= vv[j - 1];
+      accn -= n[j - 1];
+      if (acc >= need) {
+        jsel = j;
+        nsel = accn;
+      }
+    }
+    const uint32_t key = KPT * s_cross[which] + KPL * static_cast<uint32_t>(L) +
+                         static_cast<uint32_t>(__shfl(static_cast<int>(jsel), L));
+    const uint32_t at_cut = static_cast<uint32_t>(__shfl(static_cast<int>(nsel), L)) + s_above_n[which];
     if (lane == 0) {
-      s_cut[which] = 64u * s_cross[which] + static_cast<uint32_t>(L);  // a key: 0 (non-finite) keeps all
+      s_cut[which] = key;  // a key: 0 (non-finite) keeps all
       s_kept[which] = at_cut;
     }
   }
@@ -1060,7 +1114,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     }
   }
   // ---- draw after the 16-bit search
-  constexpr uint32_t kListPerWave = static_cast<uint32_t>(kFineWords) / (THREADS / 64);
+  constexpr uint32_t kFineWordsHere = static_cast<uint32_t>(fine_words(THREADS));
+  constexpr uint32_t kListPerWave = kFineWordsHere / (THREADS / 64);
   bool drawn = false;
   if constexpr (kFineSearch<D, THREADS>) {
     if (have_cut) {
@@ -1116,17 +1171,19 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           f(i0, raw, bits);
         }
       };
-      if (n_kept >= 256u && n_kept <= static_cast<uint32_t>(rv.V) / 6u &&
-          n_kept <= static_cast<uint32_t>(kFineWords) - 4096u) {
-        // Many kept tokens (the search counted them): list them first (LDS,
-        // where the histogram was, one region per wave), then run the
-        // generator on the list alone, every lane busy; a walk would run it
-        // for every group in which any lane of the wave keeps a token.
-        // With fewer than 256, most waves keep none, and the walk skips
-        // those.  The list pays one generator call per kept token, the walk
-        // one per 4 tokens of every group it runs it for, so the list is
-        // taken for at most V / 6 kept tokens; and at most 28672, which
-        // leaves each wave's region room for its share plus 256.
+      if ((n_kept >= 256u || rv.V <= 64 * THREADS) && n_kept >= 1u && n_kept <= static_cast<uint32_t>(rv.V) / 6u &&
+          n_kept <= kFineWordsHere - 4096u) {
+        // Many kept tokens (the search counted them): list them first (LDS, where
+        // the histogram was, one region per wave), then run the generator on the
+        // list alone, every lane busy; a walk would run it for every group in
+        // which any lane of the wave keeps a token.  With fewer than 256 on a long
+        // row, most of a wave's groups keep none, and the walk skips those; on a
+        // row of at most 8 groups per thread most of them keep one somewhere in
+        // the wave, and the list still pays.  The list pays one generator call per
+        // kept token, the walk one per 4 tokens of every group it runs it for, so
+        // the list is taken for at most V / 6 kept tokens; and at most 4096 fewer
+        // than the histogram's words (28672 or 12288), which leaves each wave's
+        // region room for its share plus 256 (or 512).
         uint32_t* list = reinterpret_cast<uint32_t*>(s_dyn) + wave * kListPerWave;
         uint32_t nw = 0;  // the same in every lane of the wave
         walk16([&](int32_t i0, const typename RowView<D>::Raw& raw, uint32_t bits) {

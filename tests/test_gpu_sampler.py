@@ -308,9 +308,9 @@ def test_graph_replay_matches_eager():
 @pytest.mark.parametrize("dtype,filters", [("float32", True), ("bfloat16", True), ("float16", False)])
 def test_many_rows_variant(dtype, filters):
     """More than 256 rows: fp32 rows, and 16-bit rows without top-k or top-p,
-    take the 256-thread variant; 16-bit rows that may filter keep 1024-thread
-    blocks (the full key histogram).  Per-row parameters, a ragged vocab tail
-    and a few rows with nothing allowed."""
+    take the 256-thread variant; 16-bit rows that may filter take 512-thread
+    blocks with the 8-bit-counter key histogram.  Per-row parameters, a ragged
+    vocab tail and a few rows with nothing allowed."""
     rng = np.random.default_rng(11)
     R, cols, V = 300, 2051, 2045
     bits = random_logits(rng, dtype, R, cols)
@@ -343,6 +343,75 @@ def test_key_holding_65536_tokens(dtype):
     say(f"[gpu] sampler keys holding 65536 tokens {dtype}")
     for (T, k, p, seed) in ((1.0, 10, 1.0, 1), (1.0, 2000, 1.0, 2), (0.9, 0, 0.6, 3), (1.0, 50, 0.9, 4)):
         check_rows(bits, dtype, None, None, T, k, p, 0.0, seed=seed, offset=0, min_exact=0.75)
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_many_rows_keys_holding_256_tokens(dtype):
+    """With more rows than compute units, filtered 16-bit rows count their
+    keys in 8 bits; a key holding 256 or more candidates would wrap, and the
+    row then takes the radix search.  300 rows, five of them with 255 (no
+    wrap), 256, 257, 1000 and 3000 copies of one value among random logits,
+    under top-k (a cut above the copies, and one that keeps them), top-p and
+    all three filters, with a mask on every row."""
+    rng = np.random.default_rng(43)
+    R, cols = 300, 4099
+    bits = random_logits(rng, dtype, R, cols)
+    one = {"float16": 0x3400, "bfloat16": 0x3E80}[dtype]          # 0.25
+    bits[bits == one] = one + 1                                   # only the planted copies hold 0.25
+    for r, copies in enumerate((255, 256, 257, 1000, 3000)):
+        bits[r, rng.choice(cols, copies, replace=False)] = one
+    allowed = rng.random((R, cols)) < 0.9
+    for r, copies in enumerate((255, 256, 257, 1000, 3000)):
+        allowed[r, bits[r] == one] = True                         # every copy is a candidate
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    say(f"[gpu] sampler 300 rows, keys holding 256 tokens {dtype}")
+    for (T, k, p, m, seed) in ((1.0, 10, 1.0, 0.0, 1), (1.0, 2500, 1.0, 0.0, 2), (0.9, 0, 0.6, 0.0, 3),
+                               (1.0, 50, 0.9, 0.05, 4)):
+        check_rows(bits, dtype, mask, None, T, k, p, m, seed=seed, offset=0, min_exact=0.9)
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_fuzz_filtered_16bit_many_rows(dtype):
+    """Seeded random batches of 257 to 700 rows (the 8-bit-counter histogram
+    in 512-thread blocks): shapes, masks, value spreads (heavy ties among
+    them, which may wrap a counter), and per-row filter settings."""
+    rng = np.random.default_rng(47 if dtype == "float16" else 53)
+    for case in range(4):
+        R = int(rng.integers(257, 700))
+        cols = int(rng.integers(1, 3000))
+        ties = bool(rng.integers(0, 2))
+        bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([0.3, 2.0, 8.0])), ties=ties)
+        density = rng.uniform(0.0, 1.0, (R, 1))
+        mask = workloads.pack_allowed(rng.random((R, cols)) < density, (cols + 31) // 32 + int(rng.integers(0, 2)), rng)
+        V = int(rng.integers(1, cols + 1))
+        T = rng.choice([0.0, 0.5, 1.0, 1.7], R).astype(np.float32)
+        k = rng.choice([0, 1, 5, 50, 400, 10000], R).astype(np.int32)
+        p = rng.choice([1.0, 0.99, 0.9, 0.5, 0.1], R).astype(np.float32)
+        m = rng.choice([0.0, 0.0, 0.05], R).astype(np.float32)
+        say(f"[gpu] sampler fuzz many rows {dtype} case {case}: R={R} cols={cols} V={V} ties={ties}")
+        check_rows(bits, dtype, mask, V, T, k, p, m, seed=200 + case, offset=case, min_exact=0.9)
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_kept_tokens_crowding_one_wave_many_rows(dtype):
+    """As the test above for 512-thread blocks (more rows than compute units):
+    8 waves, each with a list region of 2048 entries.  6000 kept tokens all
+    in wave 0's groups (groups g with g % 512 < 64) overflow its region, so
+    the row takes the walk; the GPU draws every row, the oracle checks 12."""
+    rng = np.random.default_rng(59)
+    R, cols = 300, 60000
+    x = rng.standard_normal((R, cols)).astype(np.float32) - np.float32(12.0)
+    group = np.arange(cols) // 8
+    x[:, (group % 512) < 64] += np.float32(16.0)       # wave 0's groups: 7504 tokens around +4
+    if dtype == "float16":
+        bits = x.astype(np.float16).view(np.uint16)
+    else:
+        b = x.view(np.uint32)
+        bits = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+    rows = list(range(0, R, 25))
+    say(f"[gpu] sampler kept tokens crowding one wave, 300 rows {dtype}")
+    check_rows(bits, dtype, None, None, 1.0, 6000, 1.0, 0.0, seed=61, offset=1, rows=rows, min_exact=0.75)
+    check_rows(bits, dtype, None, None, 1.0, 0, 0.999, 0.0, seed=62, offset=2, rows=rows, min_exact=0.75)
 
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
