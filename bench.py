@@ -618,10 +618,13 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
 
 
 def sampler_small_batch(torch, dev, mb, workloads, stream, steps=200):
-    """Greedy and unfiltered draws on the first B rows of the B=256 bf16 sampler shape, B = 1, 16, 64.
+    """Every mode on the first B rows of the B=256 bf16 sampler shape, B = 1, 16, 64.
 
-    With few rows and no filter the library splits each row over several
-    blocks; these are the batch sizes where that matters.  Cold rotation.
+    With few rows the library splits each row over several blocks: rows
+    without a filter by themselves, filtered rows through a workspace (the
+    default); these are the batch sizes where that matters.  The filtered
+    modes are timed without the workspace too ("one_block_per_row").  Cold
+    rotation.
     """
     import numpy as np
 
@@ -633,11 +636,18 @@ def sampler_small_batch(torch, dev, mb, workloads, stream, steps=200):
     for B in (1, 16, 64):
         tok = torch.empty(B, dtype=torch.int64, device=dev)
         res = {}
-        for mode, kw in (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperature=1.0))):
+        for mode, kw in (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperature=1.0)),
+                         ("top_k_50", dict(top_k=50)), ("top_p_0.9", dict(top_p=0.9)),
+                         ("top_k_50_top_p_0.9_min_p_0.05", dict(top_k=50, top_p=0.9, min_p=0.05))):
             ms = graph_ms(torch, lambda k, kw=kw: mb.mi_apply_bitmask_sample(
                 sets[k % nsets][0][:B], sets[k % nsets][1][:B], wl.vocab_size, seed=1, offset=k, out=tok, **kw),
                 steps, stream)
             res[mode] = {"us_per_call": ms * 1e3}
+            if mode.startswith("top"):
+                ms1 = graph_ms(torch, lambda k, kw=kw: mb.mi_apply_bitmask_sample(
+                    sets[k % nsets][0][:B], sets[k % nsets][1][:B], wl.vocab_size, seed=1, offset=k, out=tok,
+                    workspace=None, **kw), steps, stream)
+                res[mode]["one_block_per_row_us_per_call"] = ms1 * 1e3
         out[f"B{B}_V128000_bf16"] = res
     del sets
     torch.cuda.empty_cache()

@@ -225,6 +225,45 @@ mi_status_t mi_apply_bitmask_sample(
     int64_t vocab_size, const mi_sample_params_t *params, int64_t *tokens, hipStream_t stream);
 
 /*
+ * As mi_apply_bitmask_sample (same page and section), with a device
+ * workspace that lets a small batch spread its filtered rows over many
+ * compute units.  Without it, each row with top-k, top-p or min-p is drawn
+ * by one block, so a batch of a few such rows leaves most of the GPU idle.
+ * With it, a batch of at most 64 bf16 or fp16 rows of at least 8192 tokens
+ * splits each such row into segments: one kernel counts every segment's
+ * allowed tokens under their 16-bit keys into the row's histogram in the
+ * workspace, one finds the row's cut from it, and one draws over the
+ * segments, which merge their picks in `tokens` (five kernels on `stream`
+ * in all; `tokens` holds intermediate values until the last has run).  The
+ * tokens are the same as without the workspace: the cut comes from the same
+ * counts and the draw from the same Gumbel keys.
+ *
+ * workspace: device memory of workspace_bytes bytes, 16-byte aligned, not
+ * overlapping logits, mask, tokens or the per-row parameter arrays; its
+ * contents on entry do not matter and are overwritten.  It is used only when
+ * workspace_bytes >= mi_sample_workspace_bytes(dtype, rows, V) > 0, V being
+ * the vocab size the call resolves; otherwise (NULL included) the call runs
+ * as mi_apply_bitmask_sample.  Calls that share a workspace must not
+ * overlap in time.  Errors as mi_apply_bitmask_sample, plus
+ * MI_ERR_MISALIGNED and MI_ERR_ALIAS for a workspace that is used.
+ */
+mi_status_t mi_apply_bitmask_sample_ws(
+    const void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const mi_sample_params_t *params, int64_t *tokens, void *workspace,
+    int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes mi_apply_bitmask_sample_ws uses for `rows` rows of `vocab`
+ * tokens (the resolved vocab size) of `dtype`: rows * 262288 (a histogram of
+ * 65536 32-bit counts, a 128-byte map of its nonzero runs and 16 bytes of
+ * results per row) when the batch can
+ * split its filtered rows, else 0 (no workspace is used).  0 for invalid
+ * arguments.  Pure host arithmetic; no HIP call.
+ */
+int64_t mi_sample_workspace_bytes(mi_dtype_t dtype, int64_t rows, int64_t vocab);
+
+/*
  * Host-memory apply, for logits and masks that live on the CPU (XGrammar
  * "Bitmask Operations", Notes: Device: CPU tensors get a CPU
  * implementation).  Same arguments, rules and results as the device entry

@@ -24,6 +24,7 @@ VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3, "vec_resident": 4}
 # every symbol include/mi_bitmask.h declares
 EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",
            "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample",
+           "mi_apply_bitmask_sample_ws", "mi_sample_workspace_bytes",
            "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
            "mi_resolve_vocab_size", "mi_fill_value_bits", "mi_status_string", "mi_last_error_message",
            "mi_host_isa"]
@@ -69,11 +70,15 @@ def load_library(path: Union[str, pathlib.Path, None] = None) -> ctypes.CDLL:
                                           _dbl, _p]
     lib.mi_apply_bitmask_sample.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64,
                                             ctypes.POINTER(SampleParams), _p, _p]
+    lib.mi_apply_bitmask_sample_ws.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64,
+                                               ctypes.POINTER(SampleParams), _p, _p, _i64, _p]
+    lib.mi_sample_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64]
+    lib.mi_sample_workspace_bytes.restype = _i64
     lib.mi_apply_bitmask_inplace_host.argtypes = _INPLACE + [ctypes.c_int]
     lib.mi_apply_bitmask_out_host.argtypes = _OUT + [ctypes.c_int]
     for f in ("mi_apply_bitmask_inplace", "mi_apply_bitmask_inplace_ex", "mi_apply_bitmask_out",
               "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample",
-           "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
+              "mi_apply_bitmask_sample_ws", "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
               "mi_resolve_vocab_size", "mi_fill_value_bits"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mi_resolve_vocab_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64)]
@@ -261,7 +266,8 @@ def mi_apply_bitmask_rows(logits, mask, row_needs_mask=None, vocab_size: Optiona
 
 
 def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None, *, temperature=1.0, top_k=0,
-                            top_p=1.0, min_p=0.0, seed: int = 0, offset: int = 0, out=None, stream=None):
+                            top_p=1.0, min_p=0.0, seed: int = 0, offset: int = 0, out=None, stream=None,
+                            workspace="auto"):
     """One token per row (int64 [rows]) from the masked, filtered softmax.
 
     logits-processor page, "Ops: sample": per-row temperature (<= 0: argmax),
@@ -271,6 +277,12 @@ def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None,
     With ``mask`` (int32 [rows, ceil(V/32)] on the same GPU) masked tokens
     take no part; the logits are not modified.  A row with no allowed token
     gets -1.
+
+    ``workspace``: device memory that lets a small batch of filtered bf16 or
+    fp16 rows spread over many compute units (``mi_apply_bitmask_sample_ws``;
+    the tokens are the same either way).  "auto" allocates one when the call
+    can use it, None uses none, and a device tensor is used as it is (at
+    least ``sample_workspace_bytes`` bytes; calls sharing it must not overlap).
     """
     torch = _torch()
     if not logits.is_cuda:
@@ -311,13 +323,43 @@ def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None,
         mp, mr, mc, ms = M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M)
     else:
         mp, mr, mc, ms = None, 0, 0, 0
+    dt = MI_DTYPE[_dtype_name(L)]
+    wp, wn = None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        if vocab_size is not None:
+            V = int(vocab_size)
+        else:
+            V = L.shape[1] if mask is None else min(L.shape[1], 32 * mc)
+        need = lib.mi_sample_workspace_bytes(dt, rows, max(V, 0))
+        may_filter = any(isinstance(v, torch.Tensor) for v in (top_k, top_p, min_p)) or (
+            int(top_k) > 0 or float(top_p) < 1.0 or float(min_p) > 0.0)
+        if need > 0 and may_filter:
+            ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+            keep.append(ws)
+            wp, wn = ws.data_ptr(), need
+    elif workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != logits.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the logits' GPU")
+        wp, wn = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     for t in keep:
         _keep_alive(t, stream)
-    check(lib.mi_apply_bitmask_sample(
-        L.data_ptr(), MI_DTYPE[_dtype_name(L)], rows, L.shape[1], _row_stride(L), mp, mr, mc, ms,
-        -1 if vocab_size is None else int(vocab_size), ctypes.byref(prm), out.data_ptr(),
+    check(lib.mi_apply_bitmask_sample_ws(
+        L.data_ptr(), dt, rows, L.shape[1], _row_stride(L), mp, mr, mc, ms,
+        -1 if vocab_size is None else int(vocab_size), ctypes.byref(prm), out.data_ptr(), wp, wn,
         _stream_handle(logits.device, stream)))
     return out
+
+
+def sample_workspace_bytes(dtype, rows: int, vocab: int) -> int:
+    """Bytes of workspace ``mi_apply_bitmask_sample`` can use for ``rows`` rows of
+    ``vocab`` tokens of a torch ``dtype`` (0: none is used)."""
+    torch = _torch()
+    names = {torch.float32: "float32", torch.float16: "float16", torch.bfloat16: "bfloat16"}
+    if dtype not in names:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return int(load_library().mi_sample_workspace_bytes(MI_DTYPE[names[dtype]], int(rows), int(vocab)))
 
 
 def mi_apply_bitmask_out(logits, mask, out=None, vocab_size: Optional[int] = None,

@@ -31,6 +31,18 @@ constexpr int64_t kMaxSegments = 32;
 constexpr int64_t kFine16Rows = 256;
 constexpr int64_t kFine8Vocab = 65536;
 
+// Filtered 16-bit rows, at most this many in a batch, split over several
+// blocks when the caller gives a workspace (see split_hist in
+// sample_kernel.h).  The histogram pass takes at most kSplitHistBlocks
+// blocks in all (one per compute unit) and at most kMaxHistSegments per row
+// (every segment adds its nonzero counts to the row's histogram by atomics,
+// so fewer, longer segments contend less), each under 65536 tokens so its
+// 16-bit counters cannot wrap.
+constexpr int64_t kSplitFilteredRows = 64;
+constexpr int64_t kSplitHistBlocks = 256;
+constexpr int64_t kMaxHistSegments = 8;
+constexpr int64_t kSplitHistMaxSeg = 65280;
+
 // Checks for a call without a mask: every token below V takes part, and V
 // defaults to cols.
 mi_status_t check_logits_only(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t ls,
@@ -58,12 +70,21 @@ mi_status_t check_logits_only(const void* logits, mi_dtype_t dtype, int64_t rows
 
 }  // namespace
 
-MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
-                                           int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
-                                           int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
-                                           const mi_sample_params_t* params, int64_t* tokens, hipStream_t stream) {
+namespace {
+
+// Whether a batch takes the split filtered path (filtered 16-bit rows spread
+// over several blocks through the workspace): few rows, long enough to split.
+bool split_filtered_batch(mi_dtype_t dtype, int64_t rows, int64_t V) {
+  return dtype != MI_DTYPE_F32 && rows >= 1 && rows <= kSplitFilteredRows && V >= 8192;
+}
+
+mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+                        const int32_t* mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+                        int64_t vocab_size, const mi_sample_params_t* params, int64_t* tokens, void* workspace,
+                        int64_t workspace_bytes, hipStream_t stream) {
   if (!params) return fail(MI_ERR_NULL_POINTER, "params is NULL");
   if (!tokens && rows > 0) return fail(MI_ERR_NULL_POINTER, "tokens is NULL");
+  if (workspace_bytes < 0) return fail(MI_ERR_BAD_SHAPE, "negative workspace_bytes");
   Plan p;
   mi_status_t st;
   if (mask) {
@@ -82,6 +103,23 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
   for (const void* q : {static_cast<const void*>(params->temperature), static_cast<const void*>(params->top_k),
                         static_cast<const void*>(params->top_p), static_cast<const void*>(params->min_p)})
     if (reinterpret_cast<uintptr_t>(q) % 4) return fail(MI_ERR_MISALIGNED, "a per-row parameter array is not 4-byte aligned");
+  // The workspace is used only when this batch can split its filtered rows
+  // and it is large enough; then it must not overlap anything else.
+  const int64_t ws_need = split_filtered_batch(dtype, rows, p.V) ? mi::split_workspace_bytes(rows) : 0;
+  const bool use_ws = workspace && ws_need > 0 && workspace_bytes >= ws_need;
+  if (use_ws) {
+    if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(MI_ERR_MISALIGNED, "workspace not 16-byte aligned");
+    ByteRange wb;
+    if (!extent(workspace, 1, ws_need, ws_need, 1, &wb)) return fail(MI_ERR_BAD_SHAPE, "workspace extent overflows");
+    if (overlaps(wb, p.logits) || overlaps(wb, p.mask) || overlaps(wb, tb))
+      return fail(MI_ERR_ALIAS, "workspace overlaps logits, mask or tokens");
+    const void* per_row[4] = {params->temperature, params->top_k, params->top_p, params->min_p};
+    for (const void* q : per_row) {
+      ByteRange qb;
+      if (q && extent(q, 1, rows * 4, rows * 4, 1, &qb) && overlaps(wb, qb))
+        return fail(MI_ERR_ALIAS, "workspace overlaps a per-row parameter array");
+    }
+  }
   if (rows == 0) return MI_OK;
 
   mi::SampleArgs a{params->temperature, params->top_k, params->top_p, params->min_p,
@@ -123,8 +161,12 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     // A launch of greedy rows alone gains only at one or two rows: one block
     // reads a row about as fast as a few blocks that then merge.
     const bool greedy_only = !ar.temperature && !(ar.temperature_all > 0.f);
+    // With a workspace, a small batch that may filter splits its rows too
+    // (split_hist, split_search, then a segmented draw).
+    const bool split_filtered = use_ws && (may_filter || may_min_p);
     int32_t nseg = 1, seg_len = V;
-    if (!may_filter && !may_min_p && n <= (greedy_only ? kSplitRowsGreedy : kSplitRows) && V >= 8192) {
+    if ((split_filtered || (!may_filter && !may_min_p && n <= (greedy_only ? kSplitRowsGreedy : kSplitRows))) &&
+        V >= 8192) {
       nseg = static_cast<int32_t>(std::min<int64_t>({(kSplitBlocks + n - 1) / n, kMaxSegments, (V + 4095) / 4096}));
       seg_len = static_cast<int32_t>(((V + nseg - 1) / nseg + 255) / 256 * 256);
       nseg = (V + seg_len - 1) / seg_len;
@@ -132,26 +174,58 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
     const bool fine8 = fine && n > kFine16Rows && V <= kFine8Vocab;
     const bool deep = (n <= 256 || fine) && nseg == 1;
     const int threads = fine8 ? 512 : deep ? 1024 : 256;
-    const size_t lds = fine ? std::max(mi::sample_fine_bytes(threads), mi::sample_hist_bytes(threads))
-                            : (may_filter ? mi::sample_hist_bytes(threads) : 0);
-    if (nseg > 1) mi::clear_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
-#define MI_SAMPLE(TAG, BITS, BYTES, THREADS)                                                                   \
-  mi::sample_rows<TAG, BYTES, THREADS><<<static_cast<uint32_t>(n) * nseg, THREADS, lds, stream>>>(              \
+    const size_t lds = fine && nseg == 1 ? std::max(mi::sample_fine_bytes(threads), mi::sample_hist_bytes(threads))
+                                         : (may_filter ? mi::sample_hist_bytes(threads) : 0);
+    const mi::SplitInfo* sinfo = nullptr;
+    if (split_filtered && nseg > 1) {
+      // the histogram pass: segments of a multiple of 256 tokens, fewer than
+      // 65536, about kSplitHistBlocks blocks in all
+      int64_t hseg = std::min<int64_t>({std::max<int64_t>(kSplitHistBlocks / n, 1), kMaxHistSegments, (V + 4095) / 4096});
+      hseg = std::max<int64_t>(hseg, (V + kSplitHistMaxSeg - 1) / kSplitHistMaxSeg);
+      const int64_t hlen = ((V + hseg - 1) / hseg + 255) / 256 * 256;
+      hseg = (V + hlen - 1) / hlen;
+      uint32_t* hist = static_cast<uint32_t*>(workspace);
+      uint32_t* map = hist + static_cast<int64_t>(n) * mi::kSplitHistWords;
+      mi::SplitInfo* info = reinterpret_cast<mi::SplitInfo*>(map + static_cast<int64_t>(n) * mi::kSplitMapWords);
+      const int64_t n16 = static_cast<int64_t>(n) * (mi::kSplitHistWords + mi::kSplitMapWords) / 4;
+      mi::split_clear<<<static_cast<uint32_t>((n16 + 255) / 256), 256, 0, stream>>>(reinterpret_cast<uint4*>(hist), n16,
+                                                                                   tokens + r0, n);
+      const uint32_t hblocks = static_cast<uint32_t>(n * hseg);
+      if (dtype == MI_DTYPE_F16) {
+        mi::split_hist<mi::F16Bits><<<hblocks, 1024, mi::sample_fine_bytes(1024), stream>>>(
+            reinterpret_cast<const uint16_t*>(lg), logits_row_stride, mk, mask_row_stride, V, ar,
+            static_cast<int32_t>(hseg), static_cast<int32_t>(hlen), hist, map);
+        mi::split_search<mi::F16Bits><<<n, 1024, 0, stream>>>(ar, hist, map, info);
+      } else {
+        mi::split_hist<mi::BF16Bits><<<hblocks, 1024, mi::sample_fine_bytes(1024), stream>>>(
+            reinterpret_cast<const uint16_t*>(lg), logits_row_stride, mk, mask_row_stride, V, ar,
+            static_cast<int32_t>(hseg), static_cast<int32_t>(hlen), hist, map);
+        mi::split_search<mi::BF16Bits><<<n, 1024, 0, stream>>>(ar, hist, map, info);
+      }
+      sinfo = info;
+    } else if (nseg > 1) {
+      mi::clear_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
+    }
+#define MI_SAMPLE(TAG, BITS, BYTES, THREADS, SPLITF)                                                           \
+  mi::sample_rows<TAG, BYTES, THREADS, SPLITF><<<static_cast<uint32_t>(n) * nseg, THREADS, lds, stream>>>(      \
       reinterpret_cast<const BITS*>(lg), logits_row_stride, mk, mask_row_stride, V, ar, r0, tokens + r0, nseg,     \
-      seg_len)
+      seg_len, sinfo)
     switch (dtype) {
       case MI_DTYPE_F32:
-        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024); else MI_SAMPLE(mi::F32Bits, uint32_t, 128, 256);
+        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024, false);
+        else MI_SAMPLE(mi::F32Bits, uint32_t, 128, 256, false);
         break;
       case MI_DTYPE_F16:
-        if (fine8) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512);
-        else if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024);
-        else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256);
+        if (sinfo) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, true);
+        else if (fine8) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512, false);
+        else if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024, false);
+        else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, false);
         break;
       default:
-        if (fine8) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512);
-        else if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024);
-        else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256);
+        if (sinfo) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, true);
+        else if (fine8) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512, false);
+        else if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024, false);
+        else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, false);
     }
 #undef MI_SAMPLE
     if (nseg > 1) mi::finish_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
@@ -159,3 +233,26 @@ MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype,
   return after_launch("sample_rows");
 }
 
+}  // namespace
+
+MI_API mi_status_t mi_apply_bitmask_sample(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                                           int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
+                                           int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
+                                           const mi_sample_params_t* params, int64_t* tokens, hipStream_t stream) {
+  return sample_impl(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
+                     vocab_size, params, tokens, nullptr, 0, stream);
+}
+
+MI_API mi_status_t mi_apply_bitmask_sample_ws(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                                              int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
+                                              int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
+                                              const mi_sample_params_t* params, int64_t* tokens, void* workspace,
+                                              int64_t workspace_bytes, hipStream_t stream) {
+  return sample_impl(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
+                     vocab_size, params, tokens, workspace, workspace_bytes, stream);
+}
+
+MI_API int64_t mi_sample_workspace_bytes(mi_dtype_t dtype, int64_t rows, int64_t vocab) {
+  if (!valid_dtype(static_cast<int>(dtype)) || rows < 0 || vocab < 0 || vocab > kMaxSampleVocab) return 0;
+  return split_filtered_batch(dtype, rows, vocab) ? mi::split_workspace_bytes(rows) : 0;
+}

@@ -13,7 +13,10 @@
 // One block per row (1024 threads when each compute unit holds one row;
 // 256 when many rows share a unit, or 512 for filtered 16-bit rows, two to a
 // unit), or, for a few rows without top-k, top-p or min-p, one 256-thread
-// block per segment of a row, the segments merging by an atomic maximum.
+// block per segment of a row, the segments merging by an atomic maximum.  A
+// few filtered 16-bit rows split the same way when the caller gives a
+// workspace: their cuts come first from merged per-segment histograms
+// (split_hist, split_search below).
 // Each pass walks the row in groups of 8 consecutive tokens per thread
 // through raw buffer loads (16-byte vectors when the row start is aligned),
 // several groups in flight per thread; trip counts are uniform across the
@@ -443,6 +446,60 @@ __device__ __forceinline__ uint32_t order_key16x2(uint32_t two) {
   return two ^ (__builtin_bit_cast(uint32_t, sign) | 0x80008000u);
 }
 
+// Count the tokens the mask allows under their 16-bit keys into `fine`
+// (LDS, CB-bit counters, KW = 32 / CB to a word: key k in word k / KW), from
+// a cleared start; returns this thread's number of allowed tokens below V.
+// A token the mask rules out adds to its lane's spare word (after the 65536
+// keys) instead, so the add needs no branch and spreads over the banks.
+// Ends with a barrier.  A row of at most 4 groups per thread may come
+// already loaded in pre[4] (group j * THREADS + t in pre[j], with
+// `preloaded` set); otherwise the pass reads the row.
+template <typename D, int BYTES, int THREADS, int CB>
+__device__ __forceinline__ uint32_t count_keys(const RowView<D>& rv, uint32_t* fine,
+                                               const typename RowView<D>::Raw (&pre)[4], bool preloaded) {
+  constexpr uint32_t KW = 32 / CB;
+  constexpr uint32_t kWords = 65536 / KW;
+  const int t = static_cast<int>(threadIdx.x);
+  uint4* f4 = reinterpret_cast<uint4*>(fine);
+  for (int i = t; i < static_cast<int>(kWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  uint32_t allowed = 0;
+  const uint32_t spare = KW * (kWords + static_cast<uint32_t>(lane_id()));
+  const auto add = [&](uint32_t k, uint32_t bit) {
+    const uint32_t kk = bit ? k : spare;
+    atomicAdd(&fine[kk / KW], 1u << ((kk % KW) * CB));
+  };
+  const auto group = [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+    const uint32_t bits = rv.mask_bits(raw, g, full);
+    allowed += __builtin_popcount(bits);
+#pragma unroll
+    for (int p2 = 0; p2 < 4; ++p2) {
+      const uint32_t k2 = order_key16x2(raw.v[p2]);
+      add(k2 & 0xFFFFu, (bits >> (2 * p2)) & 1u);
+      add(k2 >> 16, (bits >> (2 * p2 + 1)) & 1u);
+    }
+  };
+  if (preloaded) {
+    const int32_t nfull = rv.V >> 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int32_t g = j * THREADS + t;
+      group(g, pre[j], g < nfull);
+    }
+  } else {
+    walk_row_raw<BYTES, THREADS>(rv, group);
+  }
+  if ((rv.V & 7) && t == 0) {  // the partial last group, by plain loads
+    for (int32_t i = rv.V & ~7; i < rv.V; ++i) {
+      const uint32_t bit = rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u;
+      allowed += bit;
+      add(order_key16x2(rv.row[i]) & 0xFFFFu, bit);
+    }
+  }
+  __syncthreads();
+  return allowed;
+}
+
 // Top-k and top-p cuts of a 16-bit row from one pass over it.  Each finite
 // bf16 or fp16 value has a 16-bit key of its own, and the tokens under one
 // key share their value, so a count per key answers both searches exactly:
@@ -472,7 +529,6 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   constexpr int kWaves = THREADS / 64;
   constexpr int CB = kFineBits<THREADS>;        // bits per counter
   constexpr uint32_t KW = 32 / CB;              // keys per word
-  constexpr uint32_t kWords = 65536 / KW;
   constexpr uint32_t KPT = 65536 / THREADS;     // keys per thread: 64 or 128
   static_assert(KPT / KW == 32, "a thread owns 32 words of the histogram");
   constexpr uint32_t KPL = KPT / 64;            // keys per lane in the final search
@@ -495,51 +551,11 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
     }
   };
 
-  uint4* f4 = reinterpret_cast<uint4*>(fine);
-  for (int i = t; i < static_cast<int>(kWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
   if (t < 2) {
     s_cut[t] = 0u;
     s_cross[t] = ~0u;  // no crossing: keep every candidate
   }
-  __syncthreads();
-
-  // ---- the pass: key k counts in word k / KW; a token the mask rules out
-  // adds to this lane's spare word instead, so the add needs no branch and
-  // spreads over the banks
-  uint32_t allowed = 0;  // tokens the mask allows below V
-  const uint32_t spare = KW * (kWords + static_cast<uint32_t>(lane));
-  const auto add = [&](uint32_t k, uint32_t bit) {
-    const uint32_t kk = bit ? k : spare;
-    atomicAdd(&fine[kk / KW], 1u << ((kk % KW) * CB));
-  };
-  const auto group = [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
-    const uint32_t bits = rv.mask_bits(raw, g, full);
-    allowed += __builtin_popcount(bits);
-#pragma unroll
-    for (int p2 = 0; p2 < 4; ++p2) {
-      const uint32_t k2 = order_key16x2(raw.v[p2]);
-      add(k2 & 0xFFFFu, (bits >> (2 * p2)) & 1u);
-      add(k2 >> 16, (bits >> (2 * p2 + 1)) & 1u);
-    }
-  };
-  if (preloaded) {  // a short row, already loaded by the caller: group j * THREADS + t in pre[j]
-    const int32_t nfull = rv.V >> 3;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int32_t g = j * THREADS + t;
-      group(g, pre[j], g < nfull);
-    }
-  } else {
-    walk_row_raw<BYTES, THREADS>(rv, group);
-  }
-  if ((rv.V & 7) && t == 0) {  // the partial last group, by plain loads
-    for (int32_t i = rv.V & ~7; i < rv.V; ++i) {
-      const uint32_t bit = rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u;
-      allowed += bit;
-      add(order_key16x2(rv.row[i]) & 0xFFFFu, bit);
-    }
-  }
-  __syncthreads();
+  uint32_t allowed = count_keys<D, BYTES, THREADS, CB>(rv, fine, pre, preloaded);  // tokens the mask allows below V
 
   // ---- sums: thread t holds keys [KPT t, KPT t + KPT), words [32t, 32t + 32),
   // read in a rotated order so a wave's lanes hit different banks.  Only
@@ -728,6 +744,267 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   return true;
 }
 
+// ---- Filtered 16-bit rows split over several blocks (few rows).
+//
+// A batch of a few rows with top-k, top-p or min-p would otherwise keep one
+// compute unit per row busy while the rest idle.  Such rows are instead
+// spread over a caller's workspace in three launches:
+//   split_hist    one 1024-thread block per segment of a row counts the
+//                 segment's allowed tokens under their 16-bit keys (LDS,
+//                 16-bit counters: a segment holds fewer than 65536 tokens)
+//                 and adds its nonzero counts into the row's histogram of
+//                 65536 32-bit counts in the workspace, two adjacent keys per
+//                 64-bit atomic (a count stays below 2^28, so the low one
+//                 never carries into the high one); it also marks each run
+//                 of 64 keys that received a count in the row's 1024-bit map;
+//   split_search  one block per row finds the maximum and the top-k / top-p
+//                 cuts from those counts, exactly as fine_search does from
+//                 its LDS histogram (same counts, same fixed-point masses, so
+//                 the same cut), reading only the marked runs, and stores the
+//                 result per row;
+//   sample_rows   one block per segment draws over its segment with that
+//                 cut, the segments merging through the row's output word.
+// Workspace layout: every row's histogram (65536 words, key k at word k),
+// then every row's run map (32 words), then one SplitInfo per row.
+
+// The split search's result for one row.
+struct SplitInfo {
+  uint32_t cut16;  // keep the candidates whose 16-bit key is at least cut16 (0: every one)
+  float best;      // the largest candidate; -inf when the row has none
+  uint32_t kept;   // the candidates the cut keeps
+  uint32_t pad;
+};
+constexpr int64_t kSplitHistWords = 65536;
+constexpr int64_t kSplitMapWords = 32;
+constexpr int64_t split_workspace_bytes(int64_t rows) {
+  return rows * ((kSplitHistWords + kSplitMapWords) * 4 + static_cast<int64_t>(sizeof(SplitInfo)));
+}
+
+// Whether row r takes the split filtered path: a positive temperature with
+// top-k, top-p or min-p in force (the same tests sample_rows makes).
+__device__ __forceinline__ bool split_filtered_row(const SampleArgs& a, int64_t r) {
+  const float temp = a.temperature ? a.temperature[r] : a.temperature_all;
+  const int32_t top_k = a.top_k ? a.top_k[r] : a.top_k_all;
+  const float top_p = a.top_p ? a.top_p[r] : a.top_p_all;
+  const float min_p = a.min_p ? a.min_p[r] : a.min_p_all;
+  const float inv_t = 1.0f / temp;
+  return temp > 0.f && ((top_k > 0 && inv_t > 0.f) || (top_p < 1.0f && inv_t > 0.f) || min_p > 0.f);
+}
+
+// Before a split filtered launch: the histograms, run maps and output words
+// at 0.  A kernel rather than a memset, so graphs replay it.
+__global__ void split_clear(uint4* __restrict__ ws, int64_t n16, int64_t* __restrict__ out, int64_t rows) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    ws[i] = make_uint4(0u, 0u, 0u, 0u);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < rows) out[i] = 0;
+}
+
+// One segment of a filtered row: its 16-bit key counts, added into the row's
+// workspace histogram (hist, rows x 65536 words) and run map (map, rows x 32
+// words).  Block b is segment b % nseg of row b / nseg; seg_len is a
+// multiple of 256 below 65536.
+template <typename D>
+__global__ __launch_bounds__(1024) void split_hist(const typename D::Bits* __restrict__ logits, int64_t ls,
+                                                   const uint32_t* __restrict__ mask, int64_t ms, int32_t V,
+                                                   SampleArgs a, int32_t nseg, int32_t seg_len,
+                                                   uint32_t* __restrict__ hist, uint32_t* __restrict__ map) {
+  extern __shared__ unsigned long long s_dyn[];
+  const int64_t r = blockIdx.x / nseg;
+  const int32_t tok0 = static_cast<int32_t>(blockIdx.x % nseg) * seg_len;
+  if (!split_filtered_row(a, r) || tok0 >= V) return;  // uniform across the block
+  const RowView<D> rv(logits + r * ls + tok0, mask ? mask + r * ms + tok0 / 32 : nullptr, min(seg_len, V - tok0));
+  uint32_t* fine = reinterpret_cast<uint32_t*>(s_dyn);
+  const typename RowView<D>::Raw pre[4] = {};
+  count_keys<D, 64, 1024, 16>(rv, fine, pre, false);  // 4 groups in flight: a segment holds few per thread
+  // Word 1024 j + t (keys 2 (1024 j + t) and the next) is added by thread
+  // t, so the nonzero words, which crowd a narrow range of keys, spread over
+  // every thread.  Its run of 64 keys, 32 j + t / 32, is bit t / 32 of map
+  // word j: a wave marks its two runs per j by one ballot, in an LDS copy
+  // of the map first.
+  __shared__ uint32_t s_map[32];
+  const int t = static_cast<int>(threadIdx.x);
+  const int wave = t >> 6;
+  if (t < 32) s_map[t] = 0u;
+  __syncthreads();
+  unsigned long long* h2 = reinterpret_cast<unsigned long long*>(hist + r * kSplitHistWords);
+  uint32_t w[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) w[j] = fine[j * 1024 + t];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint64_t b = __ballot(w[j] != 0u);
+    if (lane_id() == 0 && b)
+      atomicOr(&s_map[j], ((static_cast<uint32_t>(b) ? 1u : 0u) << (2 * wave)) |
+                              ((static_cast<uint32_t>(b >> 32) ? 1u : 0u) << (2 * wave + 1)));
+    if (w[j]) atomicAdd(h2 + j * 1024 + t, (static_cast<unsigned long long>(w[j] >> 16) << 32) | (w[j] & 0xFFFFu));
+  }
+  __syncthreads();
+  if (t < 32 && s_map[t]) atomicOr(map + r * kSplitMapWords + t, s_map[t]);
+}
+
+// One block per row of the split batch: the largest candidate and the top-k
+// and top-p cuts from the row's workspace histogram, into info[r].  The
+// same search as fine_search, on 32-bit counts that never wrap; thread t
+// holds keys [64t, 64t + 64) and reads them only when the run map marks
+// them.
+template <typename D>
+__global__ __launch_bounds__(1024) void split_search(SampleArgs a, const uint32_t* __restrict__ hist,
+                                                     const uint32_t* __restrict__ map,
+                                                     SplitInfo* __restrict__ info) {
+  using Bits = typename D::Bits;
+  constexpr int kWaves = 16;
+  constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
+  __shared__ uint32_t s_kmax[kWaves], s_c[kWaves], s_cut[2], s_cross[2], s_above_n[2], s_kept[2];
+  __shared__ unsigned long long s_m[kWaves], s_above[2];
+  const int64_t r = blockIdx.x;
+  if (!split_filtered_row(a, r)) return;  // uniform across the block
+  const float temp = a.temperature ? a.temperature[r] : a.temperature_all;
+  const int32_t top_k = a.top_k ? a.top_k[r] : a.top_k_all;
+  const float top_p = a.top_p ? a.top_p[r] : a.top_p_all;
+  const float inv_t = 1.0f / temp;
+  const bool use_k = top_k > 0 && inv_t > 0.f;
+  const bool use_p = top_p < 1.0f && inv_t > 0.f;
+  const uint32_t* h = hist + r * kSplitHistWords;
+  const int t = static_cast<int>(threadIdx.x);
+  const int lane = lane_id(), wave = t >> 6;
+  const uint32_t k0 = 64u * static_cast<uint32_t>(t);
+  const auto in_range = [](uint32_t k) { return k - D::kKey16Lo <= kSpan; };
+  const bool marked = (map[r * kSplitMapWords + (t >> 5)] >> (t & 31)) & 1u;
+  const uint4* h4 = reinterpret_cast<const uint4*>(h + k0);
+  if (t < 2) {
+    s_cut[t] = 0u;
+    s_cross[t] = ~0u;  // no crossing: keep every candidate
+  }
+
+  // ---- this thread's candidates and highest candidate key, all 64 counts
+  // loaded at once
+  uint32_t c = 0, ktop = 0;
+  if (marked) {
+    uint4 q[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) q[u] = h4[u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t n4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = k0 + 4u * u + e;
+        if (n4[e] && in_range(k)) {
+          c += n4[e];
+          ktop = k + 1;
+        }
+      }
+    }
+  }
+  uint32_t sc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t vc = static_cast<uint32_t>(__shfl_down(static_cast<int>(sc), o));
+    if (lane + o < 64) sc += vc;
+    ktop = max(ktop, static_cast<uint32_t>(__shfl_xor(static_cast<int>(ktop), o)));
+  }
+  if (lane == 0) {
+    s_c[wave] = sc;
+    s_kmax[wave] = ktop;
+  }
+  __syncthreads();
+  uint32_t tot_c = 0;
+  ktop = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    tot_c += s_c[w];
+    ktop = max(ktop, s_kmax[w]);
+    if (w > wave) sc += s_c[w];
+  }
+  if (tot_c == 0) {
+    if (t == 0) info[r] = SplitInfo{0u, -__builtin_inff(), 0u, 0u};
+    return;
+  }
+  const float best = D::value(static_cast<Bits>(bits_of_key16(ktop - 1)));
+  const float zmax = best * inv_t;
+  const auto mass = [&](uint32_t k) { return fixed_mass(D::value(static_cast<Bits>(bits_of_key16(k))), inv_t, zmax); };
+
+  // ---- top-p masses per thread (the counts read again), then their suffix totals
+  unsigned long long m = 0, sm = 0, tot_m = 0;
+  if (use_p) {
+    if (marked && c) {
+      uint4 q[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) q[u] = h4[u];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t n4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t k = k0 + 4u * u + e;
+          if (n4[e] && in_range(k)) m += static_cast<unsigned long long>(n4[e]) * mass(k);
+        }
+      }
+    }
+    sm = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long vm = __shfl_down(sm, o);
+      if (lane + o < 64) sm += vm;
+    }
+    if (lane == 0) s_m[wave] = sm;
+    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+      tot_m += s_m[w];
+      if (w > wave) sm += s_m[w];
+    }
+  }
+
+  // ---- the crossing thread posts itself; one wave per search then takes
+  // its 64 keys, one per lane (top-k on wave 0, top-p on wave 1)
+  const uint32_t need_k = static_cast<uint32_t>(top_k);  // more than the candidates: keep all
+  const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(tot_m);
+  const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
+  const unsigned long long need_p = target ? target : 1ull;  // p <= 0 keeps just the largest value
+  if (t == 0) s_kept[0] = s_kept[1] = tot_c;  // a search without a crossing keeps every candidate
+  if (use_k && need_k <= tot_c && sc >= need_k && sc - c < need_k) {
+    s_cross[0] = static_cast<uint32_t>(t);
+    s_above[0] = sc - c;
+    s_above_n[0] = sc - c;
+  }
+  if (use_p && need_p <= tot_m && sm >= need_p && sm - m < need_p) {
+    s_cross[1] = static_cast<uint32_t>(t);
+    s_above[1] = sm - m;
+    s_above_n[1] = sc - c;
+  }
+  __syncthreads();
+  const int which = wave;
+  if (which < 2 && (which == 0 ? use_k : use_p) && s_cross[which] != ~0u) {
+    const uint32_t kx = 64u * s_cross[which] + static_cast<uint32_t>(lane);
+    const uint32_t n = in_range(kx) ? h[kx] : 0u;
+    unsigned long long v = which == 0 ? n : (n ? static_cast<unsigned long long>(n) * mass(kx) : 0ull);
+    uint32_t vn = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long u = __shfl_down(v, o);
+      const uint32_t un = static_cast<uint32_t>(__shfl_down(static_cast<int>(vn), o));
+      if (lane + o < 64) {
+        v += u;
+        vn += un;
+      }
+    }
+    const unsigned long long total = v + s_above[which];
+    const uint64_t hit = __ballot(total >= (which == 0 ? static_cast<unsigned long long>(need_k) : need_p));
+    const int L = 63 - __clzll(static_cast<long long>(hit));
+    const uint32_t at_cut = static_cast<uint32_t>(__shfl(static_cast<int>(vn), L)) + s_above_n[which];
+    if (lane == 0) {
+      s_cut[which] = 64u * s_cross[which] + static_cast<uint32_t>(L);
+      s_kept[which] = at_cut;
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t kept = min(use_k ? s_kept[0] : tot_c, use_p ? s_kept[1] : tot_c);
+    info[r] = SplitInfo{max(s_cut[0], s_cut[1]), best, kept, 0u};
+  }
+}
+
 // One block of THREADS threads per row, 128 bytes of logits in flight per
 // thread: 1024 threads when each compute unit holds one row at a time; 256
 // so several rows share a compute unit when there are many rows.  The draw,
@@ -740,12 +1017,12 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
 // Gumbel key, inverted token index), so the largest wins and ties go to the
 // lowest index.  out must hold 0 beforehand (clear_tokens) and is turned
 // into token numbers afterwards (finish_tokens).
-template <typename D, int BYTES, int THREADS>
+template <typename D, int BYTES, int THREADS, bool SPLITF = false>
 __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
                                                               const uint32_t* __restrict__ mask, int64_t ms,
                                                               int32_t V, SampleArgs a, int64_t row_base,
                                                               int64_t* __restrict__ out, int32_t nseg,
-                                                              int32_t seg_len) {
+                                                              int32_t seg_len, const SplitInfo* __restrict__ info) {
   constexpr int kWaves = THREADS / 64;
   __shared__ float s_best[kWaves];
   __shared__ int32_t s_besti[kWaves];
@@ -800,10 +1077,28 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   uint32_t cut = 0;        // keep tokens with order_key(x) >= cut
   uint32_t n_kept = 0;     // with the cut from the 16-bit search: candidates at or above it
   uint32_t cut16 = 0;      // and that cut as a 16-bit key (0: keep all)
+  // A filtered row split over several blocks (SPLITF, nseg > 1): its
+  // maximum and cut come from split_search, over the whole row.
+  const bool from_split = SPLITF && temp > 0.f && (use_k || use_p || min_p > 0.f);
+  if (from_split) {
+    const SplitInfo si = info[r];
+    if (si.best == -__builtin_inff()) {  // no candidate: the row's word keeps 0 (token -1)
+      if (!split && t == 0) out[r] = -1;
+      return;
+    }
+    best = si.best;
+    have_best = true;
+    if (use_k || use_p) {
+      have_cut = true;
+      cut16 = si.cut16;
+      cut = cut16 ? order_key(D::value(static_cast<typename D::Bits>(bits_of_key16(cut16)))) : 0u;
+      n_kept = si.kept;
+    }
+  }
   // A 16-bit row with a filter and at most 4 groups per thread is loaded once
   // into registers: the histogram pass and the draw both use these words.
   typename RowView<D>::Raw pre[4] = {};
-  const bool preloaded = kFineSearch<D, THREADS> && (use_k || use_p) && rv.V <= 4 * 8 * THREADS;
+  const bool preloaded = kFineSearch<D, THREADS> && (use_k || use_p) && !from_split && rv.V <= 4 * 8 * THREADS;
   if constexpr (kFineSearch<D, THREADS>) {
     if (preloaded) {
       const int32_t nfull = rv.V >> 3;
@@ -816,7 +1111,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       }
     }
     // 16-bit rows with a filter: one pass gives the maximum and both cuts
-    if (use_k || use_p) {
+    if ((use_k || use_p) && !from_split) {
       have_cut = fine_search<D, BYTES, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p,
                                                 top_p, &best, &cut, &cut16, &n_kept, pre, preloaded);
       if (have_cut) {  // else the radix search below, after the first pass if the row needs the maximum

@@ -271,3 +271,63 @@ def test_sample_rejections(name, kw, code):
 def test_sample_accepts_the_largest_vocab_at_the_checks():
     """2^28 passes the size checks; with zero rows nothing is launched."""
     assert sample_call(mask=None, rows=0, cols=1 << 28, ls=1 << 28, vocab=1 << 28) == OK
+
+
+def sample_ws_call(workspace, workspace_bytes, **kw):
+    """A bf16 batch the workspace can split (4 rows of 8192 tokens, top-k 50)."""
+    a = dict(logits=LOGITS, dtype=2, rows=4, cols=8192, ls=8192, mask=MASK, mask_rows=4, mask_cols=256, ms=256,
+             vocab=-1, tokens=OUT)
+    a.update(kw)
+    prm = _binding.SampleParams()
+    prm.temperature_all, prm.top_k_all, prm.top_p_all, prm.min_p_all = 1.0, 50, 1.0, 0.0
+    for name in ("temperature", "top_k", "top_p", "min_p"):
+        if name in kw:
+            setattr(prm, name, kw[name])
+    return mb.load_library().mi_apply_bitmask_sample_ws(
+        a["logits"], a["dtype"], a["rows"], a["cols"], a["ls"], a["mask"], a["mask_rows"], a["mask_cols"],
+        a["ms"], a["vocab"], ctypes.byref(prm), a["tokens"], workspace, workspace_bytes, None)
+
+
+WS = 0x7F4000000000
+WS_BYTES = 4 * 262288
+
+REJECT_SAMPLE_WS = [
+    ("negative workspace bytes", dict(workspace=WS, workspace_bytes=-1), SHAPE),
+    ("workspace misaligned", dict(workspace=WS + 8, workspace_bytes=WS_BYTES), MISALIGNED),
+    ("workspace over logits", dict(workspace=LOGITS + 4096, workspace_bytes=WS_BYTES), ALIAS),
+    ("workspace over mask", dict(workspace=MASK - 16, workspace_bytes=WS_BYTES), ALIAS),
+    ("workspace over tokens", dict(workspace=OUT - 1024, workspace_bytes=WS_BYTES), ALIAS),
+    ("workspace over a per-row array", dict(workspace=WS, workspace_bytes=WS_BYTES, top_p=WS + 4096), ALIAS),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", REJECT_SAMPLE_WS, ids=[r[0] for r in REJECT_SAMPLE_WS])
+def test_sample_ws_rejections(name, kw, code):
+    kw = dict(kw)
+    assert sample_ws_call(kw.pop("workspace"), kw.pop("workspace_bytes"), **kw) == code
+    assert mb.load_library().mi_last_error_message().decode()
+
+
+def test_sample_ws_checks_only_a_workspace_it_uses():
+    """A workspace that is too small, or a batch that cannot split (fp32, more
+    than 64 rows, fewer than 8192 tokens), leaves the workspace unused: its
+    placement is not checked, and with zero rows nothing is launched."""
+    assert sample_ws_call(LOGITS + 4096, WS_BYTES - 1, rows=0) == OK
+    assert sample_ws_call(LOGITS + 4096, WS_BYTES, dtype=0, rows=0) == OK
+    assert sample_ws_call(WS + 8, WS_BYTES, rows=0, cols=8191, ls=8191) == OK
+    assert sample_ws_call(WS + 8, WS_BYTES, rows=0) == OK            # no rows: nothing to split
+
+
+def test_sample_workspace_bytes():
+    lib = mb.load_library()
+    per_row = 65536 * 4 + 128 + 16
+    assert lib.mi_sample_workspace_bytes(2, 1, 128000) == per_row
+    assert lib.mi_sample_workspace_bytes(1, 64, 8192) == 64 * per_row
+    assert lib.mi_sample_workspace_bytes(1, 65, 8192) == 0       # more rows than the split takes
+    assert lib.mi_sample_workspace_bytes(2, 16, 8191) == 0       # rows too short to split
+    assert lib.mi_sample_workspace_bytes(0, 16, 128000) == 0     # fp32 rows are not split
+    assert lib.mi_sample_workspace_bytes(7, 16, 128000) == 0     # invalid dtype
+    assert lib.mi_sample_workspace_bytes(2, 0, 128000) == 0
+    assert lib.mi_sample_workspace_bytes(2, 1, (1 << 28) + 1) == 0
+    torch = pytest.importorskip("torch")
+    assert mb.sample_workspace_bytes(torch.float16, 3, 32000) == 3 * per_row

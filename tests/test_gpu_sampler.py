@@ -57,8 +57,10 @@ def per_row(v, i):
     return v[i] if isinstance(v, np.ndarray) else v
 
 
-def check_rows(bits, dtype, mask, vocab, T, k, p, m, seed, offset, rows=None, min_exact=0.98):
-    """Sample on the GPU and check every row against the oracle; returns the tokens."""
+def check_rows(bits, dtype, mask, vocab, T, k, p, m, seed, offset, rows=None, min_exact=0.98, workspace="auto"):
+    """Sample on the GPU and check every row against the oracle; returns the tokens.
+    workspace: as for mi_apply_bitmask_sample ("auto" splits a small batch of
+    filtered 16-bit rows over several blocks; None keeps one block per row)."""
     R, cols = bits.shape
     dl = dev_logits(bits, dtype)
     dm = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask)).to("cuda")
@@ -66,7 +68,8 @@ def check_rows(bits, dtype, mask, vocab, T, k, p, m, seed, offset, rows=None, mi
     for name, v, td in (("temperature", T, torch.float32), ("top_k", k, torch.int32),
                         ("top_p", p, torch.float32), ("min_p", m, torch.float32)):
         targs[name] = torch.from_numpy(v).to("cuda", td) if isinstance(v, np.ndarray) else v
-    tok = mb.mi_apply_bitmask_sample(dl, dm, vocab, seed=seed, offset=offset, **targs).cpu().numpy()
+    tok = mb.mi_apply_bitmask_sample(dl, dm, vocab, seed=seed, offset=offset, workspace=workspace,
+                                     **targs).cpu().numpy()
     V = cols if vocab is None and mask is None else (vocab if vocab is not None else
                                                      min(cols, 32 * mask.shape[1]))
     vals = values64(bits, dtype)
@@ -340,9 +343,10 @@ def test_key_holding_65536_tokens(dtype):
     bits[bits == one] = one + 1                                   # only the planted copies hold 0.25
     for r, copies in enumerate((65535, 65536, 66000, 0)):
         bits[r, rng.choice(cols, copies, replace=False)] = one
-    say(f"[gpu] sampler keys holding 65536 tokens {dtype}")
-    for (T, k, p, seed) in ((1.0, 10, 1.0, 1), (1.0, 2000, 1.0, 2), (0.9, 0, 0.6, 3), (1.0, 50, 0.9, 4)):
-        check_rows(bits, dtype, None, None, T, k, p, 0.0, seed=seed, offset=0, min_exact=0.75)
+    for ws in (None, "auto"):    # one block per row (16-bit LDS counters), and split (32-bit counts)
+        say(f"[gpu] sampler keys holding 65536 tokens {dtype} workspace={ws}")
+        for (T, k, p, seed) in ((1.0, 10, 1.0, 1), (1.0, 2000, 1.0, 2), (0.9, 0, 0.6, 3), (1.0, 50, 0.9, 4)):
+            check_rows(bits, dtype, None, None, T, k, p, 0.0, seed=seed, offset=0, min_exact=0.75, workspace=ws)
 
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
@@ -471,8 +475,8 @@ def test_kept_tokens_crowding_one_wave(dtype):
         b = x.view(np.uint32)
         bits = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     say(f"[gpu] sampler kept tokens crowding one wave {dtype}")
-    check_rows(bits, dtype, None, None, 1.0, 0, 0.999, 0.0, seed=41, offset=0, min_exact=0.75)
-    check_rows(bits, dtype, None, None, 1.0, 6000, 1.0, 0.0, seed=42, offset=1, min_exact=0.75)
+    check_rows(bits, dtype, None, None, 1.0, 0, 0.999, 0.0, seed=41, offset=0, min_exact=0.75, workspace=None)
+    check_rows(bits, dtype, None, None, 1.0, 6000, 1.0, 0.0, seed=42, offset=1, min_exact=0.75, workspace=None)
 
 
 @pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
@@ -597,3 +601,105 @@ def test_non_finite_logits_are_not_candidates(dtype):
         tok = check_rows(bits, dtype, mask, None, 0.0, 0, 1.0, 0.0, seed=3, offset=0, min_exact=1.0)
         assert tok[3] == -1
         check_rows(bits, dtype, mask, None, 1.0, 0, 0.8, 0.0, seed=3, offset=1)
+
+
+def both_paths(dl, dm, vocab, **kw):
+    """Tokens with one block per row and with the rows split through a workspace."""
+    one = mb.mi_apply_bitmask_sample(dl, dm, vocab, workspace=None, **kw).cpu().numpy()
+    split = mb.mi_apply_bitmask_sample(dl, dm, vocab, workspace="auto", **kw).cpu().numpy()
+    return one, split
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_split_filtered_rows_equal_one_block_per_row(dtype):
+    """A small batch of filtered 16-bit rows split over several blocks (the
+    workspace) draws the same tokens as one block per row, bit for bit: the
+    cut comes from the same counts and the draw from the same Gumbel keys.
+    Batch sizes 1 to 64, ragged and masked rows, rows with no candidate,
+    heavy ties, every filter alone and together, and per-row parameters that
+    mix greedy, unfiltered and filtered rows in one batch."""
+    rng = np.random.default_rng(67 if dtype == "float16" else 71)
+    shapes = ((1, 128000, None), (3, 50257, None), (16, 32000, 31990), (64, 8192, None), (5, 70003, 70000))
+    modes = (dict(top_k=50), dict(top_p=0.9), dict(min_p=0.05), dict(top_k=50, top_p=0.9, min_p=0.05),
+             dict(top_k=1), dict(top_p=0.0), dict(top_k=1 << 20, top_p=0.999), dict(top_k=3000, temperature=0.5))
+    for R, cols, V in shapes:
+        ties = R in (3, 64)
+        bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([0.5, 2.0, 6.0])), ties=ties)
+        allowed = rng.random((R, cols)) < rng.uniform(0.001, 0.9, (R, 1))
+        if R > 2:
+            allowed[1] = False
+        mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+        dl = dev_logits(bits, dtype)
+        dm = torch.from_numpy(mask).to("cuda")
+        assert mb.sample_workspace_bytes(dl.dtype, R, V or cols) > 0
+        for i, kw in enumerate(modes):
+            say(f"[gpu] split vs one block {dtype} R={R} cols={cols} {kw}")
+            one, split = both_paths(dl, dm, V, seed=5 + i, offset=R, **kw)
+            assert np.array_equal(one, split), (R, cols, kw, np.flatnonzero(one != split)[:8])
+            if R > 2:
+                assert one[1] == -1
+        T = torch.from_numpy(rng.choice([0.0, 0.7, 1.0, 1.3], R).astype(np.float32))
+        k = torch.from_numpy(rng.choice([0, 1, 50, 5000], R).astype(np.int32))
+        p = torch.from_numpy(rng.choice([1.0, 0.9, 0.5], R).astype(np.float32))
+        m = torch.from_numpy(rng.choice([0.0, 0.0, 0.05], R).astype(np.float32))
+        say(f"[gpu] split vs one block {dtype} R={R} cols={cols} per-row parameters")
+        one, split = both_paths(dl, dm, V, temperature=T, top_k=k, top_p=p, min_p=m, seed=99, offset=7)
+        assert np.array_equal(one, split), (R, cols, np.flatnonzero(one != split)[:8])
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_split_filtered_rows_against_the_oracle(dtype):
+    """The split path against the oracle itself: 4 rows of the B=256 bf16
+    shape (or fp16 rows of 32000), with masks, under each filter."""
+    rng = np.random.default_rng(73)
+    R, cols = (4, 128256) if dtype == "bfloat16" else (8, 32000)
+    bits = random_logits(rng, dtype, R, cols)
+    allowed = rng.random((R, cols)) < rng.uniform(0.01, 0.6, (R, 1))
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32 + 1, rng)
+    V = cols - 256 if dtype == "bfloat16" else None
+    for (T, k, p, m, seed) in ((1.0, 50, 1.0, 0.0, 1), (1.0, 0, 0.9, 0.0, 2), (0.8, 0, 1.0, 0.1, 3),
+                               (1.2, 40, 0.95, 0.02, 4)):
+        say(f"[gpu] split path vs oracle {dtype} T={T} k={k} p={p} m={m}")
+        check_rows(bits, dtype, mask, V, T, k, p, m, seed=seed, offset=seed, min_exact=0.9)
+
+
+def test_split_workspace_reused_and_dirty():
+    """An explicit workspace, filled with garbage first, serves two calls in a
+    row, the second with fewer rows: its contents on entry do not matter."""
+    rng = np.random.default_rng(79)
+    bits = random_logits(rng, "bfloat16", 16, 40000)
+    dl = dev_logits(bits, "bfloat16")
+    ws = torch.full((mb.sample_workspace_bytes(torch.bfloat16, 16, 40000),), 0xFF, dtype=torch.uint8, device="cuda")
+    for R in (16, 5):
+        say(f"[gpu] split workspace reused, {R} rows")
+        want = mb.mi_apply_bitmask_sample(dl[:R], None, None, top_k=20, top_p=0.8, seed=3, workspace=None)
+        got = mb.mi_apply_bitmask_sample(dl[:R], None, None, top_k=20, top_p=0.8, seed=3, workspace=ws)
+        assert torch.equal(want, got)
+
+
+def test_split_filtered_rows_in_a_graph():
+    """The split path's five kernels captured in a HIP graph (workspace
+    allocated during capture) replay to the eager tokens three times, with
+    unrelated eager work in between."""
+    rng = np.random.default_rng(83)
+    bits = random_logits(rng, "float16", 8, 32000)
+    dl = dev_logits(bits, "float16")
+    modes = (dict(top_k=50), dict(top_p=0.9, min_p=0.05))
+    want = [mb.mi_apply_bitmask_sample(dl, None, None, seed=11, **kw).cpu() for kw in modes]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        outs = [mb.mi_apply_bitmask_sample(dl, None, None, seed=11, **kw) for kw in modes]   # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = [mb.mi_apply_bitmask_sample(dl, None, None, seed=11, **kw) for kw in modes]
+    for rep in range(3):
+        say(f"[gpu] split path graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(len(modes)):
+            assert torch.equal(outs[k].cpu(), want[k]), (rep, modes[k])
+        (dl.float() * 2).sum().item()
+    del g
