@@ -24,7 +24,8 @@
 //
 //   pass 1   max logit over the candidates and its (lowest) index -> greedy
 //            rows and rows with no candidate end here; skipped when the row
-//            uses neither top-p nor min-p (nothing else needs it);
+//            uses neither top-p nor min-p (nothing else needs it), and for
+//            16-bit rows with top-k or top-p (their key histogram gives it);
 //   16-bit   bf16 and fp16 rows with top-k or top-p, in 1024- or 512-thread
 //            blocks: one pass counts the tokens the mask allows under each
 //            of the 65536 16-bit keys (LDS, 16- or 8-bit counters); the
@@ -50,7 +51,7 @@
 //            Philox4x32-10 (counter (i / 4, row, offset lo, offset hi), key
 //            (seed lo, seed hi), word i % 4; u = (floor(x / 2^9) + 1/2) / 2^23),
 //            ties to the lowest index.  A pass of its own, except where the
-//            last radix pass (fp16, fp32) draws as it counts.  After the
+//            last radix pass (fp32) draws as it counts.  After the
 //            16-bit search the kept test runs on packed 16-bit keys, and a
 //            sparse kept set is first listed in LDS so the generator runs
 //            on the list alone.
@@ -748,7 +749,8 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
 //
 // A batch of a few rows with top-k, top-p or min-p would otherwise keep one
 // compute unit per row busy while the rest idle.  Such rows are instead
-// spread over a caller's workspace in three launches:
+// spread over a caller's workspace in three launches, between split_clear
+// (which zeroes it and the output words) and finish_tokens:
 //   split_hist    one 1024-thread block per segment of a row counts the
 //                 segment's allowed tokens under their 16-bit keys (LDS,
 //                 16-bit counters: a segment holds fewer than 65536 tokens)
