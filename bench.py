@@ -587,8 +587,9 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
 
     Per launch: one token per row from the masked logits.  Bytes counted: one
     read of the logits of every row plus its mask words; the kernel reads the
-    row once per pass (greedy 1, unfiltered 2, with top-k or top-p 2 plus one
-    per radix digit: 2 for bf16, 3 for fp16).  Cold: rotating buffer sets.
+    row once per pass (greedy 1, unfiltered 1; with top-k or top-p, 16-bit
+    rows take 2 -- the key histogram and the draw -- or 1 when a short row is
+    held in registers between them).  Cold: rotating buffer sets.
     """
     import numpy as np
 
