@@ -663,6 +663,25 @@ def test_split_filtered_rows_against_the_oracle(dtype):
         check_rows(bits, dtype, mask, V, T, k, p, m, seed=seed, offset=seed, min_exact=0.9)
 
 
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_split_filtered_long_rows(dtype):
+    """Rows of 2^21 + 5 tokens: the histogram pass needs 33 segments of under
+    65536 tokens each (more than its usual 8 per row), with a ragged last
+    segment.  Split and one-block tokens agree bit for bit, and the split
+    tokens pass the oracle."""
+    rng = np.random.default_rng(89)
+    R, cols = 2, (1 << 21) + 5
+    bits = random_logits(rng, dtype, R, cols)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.4, (cols + 31) // 32, rng)
+    dl = dev_logits(bits, dtype)
+    dm = torch.from_numpy(mask).to("cuda")
+    for i, kw in enumerate((dict(top_k=40), dict(top_p=0.8), dict(top_k=500, top_p=0.95, min_p=0.01))):
+        say(f"[gpu] split long rows {dtype} {kw}")
+        one, split = both_paths(dl, dm, None, seed=21 + i, offset=i, **kw)
+        assert np.array_equal(one, split), (kw, one, split)
+    check_rows(bits, dtype, mask, None, 1.0, 40, 0.8, 0.0, seed=30, offset=0, min_exact=1.0)
+
+
 def test_split_workspace_reused_and_dirty():
     """An explicit workspace, filled with garbage first, serves two calls in a
     row, the second with fewer rows: its contents on entry do not matter."""
