@@ -30,6 +30,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant auto]
        python bench.py --all-configs       (every workload, next to a plain fill)
        python bench.py --copy-calibration  (plain copies, for scaling HBM counters)
        python bench.py --sampler-calls N   (N eager sampler calls per mode, for counters)
+       python bench.py --split-calls N     (N eager small-batch filtered sampler calls, for kernel traces)
 """
 
 from __future__ import annotations
@@ -66,6 +67,10 @@ def parse():
     ap.add_argument("--sampler-calls", type=int, default=0, metavar="N",
                     help="only call the fused sampler N times per mode on its two shapes, eagerly (for hardware "
                          "counters)")
+    ap.add_argument("--split-calls", type=int, default=0, metavar="N",
+                    help="only call the fused sampler N times per case on the first 1 and 16 rows of the B=256 "
+                         "bf16 shape with top-k 50 and top-p 0.9, eagerly, with the workspace that splits filtered "
+                         "rows (for kernel traces)")
     return ap.parse_args()
 
 
@@ -140,6 +145,34 @@ def sampler_calls(n):
                 mb.mi_apply_bitmask_sample(x, m, wl.vocab_size, seed=1, offset=k, out=tok, **kw)
             torch.cuda.synchronize()
             print(json.dumps({"sampler_calls": {"shape": label, "mode": mode, "calls": n}}), flush=True)
+
+
+def split_calls(n):
+    """N eager calls of the fused sampler with its split-row workspace, per case.
+
+    Cases: the first B = 1 and 16 rows of the B=256 bf16 sampler shape, top-k
+    50 and top-p 0.9, in that order.  Each call is five dispatches: the
+    workspace clear, split_hist, split_search, the segmented draw
+    (sample_rows) and the token conversion.
+    """
+    import numpy as np
+    import torch
+
+    import packed_logit_bitmask_amd as mb
+    from packed_logit_bitmask_amd import workloads
+
+    dev = torch.device("cuda:0")
+    wl = workloads.mixed_bf16(n_indices=0)
+    x = torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    m = torch.from_numpy(wl.mask).to(dev)
+    for B in (1, 16):
+        tok = torch.empty(B, dtype=torch.int64, device=dev)
+        ws = torch.empty(mb.sample_workspace_bytes(torch.bfloat16, B, wl.vocab_size), dtype=torch.uint8, device=dev)
+        for mode, kw in (("top_k_50", dict(top_k=50)), ("top_p_0.9", dict(top_p=0.9))):
+            for k in range(n):
+                mb.mi_apply_bitmask_sample(x[:B], m[:B], wl.vocab_size, seed=1, offset=k, out=tok, workspace=ws, **kw)
+            torch.cuda.synchronize()
+            print(json.dumps({"split_calls": {"rows": B, "mode": mode, "calls": n}}), flush=True)
 
 
 def all_configs():
@@ -239,6 +272,9 @@ def main():
         return
     if args.sampler_calls > 0:
         sampler_calls(args.sampler_calls)
+        return
+    if args.split_calls > 0:
+        split_calls(args.split_calls)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU (--gpus 1): the apply has no cross-GPU step, and each GPU of a "
