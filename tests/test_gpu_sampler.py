@@ -648,6 +648,32 @@ def test_split_filtered_rows_equal_one_block_per_row(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_split_fuzz_equal_one_block(dtype):
+    """Seeded random small batches (1 to 64 rows of 8192 to 200 000 tokens,
+    ragged vocab, masks of random density, value spreads with and without
+    heavy ties, per-row parameters mixing every mode): the split path and one
+    block per row draw the same tokens."""
+    rng = np.random.default_rng(97 if dtype == "float16" else 101)
+    for case in range(8):
+        R = int(rng.integers(1, 65))
+        cols = int(rng.integers(8192, 200001))
+        V = int(rng.integers(8192, cols + 1))
+        ties = bool(rng.integers(0, 2))
+        bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([0.3, 2.0, 8.0])), ties=ties)
+        allowed = rng.random((R, cols)) < rng.uniform(0.0, 1.0, (R, 1))
+        mask = workloads.pack_allowed(allowed, (cols + 31) // 32 + int(rng.integers(0, 3)), rng)
+        dl = dev_logits(bits, dtype)
+        dm = torch.from_numpy(mask).to("cuda")
+        T = torch.from_numpy(rng.choice([0.0, 0.5, 1.0, 1.7], R).astype(np.float32))
+        k = torch.from_numpy(rng.choice([0, 1, 5, 50, 400, 100000], R).astype(np.int32))
+        p = torch.from_numpy(rng.choice([1.0, 0.99, 0.9, 0.5, 0.1, 0.0], R).astype(np.float32))
+        m = torch.from_numpy(rng.choice([0.0, 0.0, 0.05, 0.5], R).astype(np.float32))
+        say(f"[gpu] split fuzz {dtype} case {case}: R={R} cols={cols} V={V} ties={ties}")
+        one, split = both_paths(dl, dm, V, temperature=T, top_k=k, top_p=p, min_p=m, seed=300 + case, offset=case)
+        assert np.array_equal(one, split), (case, np.flatnonzero(one != split)[:8])
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_split_filtered_rows_against_the_oracle(dtype):
     """The split path against the oracle itself: 4 rows of the B=256 bf16
     shape (or fp16 rows of 32000), with masks, under each filter."""
