@@ -619,25 +619,32 @@ SAMPLER_MODES = (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperat
 
 
 def sampler_times(torch, dev, mb, workloads, stream, steps=200):
-    """The fused apply + sampler at the two batch/vocab shapes the logits-processor page times.
+    """The fused apply + sampler at the two batch/vocab shapes the logits-processor page times,
+    and the first of them with fp32 logits.
 
     Per launch: one token per row from the masked logits.  Bytes counted: one
     read of the logits of every row plus its mask words; the kernel reads the
     row once per pass (greedy 1, unfiltered 1; with top-k or top-p, 16-bit
     rows take 2 -- the key histogram and the draw -- or 1 when a short row is
-    held in registers between them).  Cold: rotating buffer sets.
+    held in registers between them; fp32 rows take a radix pass per 8-bit
+    digit, 4, plus the maximum for top-p and min-p).  The fp32 shape holds the
+    bf16 shape's values widened.  Cold: rotating buffer sets.
     """
     import numpy as np
 
     out = {}
-    for label, wl in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0)),
-                      ("B1024_V32000_fp16", workloads.verify_fp16())):
+    for label, wl, fp32 in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0), False),
+                            ("B1024_V32000_fp16", workloads.verify_fp16(), False),
+                            ("B256_V128000_fp32", workloads.mixed_bf16(n_indices=0), True)):
         R, V = wl.rows, (wl.vocab_size or wl.cols)
-        nbytes = R * V * (2) + R * ((V + 31) // 32) * 4
-        nsets = max(2, math.ceil(2 * INFINITY_CACHE / (wl.logits.nbytes + wl.mask.nbytes)))
+        esize = 4 if fp32 else 2
+        nbytes = R * V * esize + R * ((V + 31) // 32) * 4
+        nsets = max(2, math.ceil(2 * INFINITY_CACHE / (wl.logits.nbytes * esize // 2 + wl.mask.nbytes)))
         tdt = torch.bfloat16 if wl.dtype == "bfloat16" else torch.float16
-        sets = [(torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(tdt), torch.from_numpy(wl.mask).to(dev))
-                for _ in range(nsets)]
+        sets = []
+        for _ in range(nsets):
+            x = torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(tdt)
+            sets.append((x.float().contiguous() if fp32 else x, torch.from_numpy(wl.mask).to(dev)))
         tok = torch.empty(R, dtype=torch.int64, device=dev)
         res = {}
         for mode, kw in SAMPLER_MODES:
