@@ -673,6 +673,34 @@ def test_split_fuzz_equal_one_block(dtype):
         assert np.array_equal(one, split), (case, np.flatnonzero(one != split)[:8])
 
 
+def test_split_parameter_edges_equal_one_block():
+    """Parameter edges through the split path, against one block per row:
+    an infinite temperature (every filter keeps all), NaN top-p and min-p
+    (disabled), top-p <= 0 and min-p >= 1 (the largest value and its ties),
+    a row with a single candidate and a row with none, per-row parameters
+    in one batch of 8 bf16 rows of 20 000 tokens with heavy ties."""
+    rng = np.random.default_rng(103)
+    R, cols = 8, 20000
+    bits = random_logits(rng, "bfloat16", R, cols, sigma=1.0, ties=True)
+    allowed = rng.random((R, cols)) < 0.5
+    allowed[6] = False
+    allowed[6, 12345] = True          # one candidate
+    allowed[7] = False                # none
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    dl = dev_logits(bits, "bfloat16")
+    dm = torch.from_numpy(mask).to("cuda")
+    inf, nan = float("inf"), float("nan")
+    T = torch.tensor([inf, 1.0, 1.0, 1.0, 0.7, 1.3, 1.0, 1.0], dtype=torch.float32)
+    k = torch.tensor([10, 0, 0, 0, 3, 0, 5, 5], dtype=torch.int32)
+    p = torch.tensor([0.5, nan, 0.0, -1.0, 1.0, 0.9, 0.9, 0.9], dtype=torch.float32)
+    m = torch.tensor([0.1, nan, 0.0, 0.0, 1.0, 2.0, 0.0, 0.0], dtype=torch.float32)
+    for seed in (1, 2, 3):
+        say(f"[gpu] split parameter edges seed {seed}")
+        one, split = both_paths(dl, dm, None, temperature=T, top_k=k, top_p=p, min_p=m, seed=seed, offset=seed)
+        assert np.array_equal(one, split), (seed, one, split)
+        assert split[6] == 12345 and split[7] == -1
+
+
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_split_filtered_rows_against_the_oracle(dtype):
     """The split path against the oracle itself: 4 rows of the B=256 bf16
