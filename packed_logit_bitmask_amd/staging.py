@@ -18,6 +18,10 @@ with HIP streams and events:
   record when it was enqueued, so the next upload into that device buffer
   waits for it.
 
+A device-side wait costs the GPU a few microseconds even when the event has
+long completed, so each wait is skipped when the host already sees the event
+complete (the ordering it would enforce then already holds).
+
 The apply itself is the library's kernel; this class only moves the mask.
 """
 
@@ -59,7 +63,7 @@ class MaskStager:
         if k < 0:
             raise RuntimeError("upload() before host(): fill the buffer host() returns first")
         with torch.cuda.stream(self.copy_stream):
-            if self.consumed[k] is not None:
+            if self.consumed[k] is not None and not self.consumed[k].query():
                 self.copy_stream.wait_event(self.consumed[k])   # do not overwrite a mask still being applied
             self.devs[k].copy_(self.hosts[k], non_blocking=True)
             ev = torch.cuda.Event()
@@ -71,7 +75,8 @@ class MaskStager:
         if k < 0 or self.copied[k] is None:
             raise RuntimeError("apply before upload(): the current slot holds no mask yet")
         s = stream or torch.cuda.current_stream(self.device)
-        s.wait_event(self.copied[k])          # device-side wait for this slot's upload
+        if not self.copied[k].query():
+            s.wait_event(self.copied[k])      # device-side wait for this slot's upload
         return k, s
 
     def _done(self, k, s):
