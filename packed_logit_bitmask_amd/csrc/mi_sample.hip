@@ -174,8 +174,11 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
     const bool fine8 = fine && n > kFine16Rows && V <= kFine8Vocab;
     const bool deep = (n <= 256 || fine) && nseg == 1;
     const int threads = fine8 ? 512 : deep ? 1024 : 256;
-    const size_t lds = fine && nseg == 1 ? std::max(mi::sample_fine_bytes(threads), mi::sample_hist_bytes(threads))
-                                         : (may_filter ? mi::sample_hist_bytes(threads) : 0);
+    // the 16-bit counters: filtered 16-bit rows, and fp32 rows in 1024-thread
+    // blocks (their top-k passes; see fp32_topk_cut)
+    const bool fine_lds = may_filter && nseg == 1 && (fine || threads == 1024);
+    const size_t lds = fine_lds ? std::max(mi::sample_fine_bytes(threads), mi::sample_hist_bytes(threads))
+                                : (may_filter ? mi::sample_hist_bytes(threads) : 0);
     const mi::SplitInfo* sinfo = nullptr;
     if (split_filtered && nseg > 1) {
       // the histogram pass: segments of a multiple of 256 tokens, fewer than

@@ -32,6 +32,9 @@
 //            maximum and both cuts follow from the counts (fine_search).
 //            The radix passes below remain for fp32 and for a row where one
 //            key holds more tokens than its counter can (65536 or 256);
+//   fp32 k   fp32 rows with top-k alone, in 1024-thread blocks: two passes
+//            of 16-bit keys, the top half of each order key and then the low
+//            half inside the bucket holding the cut (fp32_topk_cut);
 //   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
@@ -745,6 +748,160 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   return true;
 }
 
+// ---- fp32 rows with top-k alone: the cut from two passes of 16-bit keys.
+//
+// Four radix passes would each do the same work per token.  Instead the first
+// pass counts every candidate under the top 16 bits of its order key (a
+// bucket of bf16 width; counts per bucket are exact), a search finds the
+// bucket holding the k-th largest candidate, and a second pass counts only
+// that bucket's candidates, under the low 16 bits of their keys, which gives
+// the exact key of the k-th largest.  Both passes use the 65536 16-bit
+// counters of the 16-bit search (LDS, two per word, a spare word per lane).
+
+// One pass over an fp32 row counting candidates (mask bit set, finite) into
+// `fine` from a cleared start: key_of(order key) is the 16-bit key a
+// candidate counts under, or ~0u when it does not count.  With SPARSE unset
+// a token that does not count adds to its lane's spare word, so the add needs
+// no branch; with SPARSE set (few tokens count) it adds nothing, and a wave
+// none of whose lanes counts skips the add.  Returns this thread's number of
+// counted tokens; ends with a barrier.
+template <int THREADS, bool SPARSE, typename K>
+__device__ __forceinline__ uint32_t count_keys32(const RowView<F32Bits>& rv, uint32_t* fine, K&& key_of) {
+  constexpr uint32_t kWords = 32768;
+  const int t = static_cast<int>(threadIdx.x);
+  uint4* f4 = reinterpret_cast<uint4*>(fine);
+  for (int i = t; i < static_cast<int>(kWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  uint32_t counted = 0;
+  const uint32_t spare = 2u * (kWords + static_cast<uint32_t>(lane_id()));
+  const auto add = [&](uint32_t x, bool candidate) {
+    const uint32_t key = order_key(__uint_as_float(x));
+    const uint32_t k = candidate && finite_key(key) ? key_of(key) : ~0u;
+    counted += k != ~0u ? 1u : 0u;
+    if constexpr (SPARSE) {
+      if (k != ~0u) atomicAdd(&fine[k >> 1], 1u << ((k & 1u) << 4));
+    } else {
+      const uint32_t kk = k != ~0u ? k : spare;
+      atomicAdd(&fine[kk >> 1], 1u << ((kk & 1u) << 4));
+    }
+  };
+  walk_row_raw<128, THREADS>(rv, [&](int32_t g, const typename RowView<F32Bits>::Raw& raw, bool full) {
+    const uint32_t bits = rv.mask_bits(raw, g, full);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) add(raw.v[q], (bits >> q) & 1u);
+  });
+  if ((rv.V & 7) && t == 0) {  // the partial last group, by plain loads
+    for (int32_t i = rv.V & ~7; i < rv.V; ++i)
+      add(rv.row[i], rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u);
+  }
+  __syncthreads();
+  return counted;
+}
+
+// Over the 65536 16-bit counters of `fine` (key k in half k & 1 of word
+// k / 2), the largest key whose suffix count (the counts of the keys at and
+// above it) reaches `need`, 1 <= need <= the total; *above gets the count of
+// the keys above it.  All 1024 threads of the block; thread t holds keys
+// [64t, 64t + 64), and wave 0 takes the crossing thread's keys one per lane.
+// Ends with a barrier.
+template <int THREADS>
+__device__ __forceinline__ uint32_t count_search(const uint32_t* fine, uint32_t need, uint32_t* above) {
+  static_assert(THREADS == 1024, "thread t holds keys [64t, 64t + 64)");
+  constexpr int kWaves = THREADS / 64;
+  __shared__ uint32_t s_c[kWaves], s_cross, s_above_t, s_key, s_above;
+  const int t = static_cast<int>(threadIdx.x);
+  const int lane = lane_id(), wave = t >> 6;
+  uint32_t c = 0;
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t w = fine[32 * t + ((j + t) & 31)];  // rotated: a wave's lanes read different banks
+    c += (w & 0xFFFFu) + (w >> 16);
+  }
+  uint32_t sc = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = static_cast<uint32_t>(__shfl_down(static_cast<int>(sc), o));
+    if (lane + o < 64) sc += v;
+  }
+  if (lane == 0) s_c[wave] = sc;
+  __syncthreads();
+  for (int w = wave + 1; w < kWaves; ++w) sc += s_c[w];
+  if (sc >= need && sc - c < need) {  // exactly one thread: sc falls with t
+    s_cross = static_cast<uint32_t>(t);
+    s_above_t = sc - c;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t kx = 64u * s_cross + static_cast<uint32_t>(lane);
+    const uint32_t n = (fine[kx >> 1] >> ((kx & 1u) << 4)) & 0xFFFFu;
+    uint32_t v = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = static_cast<uint32_t>(__shfl_down(static_cast<int>(v), o));
+      if (lane + o < 64) v += u;
+    }
+    const uint32_t total = v + s_above_t;  // the counts of the keys at and above kx
+    const uint64_t hit = __ballot(total >= need);
+    const int L = 63 - __clzll(static_cast<long long>(hit));
+    if (lane == L) {
+      s_key = kx;
+      s_above = total - n;
+    }
+  }
+  __syncthreads();
+  *above = s_above;
+  return s_key;
+}
+
+// The top-k cut of an fp32 row (an order key: keep the candidates at or
+// above it; 0 keeps every one) from the two 16-bit passes.  Returns false
+// when a bucket holds 65536 candidates or more (its 16-bit counter wraps and
+// the counts fall short): the radix search then takes over.  `fine` holds
+// at least 32832 words.
+template <int THREADS>
+__device__ __forceinline__ bool fp32_topk_cut(const RowView<F32Bits>& rv, uint32_t* fine, int32_t top_k,
+                                              uint32_t* cut) {
+  constexpr int kWaves = THREADS / 64;
+  __shared__ uint32_t s_n[kWaves], s_all[kWaves];
+  const int t = static_cast<int>(threadIdx.x);
+  const int lane = lane_id(), wave = t >> 6;
+  uint32_t counted = count_keys32<THREADS, false>(rv, fine, [](uint32_t key) { return key >> 16; });
+  uint32_t all = 0;
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t w = fine[32 * t + ((j + t) & 31)];
+    all += (w & 0xFFFFu) + (w >> 16);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    counted += static_cast<uint32_t>(__shfl_xor(static_cast<int>(counted), o));
+    all += static_cast<uint32_t>(__shfl_xor(static_cast<int>(all), o));
+  }
+  if (lane == 0) {
+    s_n[wave] = counted;
+    s_all[wave] = all;
+  }
+  __syncthreads();
+  uint32_t tot = 0, tot_all = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    tot += s_n[w];
+    tot_all += s_all[w];
+  }
+  if (tot_all != tot) return false;  // a bucket's counter wrapped
+  const uint32_t need = static_cast<uint32_t>(top_k);
+  if (need > tot) {  // k at or above the candidates (or none): keep every one
+    *cut = 0u;
+    return true;
+  }
+  uint32_t above;
+  const uint32_t bucket = count_search<THREADS>(fine, need, &above);
+  // the bucket's candidates under the low 16 bits of their keys
+  count_keys32<THREADS, true>(rv, fine,
+                              [bucket](uint32_t key) { return (key >> 16) == bucket ? (key & 0xFFFFu) : ~0u; });
+  uint32_t above_low;
+  const uint32_t low = count_search<THREADS>(fine, need - above, &above_low);
+  *cut = (bucket << 16) | low;
+  return true;
+}
+
 // ---- Filtered 16-bit rows split over several blocks (few rows).
 //
 // A batch of a few rows with top-k, top-p or min-p would otherwise keep one
@@ -1259,6 +1416,13 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // histogram search covers the rest), and a separate draw keeps the
   // kernel's register count down for the common path.
   constexpr bool kFuseDraw = sizeof(typename D::Bits) == 4;
+  // fp32 rows with top-k alone (min-p aside), in 1024-thread blocks (whose
+  // LDS then holds the 16-bit counters): two 16-bit passes instead of the
+  // radix passes
+  if constexpr (sizeof(typename D::Bits) == 4 && THREADS == 1024) {
+    if (use_k && !use_p && !have_cut)
+      have_cut = fp32_topk_cut<THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), top_k, &cut);
+  }
   if ((use_k || use_p) && !have_cut) {
     // ---- top-k and top-p cuts: radix passes over 8-bit digits of the key,
     // high to low, both searches in the same passes.  The first mass

@@ -418,6 +418,49 @@ def test_kept_tokens_crowding_one_wave_many_rows(dtype):
     check_rows(bits, dtype, None, None, 1.0, 0, 0.999, 0.0, seed=62, offset=2, rows=rows, min_exact=0.75)
 
 
+def test_fp32_top_k_two_pass_cut():
+    """fp32 rows with top-k alone take the cut from two 16-bit passes (the
+    top 16 bits of each key, then the low 16 bits inside the bucket holding
+    the k-th largest).  Rows whose cut falls among 5000 distinct values that
+    share one bf16-width bucket (1 + i * 2^-21), next to random logits; k
+    above, at and inside the crowded bucket; a row with ties at the cut; and
+    with min-p and a mask.  Against the oracle."""
+    rng = np.random.default_rng(107)
+    R, cols = 6, 40000
+    x = rng.standard_normal((R, cols)).astype(np.float32)
+    x[x >= 1.0] -= np.float32(2.0)                                    # nothing random at or above 1
+    for r in range(R):
+        pos = rng.choice(cols, 5000, replace=False)
+        x[r, pos] = np.float32(1.0) + np.arange(5000, dtype=np.float32) * np.float32(2.0 ** -21)
+    x[5, rng.choice(cols, 300, replace=False)] = np.float32(1.0) + np.float32(2000 * 2.0 ** -21)  # ties at a cut
+    bits = x.view(np.uint32)
+    allowed = rng.random((R, cols)) < 0.9
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    for (k, m, seed) in ((1, 0.0, 1), (10, 0.0, 2), (2500, 0.0, 3), (4600, 0.0, 4), (6000, 0.0, 5),
+                         (3000, 0.02, 6), (40000, 0.0, 7)):
+        say(f"[gpu] fp32 two-pass top-k k={k} min_p={m}")
+        check_rows(bits, "float32", mask, None, 1.0, k, 1.0, m, seed=seed, offset=k, min_exact=0.9)
+        check_rows(bits, "float32", None, None, 0.8, k, 1.0, m, seed=seed, offset=k + 1, min_exact=0.9)
+
+
+def test_fp32_top_k_bucket_holding_65536_tokens():
+    """A bf16-width bucket of an fp32 row holding 65535, 65536 or 66000
+    candidates: its 16-bit counter would wrap at 65536, and the row then takes
+    the radix search.  Distinct values inside the bucket, top-k cuts inside
+    and above it."""
+    rng = np.random.default_rng(109)
+    R, cols = 3, 70003
+    x = rng.standard_normal((R, cols)).astype(np.float32) - np.float32(3.0)
+    x[x >= 1.0] = np.float32(0.5)
+    for r, copies in enumerate((65535, 65536, 66000)):
+        pos = rng.choice(cols, copies, replace=False)
+        x[r, pos] = np.float32(1.0) + (np.arange(copies) % 4096).astype(np.float32) * np.float32(2.0 ** -20)
+    bits = x.view(np.uint32)
+    for (k, seed) in ((10, 1), (30000, 2), (65600, 3)):
+        say(f"[gpu] fp32 bucket holding 65536 tokens k={k}")
+        check_rows(bits, "float32", None, None, 1.0, k, 1.0, 0.0, seed=seed, offset=0, min_exact=0.9)
+
+
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_short_rows_with_filters(dtype):
     """16-bit rows shorter than one 8-token group, or with a ragged last
