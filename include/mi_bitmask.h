@@ -197,11 +197,11 @@ mi_status_t mi_apply_bitmask_out_ex(
  * entries, or NULL to use the matching *_all value for every row.
  * tokens: device int64 [rows] output (8-byte aligned; may not overlap logits
  * or mask).  Asynchronous on `stream` like the apply calls.  It uses no
- * device memory beyond its arguments: its working space is on chip (for
- * bf16 and fp16 rows with top-k or top-p, an LDS histogram of 131 KB per
- * 1024-thread block, one block per compute unit, or, with more than 256
- * rows of at most 65536 tokens, of 66 KB per 512-thread block, two blocks
- * per compute unit).  With few rows and no
+ * device memory beyond its arguments: its working space is on chip (when
+ * a row may use top-k or top-p, an LDS histogram of 131 KB per 1024-thread
+ * block, one block per compute unit, or, for bf16 and fp16 batches of more
+ * than 256 rows of at most 65536 tokens, of 66 KB per 512-thread block, two
+ * blocks per compute unit).  With few rows and no
  * top-k, top-p or min-p it splits each row over several blocks that merge
  * their answers in `tokens` itself (three kernels on `stream`; `tokens`
  * holds intermediate values until the last one has run).
