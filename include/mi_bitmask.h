@@ -82,9 +82,9 @@ typedef enum mi_status {
     MI_ERR_BAD_VOCAB = 4,      /* vocab_size < -1 or above min(cols, 32 * mask_cols) */
     MI_ERR_BAD_INDICES = 5,    /* num_indices < 0 or too large */
     MI_ERR_ALIAS = 6,          /* an output overlaps an input it must not overlap */
-    MI_ERR_MISALIGNED = 7,     /* a pointer is not aligned to its element size */
-    MI_ERR_BAD_VARIANT = 8,    /* unknown variant, or one the operation does not have */
-    MI_ERR_HIP = 9             /* the HIP runtime refused the launch */
+    MI_ERR_HIP = 7,            /* the HIP runtime refused the launch */
+    MI_ERR_MISALIGNED = 8,     /* a pointer is not aligned to its element size */
+    MI_ERR_BAD_VARIANT = 9     /* unknown variant, or one the operation does not have */
 } mi_status_t;
 
 /* Kernel variants (the *_ex entry points).  All give bit-identical results. */

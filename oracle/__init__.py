@@ -152,7 +152,12 @@ def get_bitmask_value(bitmask, i: int, j: int) -> int:
 # ----------------------------------------------------------------------------
 
 def apply_inplace_loops(logits: list, bitmask, vocab_size: int, rows_to_apply, fill: int) -> None:
-    """The page's loop over Python lists; ``logits`` is a list of row lists."""
+    """XGrammar "Bitmask Operations", apply_token_bitmask_inplace, Notes: Indices.
+
+    The double loop that page gives as the operation's definition, kept in
+    its literal form over Python lists (``logits`` is a list of row lists):
+    the oracle's rule for this op is to follow that loop as written.
+    """
     for i in rows_to_apply:
         for j in range(vocab_size):
             if get_bitmask_value(bitmask, i, j) == 0:

@@ -80,9 +80,13 @@ def philox4x32(c0, c1, c2, c3, k0, k1, rounds: int = 10):
     return c0, c1, c2, c3
 
 
-def uniforms(seed: int, offset: int, row: int, n: int) -> np.ndarray:
-    """float64 u in (0, 1) for tokens 0..n-1 of one row (exact binary32 values)."""
-    i = np.arange(n, dtype=np.uint64)
+def uniforms(seed: int, offset: int, row: int, n: int, first: int = 0) -> np.ndarray:
+    """float64 u in (0, 1) for tokens first..first+n-1 of one row (exact binary32 values).
+
+    Token i takes word i % 4 of the block for counter (i // 4, row, offset
+    low, offset high) under key (seed low, seed high).
+    """
+    i = np.arange(first, first + n, dtype=np.uint64)
     words = philox4x32(i >> np.uint64(2), np.uint64(row), np.uint64(offset & MASK32),
                        np.uint64((offset >> 32) & MASK32), np.uint64(seed & MASK32),
                        np.uint64((seed >> 32) & MASK32))

@@ -18,7 +18,7 @@ LIBRARY = PKG / "libmi_bitmask.so"
 
 MI_DTYPE = {"float32": 0, "float16": 1, "bfloat16": 2}
 STATUS = ["MI_OK", "MI_ERR_NULL_POINTER", "MI_ERR_BAD_DTYPE", "MI_ERR_BAD_SHAPE", "MI_ERR_BAD_VOCAB",
-          "MI_ERR_BAD_INDICES", "MI_ERR_ALIAS", "MI_ERR_MISALIGNED", "MI_ERR_BAD_VARIANT", "MI_ERR_HIP"]
+          "MI_ERR_BAD_INDICES", "MI_ERR_ALIAS", "MI_ERR_HIP", "MI_ERR_MISALIGNED", "MI_ERR_BAD_VARIANT"]
 VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3, "vec_resident": 4}
 
 # every symbol include/mi_bitmask.h declares
@@ -163,6 +163,21 @@ def _stream_handle(device, stream) -> int:
     return s.cuda_stream
 
 
+def _on(stream):
+    """The context every device entry point runs its marshalling in.
+
+    With an explicit ``stream``, the helper tensors a call makes (index,
+    gate and per-row parameter casts, the outputs and the workspace it
+    allocates) are made on that stream: their copies are enqueued there,
+    ahead of the library's kernels, and the allocator ties their memory to
+    that stream, so it is never handed out again while the kernels may still
+    use it.  The caller's own tensors must be ready on ``stream``, as for any
+    call that takes one.
+    """
+    import contextlib
+    return contextlib.nullcontext() if stream is None else _torch().cuda.stream(stream)
+
+
 def _indices_arg(indices, device, limit: int):
     """(pointer, count, keepalive) for an index list or int tensor."""
     torch = _torch()
@@ -189,14 +204,6 @@ def _indices_arg(indices, device, limit: int):
 _EMPTY_LIST_PTR = 256
 
 
-def _keep_alive(t, stream) -> None:
-    # An index tensor made here belongs to torch's current stream; when the
-    # kernel runs on another stream, tell the allocator so the memory is not
-    # reused before that stream is done with it.
-    if t is not None and stream is not None and t.numel():
-        t.record_stream(stream)
-
-
 def _check_mask(mask, device):
     torch = _torch()
     if not isinstance(mask, torch.Tensor) or mask.dtype != torch.int32:
@@ -220,16 +227,17 @@ def mi_apply_bitmask_inplace(logits, mask, vocab_size: Optional[int] = None,
     lib = load_library()
     L = _as_rows(logits, "logits")
     M = _check_mask(mask, logits.device)
-    ip, n, keep = _indices_arg(indices, logits.device, min(L.shape[0], M.shape[0]))
-    args = (L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
-            M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
-            -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value))
-    st = _stream_handle(logits.device, stream)
-    _keep_alive(keep, stream)
-    if variant == "auto":
-        check(lib.mi_apply_bitmask_inplace(*args, st))
-    else:
-        check(lib.mi_apply_bitmask_inplace_ex(*args, VARIANT[variant], st))
+    with _on(stream):
+        ip, n, keep = _indices_arg(indices, logits.device, min(L.shape[0], M.shape[0]))
+        args = (L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
+                M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
+                -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value))
+        st = _stream_handle(logits.device, stream)
+        if variant == "auto":
+            check(lib.mi_apply_bitmask_inplace(*args, st))
+        else:
+            check(lib.mi_apply_bitmask_inplace_ex(*args, VARIANT[variant], st))
+    del keep
     return logits
 
 
@@ -249,19 +257,19 @@ def mi_apply_bitmask_rows(logits, mask, row_needs_mask=None, vocab_size: Optiona
     lib = load_library()
     L = _as_rows(logits, "logits")
     M = _check_mask(mask, logits.device)
-    gate = None
-    if row_needs_mask is not None:
-        gate = row_needs_mask.reshape(-1)
-        if gate.numel() != L.shape[0]:
-            raise ValueError(f"row_needs_mask has {gate.numel()} entries for {L.shape[0]} rows")
-        gate = gate.to(device=logits.device, dtype=torch.int8).contiguous()
-    out = torch.empty(L.shape[0], dtype=torch.uint8, device=logits.device) if report else None
-    _keep_alive(gate, stream)
-    check(lib.mi_apply_bitmask_rows(
-        L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
-        M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M), -1 if vocab_size is None else int(vocab_size),
-        None if gate is None else gate.data_ptr(), None if out is None else out.data_ptr(), float(fill_value),
-        _stream_handle(logits.device, stream)))
+    with _on(stream):
+        gate = None
+        if row_needs_mask is not None:
+            gate = row_needs_mask.reshape(-1)
+            if gate.numel() != L.shape[0]:
+                raise ValueError(f"row_needs_mask has {gate.numel()} entries for {L.shape[0]} rows")
+            gate = gate.to(device=logits.device, dtype=torch.int8).contiguous()
+        out = torch.empty(L.shape[0], dtype=torch.uint8, device=logits.device) if report else None
+        check(lib.mi_apply_bitmask_rows(
+            L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1], _row_stride(L),
+            M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M), -1 if vocab_size is None else int(vocab_size),
+            None if gate is None else gate.data_ptr(), None if out is None else out.data_ptr(), float(fill_value),
+            _stream_handle(logits.device, stream)))
     return out
 
 
@@ -285,71 +293,85 @@ def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None,
     least ``sample_workspace_bytes`` bytes; calls sharing it must not overlap).
     """
     torch = _torch()
-    if not logits.is_cuda:
-        raise ValueError("logits must be on the GPU")
     lib = load_library()
-    L = _as_rows(logits, "logits")
-    rows = L.shape[0]
-    keep = []
+    with _on(stream):
+        c = _SampleCall(logits, mask, vocab_size, temperature, top_k, top_p, min_p, seed, offset, out)
+        wp, wn = None, 0
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a device tensor')
+            need = lib.mi_sample_workspace_bytes(c.dt, c.rows, c.vocab)
+            if need > 0 and c.may_filter:
+                ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+                c.keep.append(ws)
+                wp, wn = ws.data_ptr(), need
+        elif workspace is not None:
+            if (not isinstance(workspace, torch.Tensor) or workspace.device != logits.device
+                    or not workspace.is_contiguous()):
+                raise ValueError("workspace must be a contiguous tensor on the logits' GPU")
+            wp, wn = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        check(lib.mi_apply_bitmask_sample_ws(*c.head(), wp, wn, _stream_handle(logits.device, stream)))
+    return c.out
 
-    def per_row(v, dtype, name):
-        """(device pointer, 0) for a per-row tensor, (None, v) for a scalar."""
-        if isinstance(v, torch.Tensor):
-            t = v.reshape(-1).to(device=logits.device, dtype=dtype).contiguous()
-            if t.numel() != rows:
-                raise ValueError(f"{name} has {t.numel()} entries for {rows} rows")
-            keep.append(t)
-            return t.data_ptr(), 0
-        return None, v
 
-    prm = SampleParams()
-    prm.temperature, v = per_row(temperature, torch.float32, "temperature")
-    prm.temperature_all = float(v)
-    prm.top_k, v = per_row(top_k, torch.int32, "top_k")
-    prm.top_k_all = int(v)
-    prm.top_p, v = per_row(top_p, torch.float32, "top_p")
-    prm.top_p_all = float(v)
-    prm.min_p, v = per_row(min_p, torch.float32, "min_p")
-    prm.min_p_all = float(v)
-    prm.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
-    prm.offset = int(offset) & 0xFFFFFFFFFFFFFFFF
-    if out is None:
-        out = torch.empty(rows, dtype=torch.int64, device=logits.device)
-    if (out.dtype != torch.int64 or out.numel() != rows or not out.is_contiguous()
-            or out.device != logits.device):
-        raise ValueError("out must be a contiguous int64 tensor with one entry per row, on the logits' GPU")
-    if mask is not None:
-        M = _check_mask(mask, logits.device)
-        mp, mr, mc, ms = M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M)
-    else:
-        mp, mr, mc, ms = None, 0, 0, 0
-    dt = MI_DTYPE[_dtype_name(L)]
-    wp, wn = None, 0
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError('workspace must be "auto", None or a device tensor')
-        if vocab_size is not None:
-            V = int(vocab_size)
-        else:
-            V = L.shape[1] if mask is None else min(L.shape[1], 32 * mc)
-        need = lib.mi_sample_workspace_bytes(dt, rows, max(V, 0))
-        may_filter = any(isinstance(v, torch.Tensor) for v in (top_k, top_p, min_p)) or (
+class _SampleCall:
+    """The marshalled arguments of one sampler call (run inside ``_on``)."""
+
+    def __init__(self, logits, mask, vocab_size, temperature, top_k, top_p, min_p, seed, offset, out):
+        torch = _torch()
+        if not logits.is_cuda:
+            raise ValueError("logits must be on the GPU")
+        self.L = L = _as_rows(logits, "logits")
+        self.rows = rows = L.shape[0]
+        self.keep = []
+
+        def per_row(v, dtype, name):
+            """(device pointer, 0) for a per-row tensor, (None, v) for a scalar."""
+            if isinstance(v, torch.Tensor):
+                t = v.reshape(-1).to(device=logits.device, dtype=dtype).contiguous()
+                if t.numel() != rows:
+                    raise ValueError(f"{name} has {t.numel()} entries for {rows} rows")
+                self.keep.append(t)
+                return t.data_ptr(), 0
+            return None, v
+
+        prm = self.prm = SampleParams()
+        prm.temperature, v = per_row(temperature, torch.float32, "temperature")
+        prm.temperature_all = float(v)
+        prm.top_k, v = per_row(top_k, torch.int32, "top_k")
+        prm.top_k_all = int(v)
+        prm.top_p, v = per_row(top_p, torch.float32, "top_p")
+        prm.top_p_all = float(v)
+        prm.min_p, v = per_row(min_p, torch.float32, "min_p")
+        prm.min_p_all = float(v)
+        prm.seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        prm.offset = int(offset) & 0xFFFFFFFFFFFFFFFF
+        self.may_filter = any(isinstance(v, torch.Tensor) for v in (top_k, top_p, min_p)) or (
             int(top_k) > 0 or float(top_p) < 1.0 or float(min_p) > 0.0)
-        if need > 0 and may_filter:
-            ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
-            keep.append(ws)
-            wp, wn = ws.data_ptr(), need
-    elif workspace is not None:
-        if not isinstance(workspace, torch.Tensor) or workspace.device != logits.device or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on the logits' GPU")
-        wp, wn = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    for t in keep:
-        _keep_alive(t, stream)
-    check(lib.mi_apply_bitmask_sample_ws(
-        L.data_ptr(), dt, rows, L.shape[1], _row_stride(L), mp, mr, mc, ms,
-        -1 if vocab_size is None else int(vocab_size), ctypes.byref(prm), out.data_ptr(), wp, wn,
-        _stream_handle(logits.device, stream)))
-    return out
+        if out is None:
+            out = torch.empty(rows, dtype=torch.int64, device=logits.device)
+        if (out.dtype != torch.int64 or out.numel() != rows or not out.is_contiguous()
+                or out.device != logits.device):
+            raise ValueError("out must be a contiguous int64 tensor with one entry per row, on the logits' GPU")
+        self.out = out
+        self.vocab_arg = -1 if vocab_size is None else int(vocab_size)
+        if mask is not None:
+            M = _check_mask(mask, logits.device)
+            self.m = (M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M))
+            # the apply's vocab-size rule, from the library
+            self.vocab = resolve_vocab_size(L.shape[1], M.shape[1], vocab_size)
+        else:
+            self.m = (None, 0, 0, 0)
+            # without a mask every token below the given vocab size (else the
+            # row width) takes part; the call itself rejects a bad value
+            self.vocab = L.shape[1] if vocab_size is None else max(int(vocab_size), 0)
+        self.dt = MI_DTYPE[_dtype_name(L)]
+
+    def head(self):
+        """The arguments every sampler entry point starts with, up to ``tokens``."""
+        L = self.L
+        return (L.data_ptr(), self.dt, self.rows, L.shape[1], _row_stride(L), *self.m, self.vocab_arg,
+                ctypes.byref(self.prm), self.out.data_ptr())
 
 
 def sample_workspace_bytes(dtype, rows: int, vocab: int) -> int:
@@ -374,23 +396,24 @@ def mi_apply_bitmask_out(logits, mask, out=None, vocab_size: Optional[int] = Non
     if not logits.is_cuda:
         raise ValueError("logits must be on the GPU (the library has no CPU path)")
     lib = load_library()
-    if out is None:
-        out = torch.empty_like(logits, memory_format=torch.contiguous_format)
-    if out.dtype != logits.dtype or out.shape != logits.shape or out.device != logits.device:
-        raise ValueError("out must match logits in dtype, shape and device")
-    L = _as_rows(logits, "logits")
-    O = _as_rows(out, "out")
-    M = _check_mask(mask, logits.device)
-    ip, n, keep = _indices_arg(indices, logits.device, min(L.shape[0], M.shape[0]))
-    args = (O.data_ptr(), _row_stride(O), L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1],
-            _row_stride(L), M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
-            -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value))
-    st = _stream_handle(logits.device, stream)
-    _keep_alive(keep, stream)
-    if variant == "auto":
-        check(lib.mi_apply_bitmask_out(*args, st))
-    else:
-        check(lib.mi_apply_bitmask_out_ex(*args, VARIANT[variant], st))
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(logits, memory_format=torch.contiguous_format)
+        if out.dtype != logits.dtype or out.shape != logits.shape or out.device != logits.device:
+            raise ValueError("out must match logits in dtype, shape and device")
+        L = _as_rows(logits, "logits")
+        O = _as_rows(out, "out")
+        M = _check_mask(mask, logits.device)
+        ip, n, keep = _indices_arg(indices, logits.device, min(L.shape[0], M.shape[0]))
+        args = (O.data_ptr(), _row_stride(O), L.data_ptr(), MI_DTYPE[_dtype_name(L)], L.shape[0], L.shape[1],
+                _row_stride(L), M.data_ptr(), M.shape[0], M.shape[1], _row_stride(M),
+                -1 if vocab_size is None else int(vocab_size), ip, n, float(fill_value))
+        st = _stream_handle(logits.device, stream)
+        if variant == "auto":
+            check(lib.mi_apply_bitmask_out(*args, st))
+        else:
+            check(lib.mi_apply_bitmask_out_ex(*args, VARIANT[variant], st))
+    del keep
     return out
 
 

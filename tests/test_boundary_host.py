@@ -19,7 +19,7 @@ from packed_logit_bitmask_amd import _binding
 
 HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "mi_bitmask.h"
 
-OK, NULLP, DTYPE, SHAPE, VOCAB, INDICES, ALIAS, MISALIGNED, VARIANT, HIP = range(10)
+OK, NULLP, DTYPE, SHAPE, VOCAB, INDICES, ALIAS, HIP, MISALIGNED, VARIANT = range(10)
 
 LOGITS = 0x7F0000000000
 MASK = 0x7F1000000000
@@ -50,6 +50,19 @@ def test_status_strings():
     for code, name in enumerate(_binding.STATUS):
         assert lib.mi_status_string(code).decode() == name
     assert lib.mi_status_string(99).decode() == "MI_ERR_UNKNOWN"
+
+
+def test_status_values_match_header():
+    """The binding's status names sit at the values the header gives them,
+    and the first eight are the boundary's list in its order (MI_ERR_HIP = 7),
+    with the two codes added later after it."""
+    text = HEADER.read_text()
+    body = text[text.index("typedef enum mi_status"):]
+    body = body[:body.index("} mi_status_t;")]
+    values = {m.group(1): int(m.group(2)) for m in re.finditer(r"(MI_\w+)\s*=\s*(\d+)", body)}
+    assert values == {name: code for code, name in enumerate(_binding.STATUS)}
+    assert _binding.STATUS[:8] == ["MI_OK", "MI_ERR_NULL_POINTER", "MI_ERR_BAD_DTYPE", "MI_ERR_BAD_SHAPE",
+                                   "MI_ERR_BAD_VOCAB", "MI_ERR_BAD_INDICES", "MI_ERR_ALIAS", "MI_ERR_HIP"]
 
 
 @pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])

@@ -181,14 +181,26 @@ def large():
 
 @pytest.mark.parametrize("variant", INPLACE_VARIANTS)
 def test_named_large_fp32(large, variant):
+    """The 2.2 GB workload, inside one device buffer with random guard words
+    on both sides (4 KiB each): a store past either end of the tensor, as
+    the widest vector instantiation could make, changes a guard."""
     wl, want, dmask = large
     say(f"[gpu] named large_fp32 variant={variant}")
-    d = to_device(wl.logits, wl.dtype).view(wl.rows, wl.cols)
+    guard = 1024
+    n = wl.rows * wl.cols
+    g = np.random.default_rng(77).integers(0, 2**32, size=2 * guard, dtype=np.uint64).astype(np.uint32)
+    buf = torch.empty(n + 2 * guard, dtype=torch.int32, device="cuda")
+    buf[:guard] = torch.from_numpy(g[:guard].view(np.int32)).to("cuda")
+    buf[guard + n:] = torch.from_numpy(g[guard:].view(np.int32)).to("cuda")
+    buf[guard:guard + n] = torch.from_numpy(wl.logits.view(np.int32).reshape(-1)).to("cuda")
+    d = buf[guard:guard + n].view(torch.float32).view(wl.rows, wl.cols)
     mb.mi_apply_bitmask_inplace(d, dmask, wl.vocab_size, None, wl.fill_value, variant=variant)
     torch.cuda.synchronize()
+    assert np.array_equal(buf[:guard].cpu().numpy().view(np.uint32), g[:guard]), "store before the tensor"
+    assert np.array_equal(buf[guard + n:].cpu().numpy().view(np.uint32), g[guard:]), "store past the tensor"
     got = to_host(d, wl.dtype)
     assert np.array_equal(got, want)
-    del d
+    del d, buf
     torch.cuda.empty_cache()
 
 

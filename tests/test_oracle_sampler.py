@@ -31,6 +31,19 @@ def test_philox_known_answers(case):
     assert [int(o) for o in out] == [int(x, 16) for x in case["out"]]
 
 
+@pytest.mark.parametrize("case", KAT)
+def test_uniforms_word_order_against_known_answers(case):
+    """Token i of a row reads word i % 4 of the Philox block for counter
+    (i // 4, row, offset low, offset high) under key (seed low, seed high):
+    each published vector, read through that placement, gives the four
+    tokens' words, in order."""
+    c = [int(x, 16) for x in case["counter"]]
+    k = [int(x, 16) for x in case["key"]]
+    want = [int(x, 16) for x in case["out"]]
+    u = S.uniforms(seed=k[0] | (k[1] << 32), offset=c[2] | (c[3] << 32), row=c[1], n=4, first=4 * c[0])
+    assert u.tolist() == [((w >> 9) + 0.5) / (1 << 23) for w in want]
+
+
 def test_uniforms_exact_and_open_interval():
     u = S.uniforms(seed=123, offset=7, row=3, n=100000)
     assert (u > 0).all() and (u < 1).all()
