@@ -254,6 +254,34 @@ mi_status_t mi_apply_bitmask_sample_ws(
     int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * As mi_apply_bitmask_sample_ws, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace argument; the split path's
+ * workspace is a device array inside the library (8 393 216 bytes, enough
+ * for 32 rows), which each GPU the library runs on holds until the process
+ * ends.  Its address is looked up (hipGetDevice, hipGetSymbolAddress) on
+ * the first call made with each device current; the call itself allocates
+ * nothing and frees nothing.  The stream must belong to the current device.
+ *
+ * A batch whose split would need more than that array -- more than 32 bf16
+ * or fp16 rows (at most 64) of at least 8192 tokens, with top-k, top-p or
+ * min-p in force for some row -- is rejected with MI_ERR_BAD_SHAPE and
+ * enqueues nothing; split it, or give mi_apply_bitmask_sample_ws a
+ * workspace.  Every other batch runs as mi_apply_bitmask_sample_ws would,
+ * with the same tokens.
+ *
+ * All calls on one GPU share its array, and each clears what it uses on its
+ * own stream before using it: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race on it and must be
+ * ordered by the caller.  Errors as mi_apply_bitmask_sample, plus MI_ERR_HIP
+ * when the array's address cannot be had.
+ */
+mi_status_t mi_apply_bitmask_sample_noalloc(
+    const void *logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
+    const int32_t *mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
+    int64_t vocab_size, const mi_sample_params_t *params, int64_t *tokens, hipStream_t stream);
+
+/*
  * Workspace bytes mi_apply_bitmask_sample_ws uses for `rows` rows of `vocab`
  * tokens (the resolved vocab size) of `dtype`: rows * 262288 (a histogram of
  * 65536 32-bit counts, a 128-byte map of its nonzero runs and 16 bytes of

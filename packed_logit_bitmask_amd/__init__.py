@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     mi_apply_bitmask_out_host,
     mi_apply_bitmask_rows,
     mi_apply_bitmask_sample,
+    mi_apply_bitmask_sample_noalloc,
     resolve_vocab_size,
     sample_workspace_bytes,
 )
@@ -40,7 +41,8 @@ from .xgrammar_api import (  # noqa: F401
 __all__ = [
     "BitmaskError", "EXPORTS", "MI_DTYPE", "VARIANT", "fill_value_bits", "host_isa", "load_library",
     "mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_host",
-    "mi_apply_bitmask_out_host", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample", "resolve_vocab_size",
+    "mi_apply_bitmask_out_host", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample", "mi_apply_bitmask_sample_noalloc",
+    "resolve_vocab_size",
     "sample_workspace_bytes",
     "allocate_token_bitmask", "apply_token_bitmask_inplace", "bitmask_dtype", "get_bitmask_shape",
     "reset_token_bitmask", "MaskStager",

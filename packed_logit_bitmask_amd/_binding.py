@@ -24,7 +24,7 @@ VARIANT = {"auto": 0, "scalar": 1, "vec": 2, "wronly": 3, "vec_resident": 4}
 # every symbol include/mi_bitmask.h declares
 EXPORTS = ["mi_apply_bitmask_inplace", "mi_apply_bitmask_out", "mi_apply_bitmask_inplace_ex",
            "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample",
-           "mi_apply_bitmask_sample_ws", "mi_sample_workspace_bytes",
+           "mi_apply_bitmask_sample_ws", "mi_apply_bitmask_sample_noalloc", "mi_sample_workspace_bytes",
            "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
            "mi_resolve_vocab_size", "mi_fill_value_bits", "mi_status_string", "mi_last_error_message",
            "mi_host_isa"]
@@ -72,13 +72,15 @@ def load_library(path: Union[str, pathlib.Path, None] = None) -> ctypes.CDLL:
                                             ctypes.POINTER(SampleParams), _p, _p]
     lib.mi_apply_bitmask_sample_ws.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64, _i64,
                                                ctypes.POINTER(SampleParams), _p, _p, _i64, _p]
+    lib.mi_apply_bitmask_sample_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _i64,
+                                                    _i64, ctypes.POINTER(SampleParams), _p, _p]
     lib.mi_sample_workspace_bytes.argtypes = [ctypes.c_int, _i64, _i64]
     lib.mi_sample_workspace_bytes.restype = _i64
     lib.mi_apply_bitmask_inplace_host.argtypes = _INPLACE + [ctypes.c_int]
     lib.mi_apply_bitmask_out_host.argtypes = _OUT + [ctypes.c_int]
     for f in ("mi_apply_bitmask_inplace", "mi_apply_bitmask_inplace_ex", "mi_apply_bitmask_out",
               "mi_apply_bitmask_out_ex", "mi_apply_bitmask_rows", "mi_apply_bitmask_sample",
-              "mi_apply_bitmask_sample_ws", "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
+              "mi_apply_bitmask_sample_ws", "mi_apply_bitmask_sample_noalloc", "mi_apply_bitmask_inplace_host", "mi_apply_bitmask_out_host",
               "mi_resolve_vocab_size", "mi_fill_value_bits"):
         getattr(lib, f).restype = ctypes.c_int
     lib.mi_resolve_vocab_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64)]
@@ -311,6 +313,23 @@ def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None,
                 raise ValueError("workspace must be a contiguous tensor on the logits' GPU")
             wp, wn = workspace.data_ptr(), workspace.numel() * workspace.element_size()
         check(lib.mi_apply_bitmask_sample_ws(*c.head(), wp, wn, _stream_handle(logits.device, stream)))
+    return c.out
+
+
+def mi_apply_bitmask_sample_noalloc(logits, mask=None, vocab_size: Optional[int] = None, *, temperature=1.0,
+                                    top_k=0, top_p=1.0, min_p=0.0, seed: int = 0, offset: int = 0, out=None,
+                                    stream=None):
+    """As :func:`mi_apply_bitmask_sample`, through the entry point that
+    allocates nothing: a small split batch uses the library's own device
+    scratch instead of a workspace.  Calls that overlap on one GPU race on
+    that scratch.  The binding itself allocates only what it must convert:
+    pass ``out`` (int64, one per row) and per-row parameters already of the
+    C types (float32, int32) on the GPU, or scalars, to allocate nothing.
+    """
+    lib = load_library()
+    with _on(stream):
+        c = _SampleCall(logits, mask, vocab_size, temperature, top_k, top_p, min_p, seed, offset, out)
+        check(lib.mi_apply_bitmask_sample_noalloc(*c.head(), _stream_handle(logits.device, stream)))
     return c.out
 
 

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "host_checks.h"
 #include "sample_kernel.h"
@@ -70,6 +71,16 @@ mi_status_t check_logits_only(const void* logits, mi_dtype_t dtype, int64_t rows
 
 }  // namespace
 
+// ---- Scratch of mi_apply_bitmask_sample_noalloc: the split path's workspace
+// as a device array of the library, for callers that cannot allocate.  Each
+// GPU holds its own copy (8.4 MB, enough for kNoAllocRows split rows) until
+// the process ends.  Host code never passes the array's name to a kernel
+// (on the host it stands for no device address): it takes each device's
+// address once, through hipGetSymbolAddress, and uses that.
+constexpr int64_t kNoAllocRows = 32;
+constexpr int64_t kScratchBytes = kNoAllocRows * mi::split_workspace_bytes(1);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 // Whether a batch takes the split filtered path (filtered 16-bit rows spread
@@ -78,10 +89,35 @@ bool split_filtered_batch(mi_dtype_t dtype, int64_t rows, int64_t V) {
   return dtype != MI_DTYPE_F32 && rows >= 1 && rows <= kSplitFilteredRows && V >= 8192;
 }
 
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the
+// first call made with that device current.
+mi_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MI_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MI_ERR_HIP, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MI_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MI_OK;
+}
+
+// use_scratch: take the split path's workspace from `scratch` (workspace and
+// workspace_bytes are then ignored).
 mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols, int64_t logits_row_stride,
                         const int32_t* mask, int64_t mask_rows, int64_t mask_cols, int64_t mask_row_stride,
                         int64_t vocab_size, const mi_sample_params_t* params, int64_t* tokens, void* workspace,
-                        int64_t workspace_bytes, hipStream_t stream) {
+                        int64_t workspace_bytes, hipStream_t stream, bool use_scratch = false) {
   if (!params) return fail(MI_ERR_NULL_POINTER, "params is NULL");
   if (!tokens && rows > 0) return fail(MI_ERR_NULL_POINTER, "tokens is NULL");
   if (workspace_bytes < 0) return fail(MI_ERR_BAD_SHAPE, "negative workspace_bytes");
@@ -106,7 +142,20 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
   // The workspace is used only when this batch can split its filtered rows
   // and it is large enough; then it must not overlap anything else.
   const int64_t ws_need = split_filtered_batch(dtype, rows, p.V) ? mi::split_workspace_bytes(rows) : 0;
-  const bool use_ws = workspace && ws_need > 0 && workspace_bytes >= ws_need;
+  // whether any row may take a filter (only such batches split through a workspace)
+  const bool params_filter = params->top_k || params->top_p || params->min_p || params->top_k_all > 0 ||
+                             params->top_p_all < 1.0f || params->min_p_all > 0.f;
+  if (use_scratch) {
+    if (params_filter && ws_need > kScratchBytes)
+      return fail(MI_ERR_BAD_SHAPE,
+                  "%lld rows of %lld tokens need %lld bytes of scratch; the no-alloc entry point holds %lld "
+                  "(%lld such rows): split the batch, or pass a workspace to mi_apply_bitmask_sample_ws",
+                  (long long)rows, (long long)p.V, (long long)ws_need, (long long)kScratchBytes,
+                  (long long)kNoAllocRows);
+    workspace = nullptr;
+    workspace_bytes = 0;
+  }
+  bool use_ws = workspace && ws_need > 0 && workspace_bytes >= ws_need;
   if (use_ws) {
     if (reinterpret_cast<uintptr_t>(workspace) % 16) return fail(MI_ERR_MISALIGNED, "workspace not 16-byte aligned");
     ByteRange wb;
@@ -121,6 +170,12 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
     }
   }
   if (rows == 0) return MI_OK;
+  if (use_scratch && params_filter && ws_need > 0) {  // every argument check has passed
+    st = scratch_address(&workspace);
+    if (st != MI_OK) return st;
+    workspace_bytes = ws_need;
+    use_ws = true;
+  }
 
   mi::SampleArgs a{params->temperature, params->top_k, params->top_p, params->min_p,
                    params->temperature_all, params->top_k_all, params->top_p_all, params->min_p_all,
@@ -253,6 +308,15 @@ MI_API mi_status_t mi_apply_bitmask_sample_ws(const void* logits, mi_dtype_t dty
                                               int64_t workspace_bytes, hipStream_t stream) {
   return sample_impl(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
                      vocab_size, params, tokens, workspace, workspace_bytes, stream);
+}
+
+MI_API mi_status_t mi_apply_bitmask_sample_noalloc(const void* logits, mi_dtype_t dtype, int64_t rows, int64_t cols,
+                                                   int64_t logits_row_stride, const int32_t* mask, int64_t mask_rows,
+                                                   int64_t mask_cols, int64_t mask_row_stride, int64_t vocab_size,
+                                                   const mi_sample_params_t* params, int64_t* tokens,
+                                                   hipStream_t stream) {
+  return sample_impl(logits, dtype, rows, cols, logits_row_stride, mask, mask_rows, mask_cols, mask_row_stride,
+                     vocab_size, params, tokens, nullptr, 0, stream, true);
 }
 
 MI_API int64_t mi_sample_workspace_bytes(mi_dtype_t dtype, int64_t rows, int64_t vocab) {
