@@ -230,7 +230,9 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
     const bool deep = (n <= 256 || fine) && nseg == 1;
     const int threads = fine8 ? 512 : deep ? 1024 : 256;
     // the 16-bit counters: filtered 16-bit rows, and fp32 rows in 1024-thread
-    // blocks (their top-k passes; see fp32_topk_cut)
+    // blocks (their coarse histogram and bucket list take less; see
+    // coarse_hist32)
+    static_assert(mi::coarse_lds_bytes() <= mi::sample_fine_bytes(1024), "the fp32 cut's LDS fits the 16-bit search's");
     const bool fine_lds = may_filter && nseg == 1 && (fine || threads == 1024);
     const size_t lds = fine_lds ? std::max(mi::sample_fine_bytes(threads), mi::sample_hist_bytes(threads))
                                 : (may_filter ? mi::sample_hist_bytes(threads) : 0);

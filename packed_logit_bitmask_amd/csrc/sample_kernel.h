@@ -159,6 +159,64 @@ __device__ __forceinline__ float unit_uniform(uint32_t x) {
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & 63; }
 
+// ---- Wave scans by DPP.  A wave64 is four rows of 16 lanes: row shifts
+// (row_shr:n) combine lanes inside a row, then row broadcasts (lane 15 of a
+// row into the next row, lane 31 into rows 2 and 3) combine the rows.  Every
+// step is one VALU move, with none of the LDS round trips that __shfl makes.
+// Lanes a move has no source for (or whose row it leaves out) read 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_read(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_read(unsigned long long v) {
+  const uint32_t lo = dpp_read<CTRL, ROWS>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_read<CTRL, ROWS>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Inclusive sums inside each 16-lane row, then lane 15 of rows 0 and 2 added
+// into rows 1 and 3: lane 31 then holds the total of lanes 0..31 and lane 63
+// that of lanes 32..63 (each half-wave's sum).
+template <typename T>
+__device__ __forceinline__ T half_wave_scan(T x) {
+  x += dpp_read<kDppShr1, 0xF>(x);
+  x += dpp_read<kDppShr2, 0xF>(x);
+  x += dpp_read<kDppShr4, 0xF>(x);
+  x += dpp_read<kDppShr8, 0xF>(x);
+  x += dpp_read<kDppBcast15, 0xA>(x);
+  return x;
+}
+
+// Inclusive prefix sum over the wave's 64 lanes (lane 63 holds the total).
+template <typename T>
+__device__ __forceinline__ T wave_prefix_sum(T x) {
+  x = half_wave_scan(x);
+  x += dpp_read<kDppBcast31, 0xC>(x);
+  return x;
+}
+
+// Maximum over the wave's 64 lanes, in every lane.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp_read<kDppShr1, 0xF>(x));
+  x = max(x, dpp_read<kDppShr2, 0xF>(x));
+  x = max(x, dpp_read<kDppShr4, 0xF>(x));
+  x = max(x, dpp_read<kDppShr8, 0xF>(x));
+  x = max(x, dpp_read<kDppBcast15, 0xA>(x));
+  x = max(x, dpp_read<kDppBcast31, 0xC>(x));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+// Lane 63's value, in every lane.
+__device__ __forceinline__ uint32_t lane63(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+__device__ __forceinline__ unsigned long long lane63(unsigned long long x) {
+  return (static_cast<unsigned long long>(lane63(static_cast<uint32_t>(x >> 32))) << 32) | lane63(static_cast<uint32_t>(x));
+}
+
 
 // One row's logits and mask, read 8 consecutive tokens (a group) at a time.
 // The loads go through raw buffer resources that end at the row's vocab
@@ -538,20 +596,25 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   constexpr uint32_t KPL = KPT / 64;            // keys per lane in the final search
   constexpr uint32_t kCount = (1u << CB) - 1u;  // one counter's bits
   constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
-  __shared__ uint32_t s_n[kWaves], s_kmax[kWaves], s_all[kWaves], s_c[kWaves], s_cut[2], s_cross[2];
+  // The keys of non-finite values fill whole words at both ends of the key
+  // space, so a word holds finite keys only or none: words [kW0, kW1).
+  static_assert(D::kKey16Lo % KW == 0 && (D::kKey16Hi + 1) % KW == 0, "finite keys start and end on a word");
+  constexpr uint32_t kW0 = D::kKey16Lo / KW, kW1 = (D::kKey16Hi + 1) / KW;
+  __shared__ uint32_t s_d[kWaves], s_kmax[kWaves], s_c[kWaves], s_cut[2], s_cross[2];
   __shared__ uint32_t s_above_n[2], s_kept[2];
   __shared__ unsigned long long s_m[kWaves], s_above[2];
   const int t = static_cast<int>(threadIdx.x);
   const int lane = lane_id(), wave = t >> 6;
   // the count of key k, from the word that holds it
   const auto count_in = [](uint32_t w, uint32_t k) { return (w >> ((k % KW) * CB)) & kCount; };
-  // every count of a word, summed
+  // every count of a word, summed: one dot product with ones
   const auto word_sum = [](uint32_t w) {
     if constexpr (CB == 16) {
-      return (w & 0xFFFFu) + (w >> 16);
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      const u16x2 ones = {1, 1};
+      return __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, w), ones, 0u, false);
     } else {
-      const uint32_t s2 = (w & 0x00FF00FFu) + ((w >> 8) & 0x00FF00FFu);
-      return (s2 & 0xFFFFu) + (s2 >> 16);
+      return __builtin_amdgcn_udot4(w, 0x01010101u, 0u, false);
     }
   };
 
@@ -559,74 +622,60 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
     s_cut[t] = 0u;
     s_cross[t] = ~0u;  // no crossing: keep every candidate
   }
-  uint32_t allowed = count_keys<D, BYTES, THREADS, CB>(rv, fine, pre, preloaded);  // tokens the mask allows below V
+  const uint32_t allowed = count_keys<D, BYTES, THREADS, CB>(rv, fine, pre, preloaded);  // tokens the mask allows below V
 
   // ---- sums: thread t holds keys [KPT t, KPT t + KPT), words [32t, 32t + 32),
-  // read in a rotated order so a wave's lanes hit different banks.  Only
-  // the threads at the two ends of the key range hold keys of non-finite
-  // values; the others count every key.
+  // read eight at a time in a rotated order so a wave's lanes hit different
+  // banks.  Only the threads at the two ends of the key space hold words of
+  // non-finite keys.
   const uint32_t k0 = KPT * static_cast<uint32_t>(t);
   const auto in_range = [](uint32_t k) { return k - D::kKey16Lo <= kSpan; };
-  const bool inside = in_range(k0) && in_range(k0 + KPT - 1);
+  const uint32_t wt = 32u * static_cast<uint32_t>(t);
+  const bool inside = wt >= kW0 && wt + 32u <= kW1;
   uint32_t c = 0, all = 0, ktop = 0;  // candidates, every count, highest candidate key + 1
   uint32_t nz = 0;                    // bit j: word 32t + j counts a candidate
-  if (inside) {
-    for (int j = 0; j < 32; ++j) {
-      const int jj = (j + t) & 31;
-      const uint32_t w = fine[32 * t + jj];
-      all += word_sum(w);
-      nz |= (w ? 1u : 0u) << jj;
-    }
-    c = all;
-    if (nz) {
-      const int jt = 31 - __builtin_clz(nz);
-      const uint32_t w = fine[32 * t + jt];
-      ktop = k0 + KW * jt + static_cast<uint32_t>(31 - __builtin_clz(w)) / CB + 1u;
-    }
-  } else {
-    for (int j = 0; j < 32; ++j) {
-      const int jj = (j + t) & 31;
-      const uint32_t w = fine[32 * t + jj];
-      const uint32_t ka = k0 + KW * jj;
+  for (int j0 = 0; j0 < 32; j0 += 8) {
+    uint32_t wv[8];
 #pragma unroll
-      for (uint32_t e = 0; e < KW; ++e) {
-        const uint32_t n = count_in(w, e);
-        all += n;
-        if (in_range(ka + e) && n) {
-          c += n;
-          ktop = max(ktop, ka + e + 1);
-          nz |= 1u << jj;
-        }
+    for (int u = 0; u < 8; ++u) wv[u] = fine[wt + ((j0 + u + t) & 31)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t jj = static_cast<uint32_t>((j0 + u + t) & 31);
+      const uint32_t ws = word_sum(wv[u]);
+      all += ws;
+      if (inside || wt + jj - kW0 < kW1 - kW0) {
+        c += ws;
+        nz |= (wv[u] ? 1u : 0u) << jj;
       }
     }
   }
-  // block totals (every count, highest key) and suffix totals of c, high keys first
-  uint32_t sc = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t vc = static_cast<uint32_t>(__shfl_down(static_cast<int>(sc), o));
-    if (lane + o < 64) sc += vc;
-    ktop = max(ktop, static_cast<uint32_t>(__shfl_xor(static_cast<int>(ktop), o)));
-    allowed += static_cast<uint32_t>(__shfl_xor(static_cast<int>(allowed), o));
-    all += static_cast<uint32_t>(__shfl_xor(static_cast<int>(all), o));
+  if (nz) {
+    const int jt = 31 - __builtin_clz(nz);
+    const uint32_t w = fine[wt + jt];
+    ktop = k0 + KW * jt + static_cast<uint32_t>(31 - __builtin_clz(w)) / CB + 1u;
   }
+  // block totals (the shortfall of every count against the tokens counted,
+  // the highest key) and suffix totals of c, high keys first
+  const uint32_t pc = wave_prefix_sum(c);
+  const uint32_t wc = lane63(pc);
+  uint32_t sc = wc - pc + c;
+  const uint32_t wd = lane63(wave_prefix_sum(allowed - all));  // 0 unless a count wrapped
+  const uint32_t wk = wave_max(ktop);
   if (lane == 0) {
-    s_c[wave] = sc;
-    s_kmax[wave] = ktop;
-    s_n[wave] = allowed;
-    s_all[wave] = all;
+    s_c[wave] = wc;
+    s_kmax[wave] = wk;
+    s_d[wave] = wd;
   }
   __syncthreads();
-  uint32_t tot_c = 0, tot_allowed = 0, tot_all = 0;
+  uint32_t tot_c = 0, tot_d = 0;
   ktop = 0;
   for (int w = 0; w < kWaves; ++w) {
     tot_c += s_c[w];
-    tot_allowed += s_n[w];
-    tot_all += s_all[w];
+    tot_d += s_d[w];
     ktop = max(ktop, s_kmax[w]);
     if (w > wave) sc += s_c[w];
   }
-  if (tot_all != tot_allowed) return false;  // a count wrapped
+  if (tot_d != 0) return false;  // a count wrapped
   if (tot_c == 0) {
     *best = -__builtin_inff();
     return true;
@@ -636,35 +685,48 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   const auto mass = [&](uint32_t k) { return fixed_mass(D::value(static_cast<Bits>(bits_of_key16(k))), inv_t, zmax); };
   const auto cut_of = [](uint32_t k) { return order_key(D::value(static_cast<Bits>(bits_of_key16(k)))); };
 
-  // ---- top-p masses per thread, then their suffix totals
+  // ---- top-p masses per thread, then their suffix totals.  The keys that
+  // hold tokens crowd a narrow band, so a thread walking its own 32 words
+  // would leave most waves idle while the others step through every slot of
+  // theirs.  Instead, at step s each half-wave takes the 32 words of one
+  // thread (word s * THREADS + t to lane t, so thread (s * THREADS + t) / 32
+  // owns the half-wave's words), adds up the masses of its word's counters,
+  // sums them over the half-wave and stores that thread's total; a wave whose
+  // 64 words are all zero skips the step.  Every thread's total is written
+  // exactly once.
   unsigned long long m = 0, sm = 0, tot_m = 0;
   if (use_p) {
-    // eight words at a time, in the rotated order (different banks across
-    // the wave), loaded together before any is used
-    const uint32_t rot = static_cast<uint32_t>(t) & 31u;
-    const uint32_t nzr = rot ? (nz >> rot) | (nz << (32u - rot)) : nz;  // bit j: word (j + t) & 31
-    for (int j0 = 0; j0 < 32; j0 += 8) {
-      if (!((nzr >> j0) & 0xFFu)) continue;
-      uint32_t w[8];
+    __shared__ unsigned long long s_own[THREADS];
+    constexpr int kBatch = 4;  // words read ahead per lane
+    for (int s0 = 0; s0 < 32; s0 += kBatch) {
+      uint32_t wb[kBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = fine[32 * t + ((j0 + u + t) & 31)];
+      for (int j = 0; j < kBatch; ++j) wb[j] = fine[(s0 + j) * THREADS + t];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t ka = k0 + KW * static_cast<uint32_t>((j0 + u + t) & 31);
+      for (int j = 0; j < kBatch; ++j) {
+        const uint32_t word = static_cast<uint32_t>((s0 + j) * THREADS + t);
+        const uint32_t w = wb[j];
+        if (!__ballot(w != 0u)) {
+          if ((lane & 31) == 31) s_own[word / 32u] = 0ull;
+          continue;
+        }
+        const uint32_t ka = KW * word;  // the word's first key
+        unsigned long long mw = 0;
 #pragma unroll
         for (uint32_t e = 0; e < KW; ++e) {
-          const uint32_t n = count_in(w[u], e);
-          if (n && in_range(ka + e)) m += static_cast<unsigned long long>(n) * mass(ka + e);
+          const uint32_t n = count_in(w, e);
+          if (n && in_range(ka + e)) mw += static_cast<unsigned long long>(n) * mass(ka + e);
         }
+        mw = half_wave_scan(mw);  // lanes 31 and 63: each half-wave's total
+        if ((lane & 31) == 31) s_own[word / 32u] = mw;
       }
     }
-    sm = m;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long vm = __shfl_down(sm, o);
-      if (lane + o < 64) sm += vm;
-    }
-    if (lane == 0) s_m[wave] = sm;
+    __syncthreads();
+    m = s_own[t];
+    const unsigned long long pm = wave_prefix_sum(m);
+    const unsigned long long wm = lane63(pm);
+    sm = wm - pm + m;
+    if (lane == 0) s_m[wave] = wm;
     __syncthreads();
     for (int w = 0; w < kWaves; ++w) {
       tot_m += s_m[w];
@@ -708,16 +770,11 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
       v += vv[j];
       vn += n[j];
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long u = __shfl_down(v, o);
-      const uint32_t un = static_cast<uint32_t>(__shfl_down(static_cast<int>(vn), o));
-      if (lane + o < 64) {
-        v += u;
-        vn += un;
-      }
-    }
-    const unsigned long long total = v + s_above[which];  // the searched total at and above kb
+    // suffix totals over the lanes, from prefix sums
+    const unsigned long long pv = wave_prefix_sum(v);
+    const uint32_t pn = wave_prefix_sum(vn);
+    const unsigned long long total = lane63(pv) - pv + v + s_above[which];  // the searched total at and above kb
+    vn = lane63(pn) - pn + vn;
     const uint64_t hit = __ballot(total >= need);
     const int L = 63 - __clzll(static_cast<long long>(hit));
     // within lane L: the largest of its keys whose suffix still reaches the need
@@ -748,41 +805,62 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   return true;
 }
 
-// ---- fp32 rows with top-k alone: the cut from two passes of 16-bit keys.
+// ---- fp32 rows with top-k or top-p, in 1024-thread blocks: the cut from one
+// coarse pass and a list of the tokens in the bucket that holds it.
 //
-// Four radix passes would each do the same work per token.  Instead the first
-// pass counts every candidate under the top 16 bits of its order key (a
-// bucket of bf16 width; counts per bucket are exact), a search finds the
-// bucket holding the k-th largest candidate, and a second pass counts only
-// that bucket's candidates, under the low 16 bits of their keys, which gives
-// the exact key of the k-th largest.  Both passes use the 65536 16-bit
-// counters of the 16-bit search (LDS, two per word, a spare word per lane).
+// The coarse pass counts every candidate (for top-k) and sums its fixed-point
+// mass (for top-p) under the top 12 bits of its order key: 4096 buckets of an
+// eighth of a binade, in LDS.  A search over them finds each cut's bucket and
+// the count or mass above it.  The draw pass then keeps every candidate above
+// the higher of the two buckets whatever the rest of its key is, drops every
+// candidate below it, and lists the candidates inside it (order key and
+// index) in LDS; a radix select over the list's low 20 key bits, three
+// digits, gives the exact cut, and the listed tokens at or above it join the
+// draw.  Three passes over the row for top-p (the maximum first), two for
+// top-k alone -- against five and three for a radix search over the row.  A
+// bucket holding more candidates than the list has room for sends the row to
+// the radix search.
+constexpr int kCoarseBuckets = 4096;
+constexpr uint32_t kCoarseShift = 20;  // bucket = order key >> 20
+constexpr uint32_t kListCap = 12288;   // listed candidates: 96 KB of keys and indices
 
-// One pass over an fp32 row counting candidates (mask bit set, finite) into
-// `fine` from a cleared start: key_of(order key) is the 16-bit key a
-// candidate counts under, or ~0u when it does not count.  With SPARSE unset
-// a token that does not count adds to its lane's spare word, so the add needs
-// no branch; with SPARSE set (few tokens count) it adds nothing, and a wave
-// none of whose lanes counts skips the add.  Returns this thread's number of
-// counted tokens; ends with a barrier.
-template <int THREADS, bool SPARSE, typename K>
-__device__ __forceinline__ uint32_t count_keys32(const RowView<F32Bits>& rv, uint32_t* fine, K&& key_of) {
-  constexpr uint32_t kWords = 32768;
+// Dynamic LDS of the fp32 1024-thread kernel this path uses (it has the
+// 131 KB of the 16-bit search): the coarse masses and counts (48 KB), then,
+// reusing the space, the list and the list search's 256-bin histograms.
+constexpr size_t coarse_lds_bytes() {
+  const size_t hist = static_cast<size_t>(kCoarseBuckets) * (sizeof(unsigned long long) + sizeof(uint32_t));
+  const size_t list = static_cast<size_t>(kListCap) * 2 * sizeof(uint32_t) + 256 * (sizeof(unsigned long long) + sizeof(uint32_t));
+  return hist > list ? hist : list;
+}
+
+// The float whose order key is k (the inverse of order_key; the key of -0 is
+// that of +0 and maps back to +0).
+__device__ __forceinline__ float value_of_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One pass over an fp32 row: every candidate (mask bit set, finite) adds 1
+// to cc[bucket] when use_k and its fixed-point mass to cm[bucket] when use_p,
+// from a cleared start.  Ends with a barrier.
+template <int THREADS>
+__device__ __forceinline__ void coarse_hist32(const RowView<F32Bits>& rv, unsigned long long* cm, uint32_t* cc,
+                                              bool use_k, bool use_p, float inv_t, float zmax) {
   const int t = static_cast<int>(threadIdx.x);
-  uint4* f4 = reinterpret_cast<uint4*>(fine);
-  for (int i = t; i < static_cast<int>(kWords + 64) / 4; i += THREADS) f4[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = t; i < kCoarseBuckets; i += THREADS) {
+    cm[i] = 0ull;
+    cc[i] = 0u;
+  }
   __syncthreads();
-  uint32_t counted = 0;
-  const uint32_t spare = 2u * (kWords + static_cast<uint32_t>(lane_id()));
-  const auto add = [&](uint32_t x, bool candidate) {
-    const uint32_t key = order_key(__uint_as_float(x));
-    const uint32_t k = candidate && finite_key(key) ? key_of(key) : ~0u;
-    counted += k != ~0u ? 1u : 0u;
-    if constexpr (SPARSE) {
-      if (k != ~0u) atomicAdd(&fine[k >> 1], 1u << ((k & 1u) << 4));
-    } else {
-      const uint32_t kk = k != ~0u ? k : spare;
-      atomicAdd(&fine[kk >> 1], 1u << ((kk & 1u) << 4));
+  const auto add = [&](uint32_t xb, uint32_t bit) {
+    const float x = __uint_as_float(xb);
+    const uint32_t key = order_key(x);
+    if (bit && finite_key(key)) {
+      const uint32_t b = key >> kCoarseShift;
+      if (use_k) atomicAdd(&cc[b], 1u);
+      if (use_p) {
+        const uint32_t m = fixed_mass(x, inv_t, zmax);  // one that truncates to 0 adds nothing
+        if (m) atomicAdd(&cm[b], static_cast<unsigned long long>(m));
+      }
     }
   };
   walk_row_raw<128, THREADS>(rv, [&](int32_t g, const typename RowView<F32Bits>::Raw& raw, bool full) {
@@ -795,111 +873,60 @@ __device__ __forceinline__ uint32_t count_keys32(const RowView<F32Bits>& rv, uin
       add(rv.row[i], rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u);
   }
   __syncthreads();
-  return counted;
 }
 
-// Over the 65536 16-bit counters of `fine` (key k in half k & 1 of word
-// k / 2), the largest key whose suffix count (the counts of the keys at and
-// above it) reaches `need`, 1 <= need <= the total; *above gets the count of
-// the keys above it.  All 1024 threads of the block; thread t holds keys
-// [64t, 64t + 64), and wave 0 takes the crossing thread's keys one per lane.
-// Ends with a barrier.
-template <int THREADS>
-__device__ __forceinline__ uint32_t count_search(const uint32_t* fine, uint32_t need, uint32_t* above) {
-  static_assert(THREADS == 1024, "thread t holds keys [64t, 64t + 64)");
-  constexpr int kWaves = THREADS / 64;
-  __shared__ uint32_t s_c[kWaves], s_cross, s_above_t, s_key, s_above;
+// Over h[0 .. 4095] (thread t of 1024 holds buckets 4t .. 4t + 3), with
+// S(b) = h[b] + ... + h[4095] and need = need_of(S(0)): the largest b with
+// S(b) >= need, and *above = S(b + 1); ~0u (no cut) when need is 0 or above
+// S(0).  *need_out gets need.  Ends with a barrier.
+template <typename T, typename NeedOf>
+__device__ __forceinline__ uint32_t coarse_search(const T* h, NeedOf&& need_of, T* above, T* need_out) {
+  constexpr int kWaves = 16;
+  __shared__ T s_w[kWaves];
+  __shared__ T s_ab;
+  __shared__ uint32_t s_b;
   const int t = static_cast<int>(threadIdx.x);
   const int lane = lane_id(), wave = t >> 6;
-  uint32_t c = 0;
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t w = fine[32 * t + ((j + t) & 31)];  // rotated: a wave's lanes read different banks
-    c += (w & 0xFFFFu) + (w >> 16);
-  }
-  uint32_t sc = c;
+  T hv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) hv[j] = h[4 * t + j];
+  const T c = hv[0] + hv[1] + hv[2] + hv[3];
+  T sc = c;  // suffix total from this thread's buckets up
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t v = static_cast<uint32_t>(__shfl_down(static_cast<int>(sc), o));
+    const T v = __shfl_down(sc, o);
     if (lane + o < 64) sc += v;
   }
-  if (lane == 0) s_c[wave] = sc;
-  __syncthreads();
-  for (int w = wave + 1; w < kWaves; ++w) sc += s_c[w];
-  if (sc >= need && sc - c < need) {  // exactly one thread: sc falls with t
-    s_cross = static_cast<uint32_t>(t);
-    s_above_t = sc - c;
+  if (lane == 0) s_w[wave] = sc;
+  if (t == 0) {
+    s_b = ~0u;
+    s_ab = 0;
   }
   __syncthreads();
-  if (wave == 0) {
-    const uint32_t kx = 64u * s_cross + static_cast<uint32_t>(lane);
-    const uint32_t n = (fine[kx >> 1] >> ((kx & 1u) << 4)) & 0xFFFFu;
-    uint32_t v = n;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t u = static_cast<uint32_t>(__shfl_down(static_cast<int>(v), o));
-      if (lane + o < 64) v += u;
-    }
-    const uint32_t total = v + s_above_t;  // the counts of the keys at and above kx
-    const uint64_t hit = __ballot(total >= need);
-    const int L = 63 - __clzll(static_cast<long long>(hit));
-    if (lane == L) {
-      s_key = kx;
-      s_above = total - n;
-    }
-  }
-  __syncthreads();
-  *above = s_above;
-  return s_key;
-}
-
-// The top-k cut of an fp32 row (an order key: keep the candidates at or
-// above it; 0 keeps every one) from the two 16-bit passes.  Returns false
-// when a bucket holds 65536 candidates or more (its 16-bit counter wraps and
-// the counts fall short): the radix search then takes over.  `fine` holds
-// at least 32832 words.
-template <int THREADS>
-__device__ __forceinline__ bool fp32_topk_cut(const RowView<F32Bits>& rv, uint32_t* fine, int32_t top_k,
-                                              uint32_t* cut) {
-  constexpr int kWaves = THREADS / 64;
-  __shared__ uint32_t s_n[kWaves], s_all[kWaves];
-  const int t = static_cast<int>(threadIdx.x);
-  const int lane = lane_id(), wave = t >> 6;
-  uint32_t counted = count_keys32<THREADS, false>(rv, fine, [](uint32_t key) { return key >> 16; });
-  uint32_t all = 0;
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t w = fine[32 * t + ((j + t) & 31)];
-    all += (w & 0xFFFFu) + (w >> 16);
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    counted += static_cast<uint32_t>(__shfl_xor(static_cast<int>(counted), o));
-    all += static_cast<uint32_t>(__shfl_xor(static_cast<int>(all), o));
-  }
-  if (lane == 0) {
-    s_n[wave] = counted;
-    s_all[wave] = all;
-  }
-  __syncthreads();
-  uint32_t tot = 0, tot_all = 0;
+  T tot = 0;
   for (int w = 0; w < kWaves; ++w) {
-    tot += s_n[w];
-    tot_all += s_all[w];
+    tot += s_w[w];
+    if (w > wave) sc += s_w[w];
   }
-  if (tot_all != tot) return false;  // a bucket's counter wrapped
-  const uint32_t need = static_cast<uint32_t>(top_k);
-  if (need > tot) {  // k at or above the candidates (or none): keep every one
-    *cut = 0u;
-    return true;
+  const T need = need_of(tot);
+  if (need != 0 && need <= tot && sc >= need && sc - c < need) {  // one thread: sc falls with t
+    T acc = sc - c;  // S(4t + 4)
+    uint32_t b = 4u * static_cast<uint32_t>(t);
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (acc + hv[j] >= need) {
+        b = 4u * static_cast<uint32_t>(t) + static_cast<uint32_t>(j);
+        break;
+      }
+      acc += hv[j];
+    }
+    s_b = b;
+    s_ab = acc;
   }
-  uint32_t above;
-  const uint32_t bucket = count_search<THREADS>(fine, need, &above);
-  // the bucket's candidates under the low 16 bits of their keys
-  count_keys32<THREADS, true>(rv, fine,
-                              [bucket](uint32_t key) { return (key >> 16) == bucket ? (key & 0xFFFFu) : ~0u; });
-  uint32_t above_low;
-  const uint32_t low = count_search<THREADS>(fine, need - above, &above_low);
-  *cut = (bucket << 16) | low;
-  return true;
+  __syncthreads();
+  *above = s_ab;
+  *need_out = need;
+  return s_b;
 }
 
 // ---- Filtered 16-bit rows split over several blocks (few rows).
@@ -1416,12 +1443,158 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // histogram search covers the rest), and a separate draw keeps the
   // kernel's register count down for the common path.
   constexpr bool kFuseDraw = sizeof(typename D::Bits) == 4;
-  // fp32 rows with top-k alone (min-p aside), in 1024-thread blocks (whose
-  // LDS then holds the 16-bit counters): two 16-bit passes instead of the
-  // radix passes
+  bool drawn = false;
+  // fp32 rows with top-k or top-p in 1024-thread blocks: the coarse pass, then
+  // a draw that lists the candidates of the cut's bucket (coarse_hist32)
   if constexpr (sizeof(typename D::Bits) == 4 && THREADS == 1024) {
-    if (use_k && !use_p && !have_cut)
-      have_cut = fp32_topk_cut<THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), top_k, &cut);
+    if ((use_k || use_p) && !have_cut) {
+      unsigned long long* cm = reinterpret_cast<unsigned long long*>(s_dyn);
+      uint32_t* cc = reinterpret_cast<uint32_t*>(cm + kCoarseBuckets);
+      coarse_hist32<THREADS>(rv, cm, cc, use_k, use_p, inv_t, zmax);
+      uint32_t n_above = 0, need_k = 0;
+      unsigned long long m_above = 0, need_p = 0;
+      const uint32_t bk_ = use_k ? coarse_search<uint32_t>(
+                                       cc, [&](uint32_t tot) { return static_cast<uint32_t>(top_k) <= tot ? static_cast<uint32_t>(top_k) : 0u; },
+                                       &n_above, &need_k)
+                                 : ~0u;
+      const uint32_t bp_ = use_p ? coarse_search<unsigned long long>(
+                                       cm,
+                                       [&](unsigned long long tot) {
+                                         // p <= 0 keeps just the largest value, as p = 0 does: any mass reaches it
+                                         const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(tot);
+                                         const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
+                                         return target ? target : 1ull;
+                                       },
+                                       &m_above, &need_p)
+                                 : ~0u;
+      // the higher of the two crossing buckets (~0u: that search keeps every candidate)
+      const uint32_t bh = bk_ == ~0u ? bp_ : (bp_ == ~0u ? bk_ : max(bk_, bp_));
+      have_cut = true;  // with bh == ~0u the cut is 0: every candidate is kept
+      if (bh != ~0u) {
+        // ---- draw: candidates above bucket bh by the walk, those inside listed
+        __shared__ uint32_t s_ln;
+        uint32_t* lkey = reinterpret_cast<uint32_t*>(s_dyn);
+        uint32_t* lidx = lkey + kListCap;
+        __syncthreads();  // the searches' reads of cm and cc are done before the list overwrites them
+        if (t == 0) s_ln = 0u;
+        __syncthreads();
+        const int lane = lane_id();
+        const auto group = [&](int32_t i0, const float* x, uint32_t bits) {
+          uint32_t above = 0, inside = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t key = order_key(x[q]);
+            if (((bits >> q) & 1u) && finite_key(key)) {
+              const uint32_t b = key >> kCoarseShift;
+              above |= (b > bh ? 1u : 0u) << q;
+              inside |= (b == bh ? 1u : 0u) << q;
+            }
+          }
+          if (__ballot(inside != 0u)) {  // every lane of the wave takes this branch or none
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const uint64_t bq = __ballot((inside >> q) & 1u);
+              if (!bq) continue;
+              uint32_t base = 0;
+              if (lane == 0) base = atomicAdd(&s_ln, static_cast<uint32_t>(__popcll(bq)));
+              base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
+              const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bq >> 32),
+                                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bq), 0u));
+              if (((inside >> q) & 1u) && pos < kListCap) {
+                lkey[pos] = order_key(x[q]);
+                lidx[pos] = static_cast<uint32_t>(i0 + q);
+              }
+            }
+          }
+          const uint32_t kept = min_p_keep(x, above);
+          if (kept) gumbel_group(i0, x, kept, [&](int q, float key) { offer(key, i0 + q); });
+        };
+        walk_row_raw<BYTES / 2, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+          float x[8];
+          rv.values(raw, x);
+          group(8 * g, x, rv.mask_bits(raw, g, full));
+        });
+        if (rv.V & 7) {  // the partial last group: exact candidate bits from the plain loads
+          float x[8] = {};
+          const uint32_t ok = t == 0 ? rv.load_tail(x) : 0u;
+          group(rv.V & ~7, x, ok);
+        }
+        __syncthreads();
+        const uint32_t n = s_ln;
+        if (n > kListCap) {
+          // the bucket holds more candidates than the list: the radix search below
+          // takes the row over, and its draw replaces this one
+          have_cut = false;
+          bk = -__builtin_inff();
+          bi = 0x7FFFFFFF;
+        } else {
+          // ---- the exact cuts inside bucket bh: a radix select over the list's
+          // low 20 key bits (digits at bits 19..12, 11..4, 3..0), counting for
+          // top-k and summing masses for top-p, as the radix passes do over the row
+          const bool rk = use_k && bk_ == bh, rp = use_p && bp_ == bh;
+          unsigned long long* lh_m = reinterpret_cast<unsigned long long*>(lidx + kListCap);
+          uint32_t* lh_n = reinterpret_cast<uint32_t*>(lh_m + 256);
+          if (t == 0) s_sel = SelectState{bh << kCoarseShift, need_k - n_above, need_p - m_above, bh << kCoarseShift};
+          uint32_t pmask = ~0u << kCoarseShift;
+          for (int shift = 12; shift >= 0; shift = shift == 12 ? 4 : (shift == 4 ? 0 : -1)) {
+            for (int b = t; b < 256; b += THREADS) {
+              lh_n[b] = 0u;
+              lh_m[b] = 0ull;
+            }
+            __syncthreads();
+            const uint32_t pk = s_sel.prefix_k, pp = s_sel.prefix_p;
+            for (uint32_t i = static_cast<uint32_t>(t); i < n; i += THREADS) {
+              const uint32_t key = lkey[i];
+              const uint32_t d = (key >> shift) & 255u;
+              if (rk && (key & pmask) == pk) atomicAdd(&lh_n[d], 1u);
+              if (rp && (key & pmask) == pp) {
+                const uint32_t m = fixed_mass(value_of_key(key), inv_t, zmax);
+                if (m) atomicAdd(&lh_m[d], static_cast<unsigned long long>(m));
+              }
+            }
+            __syncthreads();
+            if (rk && wave == 0) {
+              const WaveSuffix<uint32_t> ws(lh_n);
+              int d;
+              uint32_t ab;
+              ws.pick(s_sel.need_k, &d, &ab);
+              if (lane == 0) {
+                s_sel.prefix_k |= static_cast<uint32_t>(d) << shift;
+                s_sel.need_k -= ab;
+              }
+            }
+            if (rp && wave == 1) {
+              const WaveSuffix<unsigned long long> ws(lh_m);
+              int d;
+              unsigned long long ab;
+              ws.pick(s_sel.need_p, &d, &ab);
+              if (lane == 0) {
+                s_sel.prefix_p |= static_cast<uint32_t>(d) << shift;
+                s_sel.need_p -= ab;
+              }
+            }
+            __syncthreads();
+            pmask |= 255u << shift;
+          }
+          cut = max(rk ? s_sel.prefix_k : 0u, rp ? s_sel.prefix_p : 0u);
+          // the listed candidates at or above the cut join the draw (min-p aside)
+          for (uint32_t i = static_cast<uint32_t>(t); i < n; i += THREADS) {
+            const uint32_t key = lkey[i];
+            const float x = value_of_key(key);
+            if (key >= cut && !(use_min_p && x * inv_t - zmax < ln_min_p)) {
+              const int32_t idx = static_cast<int32_t>(lidx[i]);
+              uint32_t c4[4] = {static_cast<uint32_t>((tok0 + idx) >> 2), static_cast<uint32_t>(row_base + r),
+                                a.offset_lo, a.offset_hi};
+              philox4x32_10(c4, a.seed_lo, a.seed_hi);
+              const int32_t w4 = (tok0 + idx) & 3;
+              const uint32_t word = w4 == 0 ? c4[0] : w4 == 1 ? c4[1] : w4 == 2 ? c4[2] : c4[3];
+              offer(gumbel_key(x, word), idx);
+            }
+          }
+          drawn = true;
+        }
+      }
+    }
   }
   if ((use_k || use_p) && !have_cut) {
     // ---- top-k and top-p cuts: radix passes over 8-bit digits of the key,
@@ -1577,7 +1750,6 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // ---- draw after the 16-bit search
   constexpr uint32_t kFineWordsHere = static_cast<uint32_t>(fine_words(THREADS));
   constexpr uint32_t kListPerWave = kFineWordsHere / (THREADS / 64);
-  bool drawn = false;
   if constexpr (kFineSearch<D, THREADS>) {
     if (have_cut) {
       // The kept test on 16-bit keys of the raw words, two per operation:

@@ -419,10 +419,10 @@ def test_kept_tokens_crowding_one_wave_many_rows(dtype):
 
 
 def test_fp32_top_k_two_pass_cut():
-    """fp32 rows with top-k alone take the cut from two 16-bit passes (the
-    top 16 bits of each key, then the low 16 bits inside the bucket holding
-    the k-th largest).  Rows whose cut falls among 5000 distinct values that
-    share one bf16-width bucket (1 + i * 2^-21), next to random logits; k
+    """fp32 rows with top-k alone: one coarse pass counts candidates per
+    eighth of a binade, and the draw lists the bucket holding the k-th
+    largest for an exact select.  Rows whose cut falls among 5000 distinct
+    values that share one bucket (1 + i * 2^-21), next to random logits; k
     above, at and inside the crowded bucket; a row with ties at the cut; and
     with min-p and a mask.  Against the oracle."""
     rng = np.random.default_rng(107)
@@ -444,9 +444,9 @@ def test_fp32_top_k_two_pass_cut():
 
 
 def test_fp32_top_k_bucket_holding_65536_tokens():
-    """A bf16-width bucket of an fp32 row holding 65535, 65536 or 66000
-    candidates: its 16-bit counter would wrap at 65536, and the row then takes
-    the radix search.  Distinct values inside the bucket, top-k cuts inside
+    """A coarse bucket of an fp32 row holding 65535, 65536 or 66000
+    candidates, more than the list holds: the row then takes the radix search
+    over the whole row.  Distinct values inside the bucket, top-k cuts inside
     and above it."""
     rng = np.random.default_rng(109)
     R, cols = 3, 70003
@@ -459,6 +459,58 @@ def test_fp32_top_k_bucket_holding_65536_tokens():
     for (k, seed) in ((10, 1), (30000, 2), (65600, 3)):
         say(f"[gpu] fp32 bucket holding 65536 tokens k={k}")
         check_rows(bits, "float32", None, None, 1.0, k, 1.0, 0.0, seed=seed, offset=0, min_exact=0.9)
+
+
+def crowded_fp32_rows(rng, R, cols, crowd, shift=-2.0):
+    """N(0,1) + shift logits with `crowd` distinct values 1 + i * 2^-21 (one
+    coarse bucket, an eighth of the binade [1, 2)) placed at random, so most
+    of the softmax mass sits inside that bucket."""
+    x = rng.standard_normal((R, cols)).astype(np.float32) + np.float32(shift)
+    x[x >= 1.0] = np.float32(0.75)
+    for r in range(R):
+        pos = rng.choice(cols, crowd, replace=False)
+        x[r, pos] = np.float32(1.0) + np.arange(crowd, dtype=np.float32) * np.float32(2.0 ** -21)
+    return x
+
+
+@pytest.mark.parametrize("k,p,m", [(0, 0.5, 0.0), (0, 0.1, 0.0), (0, 0.9, 0.0), (0, 0.999, 0.0),
+                                   (2500, 0.9, 0.0), (6000, 0.5, 0.0), (2500, 0.5, 0.0), (2500, 0.5, 0.3),
+                                   (0, 0.5, 0.9), (1, 0.5, 0.0), (0, 0.0, 0.0)])
+def test_fp32_coarse_cut_in_a_crowded_bucket(k, p, m):
+    """fp32 top-p (and top-k with it): the coarse pass sums masses per eighth
+    of a binade; the cut inside the bucket comes from the listed candidates.
+    About three quarters of the mass sits in 5000 distinct values of one
+    bucket, so p = 0.1 and 0.5 cut inside it and 0.9 below it; k inside it
+    with p below, k below with p inside, both inside, min-p on top, and ties
+    at the cut (300 copies of one value).  With a mask and without."""
+    rng = np.random.default_rng(211)
+    R, cols = 5, 40000
+    x = crowded_fp32_rows(rng, R, cols, 5000)
+    x[4, rng.choice(cols, 300, replace=False)] = np.float32(1.0) + np.float32(3000 * 2.0 ** -21)
+    bits = x.view(np.uint32)
+    mask = workloads.pack_allowed(rng.random((R, cols)) < 0.9, (cols + 31) // 32, rng)
+    say(f"[gpu] fp32 coarse cut k={k} p={p} m={m}")
+    check_rows(bits, "float32", mask, None, 1.0, k, p, m, seed=7, offset=int(1000 * p) + k, min_exact=0.9)
+    check_rows(bits, "float32", None, None, 0.9, k, p, m, seed=8, offset=int(1000 * p) + k, min_exact=0.9)
+
+
+def test_fp32_coarse_bucket_edges_and_overflow():
+    """Cuts on the edges of coarse buckets (values 1, 1.125 and 1.25 and the
+    floats next to them, each repeated), and a bucket holding 20000 distinct
+    values with the top-p cut inside it: more than the list holds, so the row
+    takes the radix search."""
+    rng = np.random.default_rng(212)
+    cols = 30000
+    x = rng.standard_normal((2, cols)).astype(np.float32) - np.float32(3.0)
+    edges = np.array([1.0, 1.125, 1.25], np.float32)
+    near = np.concatenate([edges, np.nextafter(edges, np.float32(0)), np.nextafter(edges, np.float32(9))])
+    x[0, rng.choice(cols, near.size * 400, replace=False)] = np.repeat(near, 400)
+    x[1, :] = np.float32(-4.0)
+    x[1, rng.choice(cols, 20000, replace=False)] = np.float32(1.0) + np.arange(20000, dtype=np.float32) * np.float32(2.0 ** -21)
+    bits = x.view(np.uint32)
+    for (k, p, seed) in ((0, 0.5, 1), (0, 0.2, 2), (0, 0.8, 3), (1000, 1.0, 4), (2400, 1.0, 5), (500, 0.7, 6)):
+        say(f"[gpu] fp32 bucket edges / list overflow k={k} p={p}")
+        check_rows(bits, "float32", None, None, 1.0, k, p, 0.0, seed=seed, offset=seed, min_exact=0.9)
 
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
