@@ -697,28 +697,28 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   unsigned long long m = 0, sm = 0, tot_m = 0;
   if (use_p) {
     __shared__ unsigned long long s_own[THREADS];
-    constexpr int kBatch = 4;  // words read ahead per lane
+    constexpr int kBatch = 4;  // steps per batch: their words, masses and half-wave sums side by side
     for (int s0 = 0; s0 < 32; s0 += kBatch) {
       uint32_t wb[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) wb[j] = fine[(s0 + j) * THREADS + t];
+      unsigned long long mw[kBatch] = {};
+      if (__ballot((wb[0] | wb[1] | wb[2] | wb[3]) != 0u)) {  // else every total of the batch is 0
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const uint32_t word = static_cast<uint32_t>((s0 + j) * THREADS + t);
-        const uint32_t w = wb[j];
-        if (!__ballot(w != 0u)) {
-          if ((lane & 31) == 31) s_own[word / 32u] = 0ull;
-          continue;
-        }
-        const uint32_t ka = KW * word;  // the word's first key
-        unsigned long long mw = 0;
+        for (int j = 0; j < kBatch; ++j) {
+          const uint32_t ka = KW * static_cast<uint32_t>((s0 + j) * THREADS + t);  // the word's first key
 #pragma unroll
-        for (uint32_t e = 0; e < KW; ++e) {
-          const uint32_t n = count_in(w, e);
-          if (n && in_range(ka + e)) mw += static_cast<unsigned long long>(n) * mass(ka + e);
+          for (uint32_t e = 0; e < KW; ++e) {
+            const uint32_t n = count_in(wb[j], e);
+            if (n && in_range(ka + e)) mw[j] += static_cast<unsigned long long>(n) * mass(ka + e);
+          }
         }
-        mw = half_wave_scan(mw);  // lanes 31 and 63: each half-wave's total
-        if ((lane & 31) == 31) s_own[word / 32u] = mw;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) mw[j] = half_wave_scan(mw[j]);  // lanes 31 and 63: each half-wave's total
+      }
+      if ((lane & 31) == 31) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) s_own[static_cast<uint32_t>((s0 + j) * THREADS + t) / 32u] = mw[j];
       }
     }
     __syncthreads();
@@ -822,14 +822,19 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
 // the radix search.
 constexpr int kCoarseBuckets = 4096;
 constexpr uint32_t kCoarseShift = 20;  // bucket = order key >> 20
-constexpr uint32_t kListCap = 12288;   // listed candidates: 96 KB of keys and indices
+// The list: one region per wave of the 1024-thread block, each wave appending
+// to its own (no atomics); a wave that fills its region sends the row to the
+// radix search.
+constexpr uint32_t kCoarseListWaves = 16;
+constexpr uint32_t kCoarseListPerWave = 960;
+constexpr uint32_t kCoarseListCap = kCoarseListWaves * kCoarseListPerWave;  // 15360 keys and indices, 120 KB
 
 // Dynamic LDS of the fp32 1024-thread kernel this path uses (it has the
 // 131 KB of the 16-bit search): the coarse masses and counts (48 KB), then,
 // reusing the space, the list and the list search's 256-bin histograms.
 constexpr size_t coarse_lds_bytes() {
   const size_t hist = static_cast<size_t>(kCoarseBuckets) * (sizeof(unsigned long long) + sizeof(uint32_t));
-  const size_t list = static_cast<size_t>(kListCap) * 2 * sizeof(uint32_t) + 256 * (sizeof(unsigned long long) + sizeof(uint32_t));
+  const size_t list = static_cast<size_t>(kCoarseListCap) * 2 * sizeof(uint32_t) + 256 * (sizeof(unsigned long long) + sizeof(uint32_t));
   return hist > list ? hist : list;
 }
 
@@ -1472,13 +1477,13 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       have_cut = true;  // with bh == ~0u the cut is 0: every candidate is kept
       if (bh != ~0u) {
         // ---- draw: candidates above bucket bh by the walk, those inside listed
-        __shared__ uint32_t s_ln;
         uint32_t* lkey = reinterpret_cast<uint32_t*>(s_dyn);
-        uint32_t* lidx = lkey + kListCap;
+        uint32_t* lidx = lkey + kCoarseListCap;
         __syncthreads();  // the searches' reads of cm and cc are done before the list overwrites them
-        if (t == 0) s_ln = 0u;
-        __syncthreads();
         const int lane = lane_id();
+        uint32_t* wkey = lkey + wave * kCoarseListPerWave;  // this wave's region
+        uint32_t* widx = lidx + wave * kCoarseListPerWave;
+        uint32_t nw = 0;  // entries this wave has listed (the same in every lane)
         const auto group = [&](int32_t i0, const float* x, uint32_t bits) {
           uint32_t above = 0, inside = 0;
 #pragma unroll
@@ -1491,18 +1496,19 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
             }
           }
           if (__ballot(inside != 0u)) {  // every lane of the wave takes this branch or none
+            // this lane's entries go after those of the lanes below it
+            const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(inside));
+            const uint32_t incl = wave_prefix_sum(cnt);
+            uint32_t pos = nw + incl - cnt;
+            nw += lane63(incl);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-              const uint64_t bq = __ballot((inside >> q) & 1u);
-              if (!bq) continue;
-              uint32_t base = 0;
-              if (lane == 0) base = atomicAdd(&s_ln, static_cast<uint32_t>(__popcll(bq)));
-              base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
-              const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bq >> 32),
-                                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bq), 0u));
-              if (((inside >> q) & 1u) && pos < kListCap) {
-                lkey[pos] = order_key(x[q]);
-                lidx[pos] = static_cast<uint32_t>(i0 + q);
+              if ((inside >> q) & 1u) {
+                if (pos < kCoarseListPerWave) {
+                  wkey[pos] = order_key(x[q]);
+                  widx[pos] = static_cast<uint32_t>(i0 + q);
+                }
+                ++pos;
               }
             }
           }
@@ -1519,9 +1525,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           const uint32_t ok = t == 0 ? rv.load_tail(x) : 0u;
           group(rv.V & ~7, x, ok);
         }
-        __syncthreads();
-        const uint32_t n = s_ln;
-        if (n > kListCap) {
+        const bool over = __syncthreads_or(nw > kCoarseListPerWave);
+        if (over) {
           // the bucket holds more candidates than the list: the radix search below
           // takes the row over, and its draw replaces this one
           have_cut = false;
@@ -1532,7 +1537,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           // low 20 key bits (digits at bits 19..12, 11..4, 3..0), counting for
           // top-k and summing masses for top-p, as the radix passes do over the row
           const bool rk = use_k && bk_ == bh, rp = use_p && bp_ == bh;
-          unsigned long long* lh_m = reinterpret_cast<unsigned long long*>(lidx + kListCap);
+          unsigned long long* lh_m = reinterpret_cast<unsigned long long*>(lidx + kCoarseListCap);
           uint32_t* lh_n = reinterpret_cast<uint32_t*>(lh_m + 256);
           if (t == 0) s_sel = SelectState{bh << kCoarseShift, need_k - n_above, need_p - m_above, bh << kCoarseShift};
           uint32_t pmask = ~0u << kCoarseShift;
@@ -1543,8 +1548,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
             }
             __syncthreads();
             const uint32_t pk = s_sel.prefix_k, pp = s_sel.prefix_p;
-            for (uint32_t i = static_cast<uint32_t>(t); i < n; i += THREADS) {
-              const uint32_t key = lkey[i];
+            for (uint32_t i = static_cast<uint32_t>(lane); i < nw; i += 64u) {  // this wave's entries
+              const uint32_t key = wkey[i];
               const uint32_t d = (key >> shift) & 255u;
               if (rk && (key & pmask) == pk) atomicAdd(&lh_n[d], 1u);
               if (rp && (key & pmask) == pp) {
@@ -1578,11 +1583,11 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           }
           cut = max(rk ? s_sel.prefix_k : 0u, rp ? s_sel.prefix_p : 0u);
           // the listed candidates at or above the cut join the draw (min-p aside)
-          for (uint32_t i = static_cast<uint32_t>(t); i < n; i += THREADS) {
-            const uint32_t key = lkey[i];
+          for (uint32_t i = static_cast<uint32_t>(lane); i < nw; i += 64u) {  // this wave's entries
+            const uint32_t key = wkey[i];
             const float x = value_of_key(key);
             if (key >= cut && !(use_min_p && x * inv_t - zmax < ln_min_p)) {
-              const int32_t idx = static_cast<int32_t>(lidx[i]);
+              const int32_t idx = static_cast<int32_t>(widx[i]);
               uint32_t c4[4] = {static_cast<uint32_t>((tok0 + idx) >> 2), static_cast<uint32_t>(row_base + r),
                                 a.offset_lo, a.offset_hi};
               philox4x32_10(c4, a.seed_lo, a.seed_hi);

@@ -513,6 +513,27 @@ def test_fp32_coarse_bucket_edges_and_overflow():
         check_rows(bits, "float32", None, None, 1.0, k, p, 0.0, seed=seed, offset=seed, min_exact=0.9)
 
 
+def test_fp32_coarse_bucket_crowding_one_wave():
+    """The draw lists the cut bucket's candidates per wave (wave w of the
+    1024-thread block reads the groups g with g % 1024 in [64 w, 64 w + 64)).
+    1500 distinct values of one bucket placed in wave 0's groups fill its
+    region though the whole list would hold them: the row takes the radix
+    search.  A second row spreads the same values over the row."""
+    rng = np.random.default_rng(213)
+    cols = 40000
+    x = rng.standard_normal((2, cols)).astype(np.float32) - np.float32(3.0)
+    g = np.arange(cols // 8)
+    wave0 = np.flatnonzero((g % 1024) < 64)
+    pos0 = (wave0[:, None] * 8 + np.arange(8)).reshape(-1)
+    vals = np.float32(1.0) + np.arange(1500, dtype=np.float32) * np.float32(2.0 ** -21)
+    x[0, rng.choice(pos0, 1500, replace=False)] = vals
+    x[1, rng.choice(cols, 1500, replace=False)] = vals
+    bits = x.view(np.uint32)
+    for (k, p, seed) in ((0, 0.5, 1), (700, 1.0, 2), (300, 0.6, 3)):
+        say(f"[gpu] fp32 list crowding one wave k={k} p={p}")
+        check_rows(bits, "float32", None, None, 1.0, k, p, 0.0, seed=seed, offset=seed, min_exact=0.9)
+
+
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_short_rows_with_filters(dtype):
     """16-bit rows shorter than one 8-token group, or with a ragged last
