@@ -360,6 +360,7 @@ def main():
         extras["ceiling_cold"]["own_copy_same_rows"] = own_copy(torch, dev, mb, R, wl.logits.shape[1],
                                                                  wl.mask.shape[1], args.steps, stream)
         extras["gated_rows_cold"] = gated_rows(torch, dev, mb, workloads, args.steps, stream)
+        extras["out_of_place_index_list_cold"] = out_of_place_listed(torch, dev, mb, workloads, args.steps, stream)
         extras["vocab_shard_tp8_cold"] = vocab_shard(torch, dev, mb, wl, args.steps, stream)
         extras["host_path"] = host_path(torch, mb, wl, eff)
         extras["mask_upload_overlap"] = upload_overlap(torch, dev, mb, wl)
@@ -565,6 +566,44 @@ def gated_rows(torch, dev, mb, workloads, steps, stream):
             "gated_with_report": {"ms_per_step": t_rep, "GBps": eff / (t_rep * 1e-3) / 1e9},
             "gated": {"ms_per_step": t_gate, "GBps": eff / (t_gate * 1e-3) / 1e9},
             "index_list_same_rows": {"ms_per_step": t_idx, "GBps": eff / (t_idx * 1e-3) / 1e9}}
+
+
+def out_of_place_listed(torch, dev, mb, workloads, steps, stream):
+    """Out of place with an index list on the speculative-verify shape.
+
+    fp16 logits [1024, 32000] into a separate output, the mask applied to 128
+    listed rows (random, unsorted) and every other row copied: one pass over
+    every row (each block finds whether the list holds its row).  Effective
+    bytes: every row read and written once, plus the listed rows' mask
+    words.  Beside it, the same call with no list (every row masked) and a
+    list of 1100 rows, past the one-pass limit of 1024 (a copy, then the
+    in-place apply of the listed rows on the output).  Cold rotation.
+    """
+    import numpy as np
+
+    wl = workloads.verify_fp16()
+    rng = np.random.default_rng(9)
+    W = (wl.cols + 31) // 32
+    nsets = max(2, math.ceil(2 * INFINITY_CACHE / (2 * wl.logits.nbytes + wl.mask.nbytes)))
+    sets = [(torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(torch.float16), torch.from_numpy(wl.mask).to(dev),
+             torch.empty(wl.rows, wl.cols, dtype=torch.float16, device=dev)) for _ in range(nsets)]
+    out = {}
+    for label, n in (("list_128", 128), ("no_list", None), ("list_1100_past_one_pass", 1100)):
+        idx = None
+        if n is not None:
+            idx = torch.from_numpy(rng.choice(wl.rows, size=min(n, wl.rows), replace=False).astype(np.int32)).to(dev)
+            if n > wl.rows:
+                idx = torch.cat([idx, idx[: n - wl.rows]])
+        listed = wl.rows if n is None else int(idx.numel())
+        eff = wl.rows * wl.cols * 2 * 2 + min(listed, wl.rows) * W * 4
+        ms = graph_ms(torch, lambda k: mb.mi_apply_bitmask_out(sets[k % nsets][0], sets[k % nsets][1],
+                                                               sets[k % nsets][2], None, idx, -65504.0),
+                      steps, stream)
+        out[label] = {"ms_per_step": ms, "effective_bytes": eff, "GBps": eff / (ms * 1e-3) / 1e9}
+    del sets
+    torch.cuda.empty_cache()
+    out["workload"] = "fp16 [1024,32000] out of place, fill -65504, verify_fp16 masks"
+    return out
 
 
 def upload_overlap(torch, dev, mb, wl, steps=30):

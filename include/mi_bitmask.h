@@ -122,8 +122,10 @@ mi_status_t mi_apply_bitmask_inplace(
  * masked copy over [0, V) and a plain copy over [V, cols); rows outside an
  * index list are plain copies.  out == logits with equal pitch is the
  * in-place apply; any other overlap of out with logits, mask or indices is
- * MI_ERR_ALIAS.  With an index list the call runs two kernels (copy, then
- * the in-place apply on out).
+ * MI_ERR_ALIAS.  One kernel, one pass over every row, without an index list
+ * or with one of at most 1024 entries (each block looks for its row in the
+ * list); with a longer list, two kernels (a copy, then the in-place apply of
+ * the listed rows on out).
  */
 mi_status_t mi_apply_bitmask_out(
     void *out, int64_t out_row_stride,

@@ -82,6 +82,25 @@ struct RowMap {
   __device__ __forceinline__ bool gated_off(int64_t r) const { return gate && gate[r] == 0; }
 };
 
+// Out of place with a short index list, in one pass over every row: a block
+// masks its row only when the list holds it (XGrammar "Bitmask Operations",
+// Notes: Indices), and copies it otherwise.  Every thread compares its share
+// of the list with the row, and a block-wide OR decides; a listed value
+// outside [0, row_limit) matches no row, as in the in-place apply.  Called
+// by every thread of the block (it holds a barrier).
+struct ListedRows {
+  const int32_t* indices = nullptr;  // nullptr: no list (the caller's `apply` stands)
+  int32_t count = 0;
+  int64_t row_limit = 0;
+
+  __device__ __forceinline__ int32_t holds(int64_t r) const {
+    bool found = false;
+    for (int32_t i = static_cast<int32_t>(threadIdx.x); i < count; i += kBlock)
+      found |= static_cast<int64_t>(indices[i]) == r;
+    return (__syncthreads_or(found) != 0 && r < row_limit) ? 1 : 0;
+  }
+};
+
 // Per-row report for the gated apply: 1 when row r still admits one of its
 // first V tokens (TensorRT-Edge-LLM "Guided Decoder": rowHasAnyToken; an
 // all-zero row is unsatisfiable).  A gated-off row is not masked, so it
@@ -318,9 +337,10 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void out_scalar(
     T* __restrict__ out, int64_t os, const T* __restrict__ in, int64_t ls,
     const uint32_t* __restrict__ mask, int64_t ms, int32_t V, int32_t cols, int32_t apply,
-    int64_t slot_base, uint32_t chunks, T fill) {
+    ListedRows listed, int64_t slot_base, uint32_t chunks, T fill) {
   const int64_t r = slot_base + blockIdx.x / chunks;
   const int32_t chunk = static_cast<int32_t>(blockIdx.x % chunks);
+  if (listed.indices) apply = listed.holds(r);
   T* __restrict__ orow = out + r * os;
   const T* __restrict__ irow = in + r * ls;
   const uint32_t* __restrict__ mrow = mask + r * ms;
@@ -346,11 +366,12 @@ template <typename T, int U, int POLICY>
 __global__ __launch_bounds__(kBlock) void out_vec(
     T* __restrict__ out, int64_t os, const T* __restrict__ in, int64_t ls,
     const uint32_t* __restrict__ mask, int64_t ms, int32_t V, int32_t W, int32_t cols,
-    int32_t apply, int64_t slot_base, uint32_t chunks, T fill) {
+    int32_t apply, ListedRows listed, int64_t slot_base, uint32_t chunks, T fill) {
   constexpr int VW = Bits16B<T>::VW;
   constexpr uint32_t FULL = Bits16B<T>::FULL;
   const int64_t r = slot_base + blockIdx.x / chunks;
   const int32_t chunk = static_cast<int32_t>(blockIdx.x % chunks);
+  if (listed.indices) apply = listed.holds(r);
   T* __restrict__ orow = out + r * os;
   const T* __restrict__ irow = in + r * ls;
   const uint32_t* __restrict__ mrow = mask + r * ms;

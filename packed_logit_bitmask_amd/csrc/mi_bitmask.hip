@@ -54,6 +54,10 @@ VecShape inplace_shape(int64_t write_bytes) {
 
 constexpr VecShape kOutShape{2, mi::kStoreDeviceStream};
 
+// Out of place with an index list: one fused pass up to this many entries
+// (each block compares its row with every entry), copy then in place beyond.
+constexpr int64_t kFusedListMax = 1024;
+
 // Launch over `slots` row slots, `chunks` blocks per slot, splitting into
 // several launches when one grid would be too large.  With `extra_per_slot`
 // set, each launch also carries one extra block per slot (the per-row report
@@ -129,10 +133,12 @@ mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64
   }
 }
 
-// Out of place over every row: apply != 0 masks [0, V), apply == 0 copies.
+// Out of place over every row: apply != 0 masks [0, V), apply == 0 copies;
+// with `listed` set, only the rows the list holds are masked.
 template <typename T>
 mi_status_t run_out(void* out_v, int64_t os, const void* in_v, int64_t ls, const int32_t* mask_i, int64_t ms,
-                    int64_t rows, int64_t cols, const Plan& p, int32_t apply, bool vec, hipStream_t stream) {
+                    int64_t rows, int64_t cols, const Plan& p, int32_t apply, const mi::ListedRows& listed, bool vec,
+                    hipStream_t stream) {
   T* out = static_cast<T*>(out_v);
   const T* in = static_cast<const T*>(in_v);
   const uint32_t* mask = reinterpret_cast<const uint32_t*>(mask_i);
@@ -145,13 +151,13 @@ mi_status_t run_out(void* out_v, int64_t os, const void* in_v, int64_t ls, const
     const int64_t chunks = std::max<int64_t>(1, (cols / VW + per - 1) / per);
     launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t) {
       mi::out_vec<T, kOutShape.unroll, kOutShape.policy><<<blocks, mi::kBlock, 0, stream>>>(
-          out, os, in, ls, mask, ms, V, W, C, apply, s0, ch, fill);
+          out, os, in, ls, mask, ms, V, W, C, apply, listed, s0, ch, fill);
     });
     return after_launch("out_vec");
   }
   const int64_t chunks = (cols + mi::kBlock * 8 - 1) / (mi::kBlock * 8);
   launch_slots(rows, chunks, [&](int64_t s0, uint32_t blocks, uint32_t ch, uint32_t) {
-    mi::out_scalar<T><<<blocks, mi::kBlock, 0, stream>>>(out, os, in, ls, mask, ms, V, C, apply, s0, ch, fill);
+    mi::out_scalar<T><<<blocks, mi::kBlock, 0, stream>>>(out, os, in, ls, mask, ms, V, C, apply, listed, s0, ch, fill);
   });
   return after_launch("out_scalar");
 }
@@ -208,13 +214,18 @@ mi_status_t out_impl(void* out, int64_t os, const void* logits, mi_dtype_t dtype
       (reinterpret_cast<uintptr_t>(out) - reinterpret_cast<uintptr_t>(logits)) % 16 == 0 &&
       (rows == 1 || ((os - ls) * p.esize) % 16 == 0);
   const bool vec = variant == MI_VARIANT_SCALAR ? false : same_phase;
-  // Without an index list every row is processed in one fused pass.  With one,
+  // One fused pass over every row: without an index list each row is masked;
+  // with a list of at most kFusedListMax entries each block finds whether the
+  // list holds its row.  A longer list would cost every block a long scan:
   // out first becomes a copy of logits and the listed rows are then masked in
   // place on out (rows outside the list stay copies).
+  const bool fused_list = indices != nullptr && p.V > 0 && num_indices > 0 && num_indices <= kFusedListMax;
   const int32_t apply = (indices == nullptr && p.V > 0) ? 1 : 0;
-  st = p.esize == 4 ? run_out<uint32_t>(out, os, logits, ls, mask, ms, rows, cols, p, apply, vec, stream)
-                    : run_out<uint16_t>(out, os, logits, ls, mask, ms, rows, cols, p, apply, vec, stream);
-  if (st != MI_OK || indices == nullptr || p.V == 0 || p.R == 0) return st;
+  mi::ListedRows listed;
+  if (fused_list) listed = mi::ListedRows{indices, static_cast<int32_t>(num_indices), p.row_limit};
+  st = p.esize == 4 ? run_out<uint32_t>(out, os, logits, ls, mask, ms, rows, cols, p, apply, listed, vec, stream)
+                    : run_out<uint16_t>(out, os, logits, ls, mask, ms, rows, cols, p, apply, listed, vec, stream);
+  if (st != MI_OK || indices == nullptr || fused_list || p.V == 0 || p.R == 0) return st;
   const mi_variant_t iv = variant == MI_VARIANT_SCALAR ? MI_VARIANT_SCALAR : auto_inplace(dtype);
   return p.esize == 4 ? run_inplace<uint32_t>(out, os, mask, ms, indices, p, iv, stream)
                       : run_inplace<uint16_t>(out, os, mask, ms, indices, p, iv, stream);

@@ -285,6 +285,27 @@ def test_out_of_range_device_indices_are_skipped():
         run_out_case(rng, wl, variant, indices_dev=dev_idx, expect_rows=[4, 2, 0])
 
 
+@pytest.mark.parametrize("n_list", [1, 1023, 1024, 1025, 3000])
+def test_out_of_place_index_list_sizes(n_list):
+    """Out of place with an index list: up to 1024 entries in one pass (each
+    block looks for its row in the list), beyond that a copy then the in-place
+    apply.  Lists on both sides of the limit, with duplicates, entries past
+    the mask rows and past the logits rows, and negative entries; more logits
+    rows than mask rows."""
+    rng = np.random.default_rng(8000 + n_list)
+    rows, mask_rows = 3100, 3050
+    wl, _, _ = workloads.random_case(rng, "float16", rows, 700, mask_rows=mask_rows, vocab_size=690, density=0.3)
+    valid = rng.permutation(mask_rows)[: max(1, n_list - 6)]
+    extra = np.array([-1, mask_rows, rows - 1, rows, 1 << 30, int(valid[0])], dtype=np.int64)[: n_list - valid.size]
+    idx = np.concatenate([valid, extra]).astype(np.int32)
+    rng.shuffle(idx)
+    expect = sorted({int(i) for i in idx if 0 <= i < mask_rows})
+    say(f"[gpu] out of place, index list of {idx.size}")
+    for variant in OUT_VARIANTS:
+        run_out_case(rng, wl, variant, stride=703, out_stride=701, guard=2, out_guard=3,
+                     indices_dev=torch.from_numpy(idx).to("cuda"), expect_rows=expect)
+
+
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
 def test_degenerate_shapes(dtype):
     rng = np.random.default_rng(8)
