@@ -123,7 +123,7 @@ def copy_calibration():
 
 
 def sampler_calls(n):
-    """N eager calls of the fused sampler per mode on the two shapes the sampler figures use.
+    """N eager calls of the fused sampler per mode on the three shapes the sampler figures use.
 
     Under rocprofv3 --pmc each call is one dispatch, in the order printed.
     """
@@ -134,10 +134,13 @@ def sampler_calls(n):
     from packed_logit_bitmask_amd import workloads
 
     dev = torch.device("cuda:0")
-    for label, wl in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0)),
-                      ("B1024_V32000_fp16", workloads.verify_fp16())):
+    for label, wl, fp32 in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0), False),
+                            ("B1024_V32000_fp16", workloads.verify_fp16(), False),
+                            ("B256_V128000_fp32", workloads.mixed_bf16(n_indices=0), True)):
         tdt = torch.bfloat16 if wl.dtype == "bfloat16" else torch.float16
         x = torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(tdt)
+        if fp32:
+            x = x.float().contiguous()
         m = torch.from_numpy(wl.mask).to(dev)
         tok = torch.empty(wl.rows, dtype=torch.int64, device=dev)
         for mode, kw in SAMPLER_MODES:
@@ -341,8 +344,14 @@ def main():
 
     ms_step = timed(args.variant, args.steps, args.warmup, rotate=True)
     gbps = eff / (ms_step * 1e-3) / 1e9
+    print(f"# headline: {ms_step * 1e3:.3f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
 
     extras = {}
+
+    def phase(name, value):
+        extras[name] = value
+        print(f"# {name} done", file=sys.stderr, flush=True)
+
     if not args.no_extras:
         warm = timed(args.variant, args.steps, 10, rotate=False)
         warm_res = timed("vec_resident", args.steps, 10, rotate=False)
@@ -355,22 +364,22 @@ def main():
         for var in ("scalar", "vec", "wronly", "vec_resident"):
             t = timed(var, args.steps, 10, rotate=True)
             per[var] = {"ms_per_step": t, "GBps": eff / (t * 1e-3) / 1e9}
-        extras["variants_cold"] = per
-        extras["ceiling_cold"] = ceilings(torch, dev, eff, nsets, args.steps, stream, rmw_bytes=R * V * 2)
+        phase("variants_cold", per)
+        phase("ceiling_cold", ceilings(torch, dev, eff, nsets, args.steps, stream, rmw_bytes=R * V * 2))
         extras["ceiling_cold"]["own_copy_same_rows"] = own_copy(torch, dev, mb, R, wl.logits.shape[1],
                                                                  wl.mask.shape[1], args.steps, stream)
-        extras["gated_rows_cold"] = gated_rows(torch, dev, mb, workloads, args.steps, stream)
-        extras["out_of_place_index_list_cold"] = out_of_place_listed(torch, dev, mb, workloads, args.steps, stream)
-        extras["vocab_shard_tp8_cold"] = vocab_shard(torch, dev, mb, wl, args.steps, stream)
-        extras["host_path"] = host_path(torch, mb, wl, eff)
-        extras["mask_upload_overlap"] = upload_overlap(torch, dev, mb, wl)
-        extras["fused_sampler_cold"] = sampler_times(torch, dev, mb, workloads, stream)
-        extras["fused_sampler_small_batch_cold"] = sampler_small_batch(torch, dev, mb, workloads, stream)
+        phase("gated_rows_cold", gated_rows(torch, dev, mb, workloads, args.steps, stream))
+        phase("out_of_place_index_list_cold", out_of_place_listed(torch, dev, mb, workloads, args.steps, stream))
+        phase("vocab_shard_tp8_cold", vocab_shard(torch, dev, mb, wl, args.steps, stream))
+        phase("host_path", host_path(torch, mb, wl, eff))
+        phase("mask_upload_overlap", upload_overlap(torch, dev, mb, wl))
+        phase("fused_sampler_cold", sampler_times(torch, dev, mb, workloads, stream))
+        phase("fused_sampler_small_batch_cold", sampler_small_batch(torch, dev, mb, workloads, stream))
 
     cpu = cpu_baseline(wl, eff, args.cpu_seconds)
     if not args.no_extras:
-        extras["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl, eff, args.cpu_seconds / 2)
-        extras["cpu_baseline_python_small"] = cpu_baseline_python()
+        phase("cpu_baseline_all_cores", cpu_baseline_all_cores(wl, eff, args.cpu_seconds / 2))
+        phase("cpu_baseline_python_small", cpu_baseline_python())
 
     traffic = counted_traffic()
     line = {
@@ -665,9 +674,10 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
     read of the logits of every row plus its mask words; the kernel reads the
     row once per pass (greedy 1, unfiltered 1; with top-k or top-p, 16-bit
     rows take 2 -- the key histogram and the draw -- or 1 when a short row is
-    held in registers between them; fp32 rows take a radix pass per 8-bit
-    digit, 4, plus the maximum for top-p and min-p).  The fp32 shape holds the
-    bf16 shape's values widened.  Cold: rotating buffer sets.
+    held in registers between them; fp32 rows take 2 -- the coarse 12-bit
+    bucket pass and the draw that lists the cut's bucket -- plus the maximum
+    for top-p and min-p).  The fp32 shape holds the bf16 shape's values
+    widened.  Cold: rotating buffer sets.
     """
     import numpy as np
 

@@ -30,11 +30,15 @@
 //            blocks: one pass counts the tokens the mask allows under each
 //            of the 65536 16-bit keys (LDS, 16- or 8-bit counters); the
 //            maximum and both cuts follow from the counts (fine_search).
-//            The radix passes below remain for fp32 and for a row where one
-//            key holds more tokens than its counter can (65536 or 256);
-//   fp32 k   fp32 rows with top-k alone, in 1024-thread blocks: two passes
-//            of 16-bit keys, the top half of each order key and then the low
-//            half inside the bucket holding the cut (fp32_topk_cut);
+//            The radix passes below remain for a row where one key holds
+//            more tokens than its counter can (65536 or 256);
+//   fp32     fp32 rows with top-k or top-p in 1024-thread blocks: one pass
+//            counts and sums mass under the top 12 bits of each order key
+//            (coarse_hist32), a search picks the cut's bucket, and the draw
+//            pass lists the candidates of that bucket in LDS, where a radix
+//            select over the low 20 bits gives the exact cut; a bucket too
+//            crowded for the list, and fp32 rows in smaller blocks, take
+//            the radix passes below;
 //   top-k    radix search over an order-preserving 32-bit key of the logit
 //            (temperature > 0 keeps the order), counting tokens: the key of
 //            the k-th largest logit, ties kept -- exact integer work;
