@@ -396,6 +396,38 @@ def test_fuzz_filtered_16bit_many_rows(dtype):
         check_rows(bits, dtype, mask, V, T, k, p, m, seed=200 + case, offset=case, min_exact=0.9)
 
 
+@pytest.mark.parametrize("dtype,R", [("float16", 1100), ("bfloat16", 1101), ("float32", 1030)])
+def test_tokens_independent_of_batch_size(dtype, R):
+    """The generator is keyed by the row, so a row's token does not depend on
+    how many rows share the launch, although the kernel does: 16-bit rows
+    take 1024-thread blocks with 16-bit counters up to 256 rows and 512-thread
+    blocks with 8-bit counters beyond; fp32 rows the coarse-bucket cut in
+    1024-thread blocks up to 256 rows and the radix search in 256-thread
+    blocks beyond.  Rows of mixed densities (all allowed, none, sparse) and
+    per-row filters; the first 256 and 520 rows of the batch must draw the
+    same tokens as the whole batch, and a sample of rows is checked against
+    the oracle."""
+    rng = np.random.default_rng(71 + R)
+    cols = 3000 if dtype != "float32" else 700
+    bits = random_logits(rng, dtype, R, cols)
+    kind = rng.choice(4, R, p=[0.2, 0.05, 0.5, 0.25])           # all allowed, none, sparse, medium
+    dens = np.choose(kind, [1.0, 0.0, 0.05, 0.5])[:, None]
+    allowed = rng.random((R, cols)) < dens
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    T = rng.choice([0.6, 1.0, 1.3], R).astype(np.float32)
+    k = rng.choice([0, 5, 60], R).astype(np.int32)
+    p = rng.choice([1.0, 0.9, 0.5], R).astype(np.float32)
+    m = rng.choice([0.0, 0.03], R).astype(np.float32)
+    say(f"[gpu] sampler tokens independent of batch size {dtype} R={R}")
+    tok = check_rows(bits, dtype, mask, None, T, k, p, m, seed=73, offset=5, rows=list(range(0, R, 7)),
+                     min_exact=0.9)
+    assert (tok[kind == 1] == -1).all() and (tok[kind != 1] >= 0).all()
+    for n in (256, 520):
+        part = check_rows(bits[:n], dtype, mask[:n], None, T[:n], k[:n], p[:n], m[:n], seed=73, offset=5,
+                          rows=[], min_exact=0.0)
+        assert (part == tok[:n]).all(), f"{int((part != tok[:n]).sum())} of the first {n} rows differ"
+
+
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_kept_tokens_crowding_one_wave_many_rows(dtype):
     """As the test above for 512-thread blocks (more rows than compute units):
