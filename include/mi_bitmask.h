@@ -261,9 +261,11 @@ mi_status_t mi_apply_bitmask_sample_ws(
  * forbid hipMalloc.  It takes no workspace argument; the split path's
  * workspace is a device array inside the library (8 393 216 bytes, enough
  * for 32 rows), which each GPU the library runs on holds until the process
- * ends.  Its address is looked up (hipGetDevice, hipGetSymbolAddress) on
- * the first call made with each device current; the call itself allocates
- * nothing and frees nothing.  The stream must belong to the current device.
+ * ends.  The array used is that of the GPU the stream runs on (the current
+ * device for the null stream); its address is looked up once per device
+ * (hipGetSymbolAddress with that device current, switching to it and back
+ * if the stream's device is not current); the call itself allocates
+ * nothing and frees nothing.
  *
  * A batch whose split would need more than that array -- more than 32 bf16
  * or fp16 rows (at most 64) of at least 8192 tokens, with top-k, top-p or

@@ -93,17 +93,31 @@ constexpr int kMaxDevices = 256;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-// The device address of `scratch` on the current device, looked up on the
-// first call made with that device current.
-mi_status_t scratch_address(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+// The device address of `scratch` on the GPU that `stream` runs on (the
+// current device for the null stream), looked up once per device with that
+// device current: each GPU holds its own copy of the array.
+mi_status_t scratch_address(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return fail(MI_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(MI_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
   if (dev < 0 || dev >= kMaxDevices) return fail(MI_ERR_HIP, "device %d beyond the %d the library tracks", dev, kMaxDevices);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
+    if (dev != cur) {
+      e = hipSetDevice(dev);
+      if (e != hipSuccess) return fail(MI_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    }
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t back = hipSetDevice(cur);
+      if (back != hipSuccess) return fail(MI_ERR_HIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(back));
+    }
     if (e != hipSuccess || !p)
       return fail(MI_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
     g_scratch_ptr[dev] = p;
@@ -171,7 +185,7 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
   }
   if (rows == 0) return MI_OK;
   if (use_scratch && params_filter && ws_need > 0) {  // every argument check has passed
-    st = scratch_address(&workspace);
+    st = scratch_address(stream, &workspace);
     if (st != MI_OK) return st;
     workspace_bytes = ws_need;
     use_ws = true;
