@@ -809,6 +809,242 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   return true;
 }
 
+// ---- sparse 16-bit rows with top-k or top-p in 512-thread blocks (batches
+// of many rows): when the mask allows at most kSparseMax tokens below V,
+// the candidates are listed in LDS (token and 16-bit key) from the groups
+// the mask allows -- the logits of other groups are not read -- and both
+// cuts come from a radix select over the list (two 8-bit digits of the
+// key), counting for top-k and summing the same fixed-point masses for
+// top-p: the same cuts as fine_search's histogram over all 65536 keys,
+// whose clearing, filling and scanning cost as much for 1600 candidates as
+// for 32000.  The draw then runs on the list.
+constexpr uint32_t kSparseMax = 4096;
+constexpr uint32_t kSparseSlots = 2 * kSparseMax;  // list slots, an equal region per wave
+constexpr size_t sparse_lds_bytes() { return kSparseSlots * (4 + 2) + 256 * (4 + 8); }
+
+// The row's candidates, as sparse_search left them: wave w's entries in
+// slots [w * per_wave, w * per_wave + nw).
+template <int THREADS>
+struct SparseList {
+  static constexpr uint32_t kPerWave = kSparseSlots / (THREADS / 64);
+  const uint32_t* idx;   // token
+  const uint16_t* key;   // 16-bit order key
+  __device__ __forceinline__ explicit SparseList(const uint32_t* lds)
+      : idx(lds), key(reinterpret_cast<const uint16_t*>(lds + kSparseSlots)) {}
+};
+
+// Whether the row is sparse (the mask allows at most kSparseMax tokens); if
+// so, lists its candidates, sets *best (-inf without a candidate) and
+// *cut16 (the lower of the two cuts as a 16-bit key, 0 to keep every
+// candidate), leaves this wave's entry count in *nw and returns true.
+// Otherwise returns false and only LDS has changed.  Block-uniform; ends
+// with a barrier.
+template <typename D, int THREADS>
+__device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* lds, float inv_t, bool use_k,
+                                              int32_t top_k, bool use_p, float top_p, float* best, uint32_t* cut16,
+                                              uint32_t* nw_out) {
+  constexpr int kWaves = THREADS / 64;
+  constexpr uint32_t kPerWave = SparseList<THREADS>::kPerWave;
+  static_assert(sparse_lds_bytes() <= sample_fine_bytes(THREADS), "the list fits the histogram's LDS");
+  uint32_t* lidx = lds;
+  uint16_t* lkey = reinterpret_cast<uint16_t*>(lds + kSparseSlots);
+  uint32_t* hn = lds + kSparseSlots + kSparseSlots / 2;
+  unsigned long long* hm = reinterpret_cast<unsigned long long*>(hn + 256);
+  __shared__ uint32_t s_red[kWaves], s_cnt[kWaves];
+  __shared__ unsigned long long s_redm[kWaves];
+  __shared__ SelectState s_ss;
+  const int t = static_cast<int>(threadIdx.x);
+  const int lane = lane_id(), wave = t >> 6;
+  const int32_t nfull = rv.V >> 3;
+  const int32_t ngroups = (rv.V + 7) >> 3;  // the last one partial when V % 8 != 0
+  // group g's mask bits below V (a group past the row loads nothing and has none)
+  const auto gbits = [&](int32_t g) {
+    uint32_t b = (load_word(rv.rm, g < ngroups ? (g >> 2) * 4 : kSkip) >> ((g & 3) * 8)) & 0xFFu;
+    if (g == nfull) b &= (1u << (rv.V & 7)) - 1u;
+    return b;
+  };
+  const auto block_sum = [&](uint32_t x) {
+    x = lane63(wave_prefix_sum(x));
+    __syncthreads();
+    if (lane == 0) s_red[wave] = x;
+    __syncthreads();
+    uint32_t sum = 0;
+    for (int w = 0; w < kWaves; ++w) sum += s_red[w];
+    return sum;
+  };
+
+  // ---- the allowed tokens' logits (only groups the mask allows are read),
+  // and the candidates listed in this wave's region: allowed tokens with
+  // finite values
+  uint32_t nw = 0;  // this wave's entries (the same in every lane)
+  const uint32_t region = static_cast<uint32_t>(wave) * kPerWave;
+  const auto load_values = [&](int32_t base, const uint32_t (&b)[8], uint32_t (&v)[8][4]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int32_t g = base + j * THREADS + t;
+      if (rv.aligned && g < nfull) {
+        const uint4 q4 = load16(rv.rl, b[j] ? g * 16 : kSkip);
+        v[j][0] = q4.x;
+        v[j][1] = q4.y;
+        v[j][2] = q4.z;
+        v[j][3] = q4.w;
+      } else {  // a misaligned row, or the partial last group: the allowed tokens one by one
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+              rv.rl, ((b[j] >> (2 * q2)) & 1u) ? (8 * g + 2 * q2) * 2 : kSkip, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+              rv.rl, ((b[j] >> (2 * q2 + 1)) & 1u) ? (8 * g + 2 * q2 + 1) * 2 : kSkip, 0, 0);
+          v[j][q2] = lo | (hi << 16);
+        }
+      }
+    }
+  };
+  const auto list_values = [&](int32_t base, const uint32_t (&b)[8], const uint32_t (&v)[8][4]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int32_t g = base + j * THREADS + t;
+      uint32_t keys[8];
+      uint32_t cand = 0;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const uint32_t k2 = order_key16x2(v[j][q2]);
+        keys[2 * q2] = k2 & 0xFFFFu;
+        keys[2 * q2 + 1] = k2 >> 16;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        cand |= (((b[j] >> q) & 1u) && keys[q] - D::kKey16Lo <= D::kKey16Hi - D::kKey16Lo ? 1u : 0u) << q;
+      if (__ballot(cand != 0u)) {  // this lane's entries go after those of the lanes below it
+        const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(cand));
+        const uint32_t incl = wave_prefix_sum(cnt);
+        uint32_t pos = nw + incl - cnt;
+        nw += lane63(incl);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if ((cand >> q) & 1u) {
+            if (pos < kPerWave) {
+              lidx[region + pos] = static_cast<uint32_t>(8 * g + q);
+              lkey[region + pos] = static_cast<uint16_t>(keys[q]);
+            }
+            ++pos;
+          }
+        }
+      }
+    }
+  };
+  // the count first, from the mask alone: a dense row reads no logits here
+  uint32_t allowed = 0;
+  for (int32_t base = 0; base < ngroups; base += 8 * THREADS) {
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = gbits(base + j * THREADS + t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) allowed += __builtin_popcount(b[j]);
+  }
+  if (block_sum(allowed) > kSparseMax) return false;
+  for (int32_t base = 0; base < ngroups; base += 8 * THREADS) {
+    uint32_t b[8], v[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = gbits(base + j * THREADS + t);
+    load_values(base, b, v);
+    list_values(base, b, v);
+  }
+
+  // ---- the largest candidate and the candidate count; a wave whose
+  // region overflowed sends the row to the histogram search
+  uint32_t km = 0;
+  for (uint32_t i = static_cast<uint32_t>(lane); i < min(nw, kPerWave); i += 64u)
+    km = max(km, static_cast<uint32_t>(lkey[region + i]));
+  km = wave_max(km);
+  __syncthreads();
+  if (lane == 0) {
+    s_red[wave] = km;
+    s_cnt[wave] = nw;
+  }
+  __syncthreads();
+  km = 0;
+  uint32_t ntot = 0;
+  bool over = false;
+  for (int w = 0; w < kWaves; ++w) {
+    km = max(km, s_red[w]);
+    ntot += s_cnt[w];
+    over |= s_cnt[w] > kPerWave;
+  }
+  if (over) return false;
+  *nw_out = nw;
+  *cut16 = 0u;
+  if (km == 0u) {
+    *best = -__builtin_inff();
+    return true;
+  }
+  *best = D::value(static_cast<typename D::Bits>(bits_of_key16(km)));
+  const float zmax = *best * inv_t;
+  const auto mass = [&](uint32_t k) {
+    return fixed_mass(D::value(static_cast<typename D::Bits>(bits_of_key16(k))), inv_t, zmax);
+  };
+
+  // ---- the cuts: a radix select over the list, top-k by counts, top-p by masses
+  unsigned long long z = 0;
+  if (use_p) {
+    for (uint32_t i = static_cast<uint32_t>(lane); i < nw; i += 64u) z += mass(lkey[region + i]);
+    z = lane63(wave_prefix_sum(z));
+    __syncthreads();
+    if (lane == 0) s_redm[wave] = z;
+    __syncthreads();
+    z = 0;
+    for (int w = 0; w < kWaves; ++w) z += s_redm[w];
+  }
+  const bool do_k = use_k && static_cast<uint32_t>(top_k) <= ntot;  // k beyond the candidates keeps all
+  const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(z);
+  const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
+  const unsigned long long need_p = target ? target : 1ull;  // p <= 0 keeps just the largest value
+  if (!do_k && !use_p) return true;
+  if (t == 0) s_ss = SelectState{0u, static_cast<uint32_t>(top_k), need_p, 0u};
+  for (int shift = 8; shift >= 0; shift -= 8) {
+    const uint32_t pmask = shift == 8 ? 0u : 0xFF00u;
+    for (int i = t; i < 256; i += THREADS) {
+      hn[i] = 0u;
+      hm[i] = 0ull;
+    }
+    __syncthreads();
+    const uint32_t pk = s_ss.prefix_k, pp = s_ss.prefix_p;
+    for (uint32_t i = static_cast<uint32_t>(lane); i < nw; i += 64u) {
+      const uint32_t key = lkey[region + i];
+      const uint32_t d = (key >> shift) & 255u;
+      if (do_k && (key & pmask) == pk) atomicAdd(&hn[d], 1u);
+      if (use_p && (key & pmask) == pp) {
+        const uint32_t m = mass(key);
+        if (m) atomicAdd(&hm[d], static_cast<unsigned long long>(m));
+      }
+    }
+    __syncthreads();
+    if (do_k && wave == 0) {
+      const WaveSuffix<uint32_t> ws(hn);
+      int d;
+      uint32_t ab;
+      ws.pick(s_ss.need_k, &d, &ab);
+      if (lane == 0) {
+        s_ss.prefix_k |= static_cast<uint32_t>(d) << shift;
+        s_ss.need_k -= ab;
+      }
+    }
+    if (use_p && wave == 1) {
+      const WaveSuffix<unsigned long long> ws(hm);
+      int d;
+      unsigned long long ab;
+      ws.pick(s_ss.need_p, &d, &ab);
+      if (lane == 0) {
+        s_ss.prefix_p |= static_cast<uint32_t>(d) << shift;
+        s_ss.need_p -= ab;
+      }
+    }
+    __syncthreads();
+  }
+  *cut16 = max(do_k ? s_ss.prefix_k : 0u, use_p ? s_ss.prefix_p : 0u);
+  return true;
+}
+
 // ---- fp32 rows with top-k or top-p, in 1024-thread blocks: the cut from one
 // coarse pass and a list of the tokens in the bucket that holds it.
 //
@@ -1293,6 +1529,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // A 16-bit row with a filter and at most 4 groups per thread is loaded once
   // into registers: the histogram pass and the draw both use these words.
   typename RowView<D>::Raw pre[4] = {};
+  bool sparse = false;     // the cuts came from sparse_search, whose list the draw walks
+  uint32_t sparse_nw = 0;  // that list's entries in this wave's region
   const bool preloaded = kFineSearch<D, THREADS> && (use_k || use_p) && !from_split && rv.V <= 4 * 8 * THREADS;
   if constexpr (kFineSearch<D, THREADS>) {
     if (preloaded) {
@@ -1305,8 +1543,25 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         for (int j = 0; j < 4; ++j) pre[j] = rv.template load_raw<false>(j * THREADS + t, j * THREADS + t < nfull);
       }
     }
+    // a sparse row of a batch of many rows: the cuts from a list of its
+    // candidates, which the draw then walks (sparse_search)
+    if constexpr (THREADS == 512) {
+      if ((use_k || use_p) && !from_split && !preloaded && rv.has_mask) {
+        sparse = sparse_search<D, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p, top_p,
+                                           &best, &cut16, &sparse_nw);
+        if (sparse) {
+          have_cut = true;
+          have_best = true;
+          if (best == -__builtin_inff()) {  // no candidate
+            if (t == 0) out[r] = -1;
+            return;
+          }
+          cut = cut16 ? order_key(D::value(static_cast<typename D::Bits>(bits_of_key16(cut16)))) : 0u;
+        }
+      }
+    }
     // 16-bit rows with a filter: one pass gives the maximum and both cuts
-    if ((use_k || use_p) && !from_split) {
+    if ((use_k || use_p) && !from_split && !sparse) {
       have_cut = fine_search<D, BYTES, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p,
                                                 top_p, &best, &cut, &cut16, &n_kept, pre, preloaded);
       if (have_cut) {  // else the radix search below, after the first pass if the row needs the maximum
@@ -1783,6 +2038,25 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       };
       // every group of the row, the partial last one included (its words
       // loaded by thread 0 alone), through f(i0, raw, mask bits)
+      if (sparse) {
+        // ---- draw over the listed candidates at or above the cut (min-p aside)
+        const SparseList<THREADS> sl(reinterpret_cast<const uint32_t*>(s_dyn));
+        const uint32_t region = static_cast<uint32_t>(wave) * SparseList<THREADS>::kPerWave;
+        for (uint32_t i = static_cast<uint32_t>(lane_id()); i < sparse_nw; i += 64u) {
+          const uint32_t k16 = sl.key[region + i];
+          if (k16 - lo16 > span16) continue;
+          const float x = D::value(static_cast<typename D::Bits>(bits_of_key16(k16)));
+          if (use_min_p && x * inv_t - zmax < ln_min_p) continue;
+          const int32_t idx = static_cast<int32_t>(sl.idx[region + i]);
+          uint32_t c4[4] = {static_cast<uint32_t>((tok0 + idx) >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo,
+                            a.offset_hi};
+          philox4x32_10(c4, a.seed_lo, a.seed_hi);
+          const int32_t w4 = (tok0 + idx) & 3;
+          const uint32_t word = w4 == 0 ? c4[0] : w4 == 1 ? c4[1] : w4 == 2 ? c4[2] : c4[3];
+          offer(gumbel_key(x, word), idx);
+        }
+        drawn = true;
+      }
       const auto walk16 = [&](auto&& f) {
         if (preloaded) {
           const int32_t nfull = rv.V >> 3;
@@ -1813,7 +2087,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
           f(i0, raw, bits);
         }
       };
-      if ((n_kept >= 256u || rv.V <= 64 * THREADS) && n_kept >= 1u && n_kept <= static_cast<uint32_t>(rv.V) / 6u &&
+      if (!drawn && (n_kept >= 256u || rv.V <= 64 * THREADS) && n_kept >= 1u && n_kept <= static_cast<uint32_t>(rv.V) / 6u &&
           n_kept <= kFineWordsHere - 4096u) {
         // Many kept tokens (the search counted them): list them first (LDS, where
         // the histogram was, one region per wave), then run the generator on the

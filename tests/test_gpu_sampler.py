@@ -428,6 +428,73 @@ def test_tokens_independent_of_batch_size(dtype, R):
         assert (part == tok[:n]).all(), f"{int((part != tok[:n]).sum())} of the first {n} rows differ"
 
 
+@pytest.mark.parametrize("dtype,V", [("float16", 20003), ("bfloat16", 20003), ("bfloat16", 50001)])
+def test_sparse_rows_listed_search(dtype, V):
+    """Filtered 16-bit rows of a batch of more than 256 rows whose mask allows at
+    most 4096 tokens take their cuts from a list of the candidates instead of
+    the 65536-key histogram.  Rows allowing 0, 1, 7, 4095, 4096 (listed) and
+    4097 (histogram) tokens; 2000 allowed tokens all in one wave's groups
+    (its list region overflows: histogram); ties among the candidates, -0
+    and +0, NaN and infinities among the allowed tokens; k beyond the
+    candidates, p = 0, min-p; a misaligned row pitch and a ragged vocab.
+    Every row against the oracle, and the first 256 rows against the same
+    rows drawn as a batch of 256 (the histogram search in 1024-thread
+    blocks): the same tokens.  A row of 50001 tokens is read in two batches
+    of groups per thread, one of 20003 in one."""
+    rng = np.random.default_rng((97 if dtype == "float16" else 101) + V)
+    R, cols = 300, V + 8
+    bits = random_logits(rng, dtype, R, cols, sigma=1.5)
+    allowed = np.zeros((R, cols), bool)
+    counts = [0, 1, 7, 4095, 4096, 4097, 60, 2000, 300, 4096]
+    for r in range(R):
+        n = counts[r % len(counts)] if r < 200 else int(rng.integers(0, 3000))
+        allowed[r, rng.choice(V, min(n, V), replace=False)] = True
+    group = np.arange(cols) // 8
+    wave0 = np.flatnonzero(((group % 512) < 64) & (np.arange(cols) < V))
+    for r in (10, 11):                            # crowd wave 0's region (1024 entries)
+        allowed[r] = False
+        allowed[r, rng.choice(wave0, 2000, replace=False)] = True
+    # ties, signed zeros and non-finite values among the candidates
+    zero = {"float16": (0x0000, 0x8000), "bfloat16": (0x0000, 0x8000)}[dtype]
+    inf, nan = {"float16": (0x7C00, 0x7E00), "bfloat16": (0x7F80, 0x7FC0)}[dtype]
+    for r in range(0, R, 3):
+        idx = np.flatnonzero(allowed[r])
+        if idx.size >= 8:
+            bits[r, idx[:3]] = zero[0]
+            bits[r, idx[3:5]] = zero[1]
+            bits[r, idx[5]] = nan
+            bits[r, idx[6]] = inf
+            bits[r, idx[7]] = inf | 0x8000
+            bits[r, idx[8:12]] = bits[r, idx[12]] if idx.size > 12 else bits[r, idx[8]]
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32 + 1, rng)
+    pitch = cols + 3                                # rows start off a 16-byte boundary
+    padded = np.zeros((R, pitch), bits.dtype)
+    padded[:, :cols] = bits
+    T = rng.choice([0.7, 1.0, 1.3], R).astype(np.float32)
+    k = rng.choice([0, 1, 5, 100, 5000], R).astype(np.int32)
+    p = rng.choice([1.0, 0.9, 0.5, 0.0], R).astype(np.float32)
+    m = rng.choice([0.0, 0.0, 0.05], R).astype(np.float32)
+    say(f"[gpu] sampler sparse rows listed search {dtype} V={V}")
+    dl = dev_logits(padded, dtype)[:, :cols]
+    dm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda")
+    targs = dict(temperature=torch.from_numpy(T).cuda(), top_k=torch.from_numpy(k).cuda(),
+                 top_p=torch.from_numpy(p).cuda(), min_p=torch.from_numpy(m).cuda())
+    tok = mb.mi_apply_bitmask_sample(dl, dm, V, seed=103, offset=9, **targs).cpu().numpy()
+    part = mb.mi_apply_bitmask_sample(dl[:256], dm[:256], V, seed=103, offset=9,
+                                      **{n: v[:256] for n, v in targs.items()}).cpu().numpy()
+    assert (part == tok[:256]).all(), f"{int((part != tok[:256]).sum())} of the first 256 rows differ"
+    vals = values64(bits, dtype)
+    exact = 0
+    for r in range(R):
+        al = S.allowed_tokens(mask[r], V, cols)
+        want, det = S.sample_row(vals[r], al, float(T[r]), int(k[r]), float(p[r]), float(m[r]), 103, 9, r,
+                                 margin=MARGIN)
+        assert tok[r] in det["candidates"], (r, tok[r], want)
+        exact += int(tok[r] == want)
+    assert exact >= 0.98 * R, f"only {exact}/{R} draws equal the oracle's"
+    assert tok[0] == -1 and (tok[allowed[:, :V].sum(1) == 0] == -1).all()
+
+
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_kept_tokens_crowding_one_wave_many_rows(dtype):
     """As the test above for 512-thread blocks (more rows than compute units):
