@@ -820,7 +820,7 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
 // for 32000.  The draw then runs on the list.
 constexpr uint32_t kSparseMax = 4096;
 constexpr uint32_t kSparseSlots = 2 * kSparseMax;  // list slots, an equal region per wave
-constexpr size_t sparse_lds_bytes() { return kSparseSlots * (4 + 2) + 256 * (4 + 8); }
+constexpr size_t sparse_lds_bytes() { return kSparseSlots * (4 + 2) + 2 * 256 * (4 + 8); }
 
 // The row's candidates, as sparse_search left them: wave w's entries in
 // slots [w * per_wave, w * per_wave + nw).
@@ -848,10 +848,9 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
   static_assert(sparse_lds_bytes() <= sample_fine_bytes(THREADS), "the list fits the histogram's LDS");
   uint32_t* lidx = lds;
   uint16_t* lkey = reinterpret_cast<uint16_t*>(lds + kSparseSlots);
-  uint32_t* hn = lds + kSparseSlots + kSparseSlots / 2;
-  unsigned long long* hm = reinterpret_cast<unsigned long long*>(hn + 256);
+  uint32_t* hn = lds + kSparseSlots + kSparseSlots / 2;                  // two digits' counts
+  unsigned long long* hm = reinterpret_cast<unsigned long long*>(hn + 512);  // and masses
   __shared__ uint32_t s_red[kWaves], s_cnt[kWaves];
-  __shared__ unsigned long long s_redm[kWaves];
   __shared__ SelectState s_ss;
   const int t = static_cast<int>(threadIdx.x);
   const int lane = lane_id(), wave = t >> 6;
@@ -935,28 +934,56 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
   };
   // the count first, from the mask alone: a dense row reads no logits here
   uint32_t allowed = 0;
-  for (int32_t base = 0; base < ngroups; base += 8 * THREADS) {
-    uint32_t b[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = gbits(base + j * THREADS + t);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) allowed += __builtin_popcount(b[j]);
-  }
-  if (block_sum(allowed) > kSparseMax) return false;
-  for (int32_t base = 0; base < ngroups; base += 8 * THREADS) {
+  *cut16 = 0u;
+  *nw_out = 0u;
+  if (ngroups <= 8 * THREADS) {  // one batch: its mask bytes stay in registers
     uint32_t b[8], v[8][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = gbits(base + j * THREADS + t);
-    load_values(base, b, v);
-    list_values(base, b, v);
+    for (int j = 0; j < 8; ++j) b[j] = gbits(j * THREADS + t);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) allowed += __builtin_popcount(b[j]);
+    allowed = block_sum(allowed);
+    if (allowed > kSparseMax) return false;
+    if (allowed == 0u) {  // nothing allowed: no candidate
+      *best = -__builtin_inff();
+      return true;
+    }
+    load_values(0, b, v);
+    list_values(0, b, v);
+  } else {
+    for (int32_t base = 0; base < ngroups; base += 8 * THREADS) {
+      uint32_t b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = gbits(base + j * THREADS + t);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) allowed += __builtin_popcount(b[j]);
+    }
+    allowed = block_sum(allowed);
+    if (allowed > kSparseMax) return false;
+    if (allowed == 0u) {
+      *best = -__builtin_inff();
+      return true;
+    }
+    for (int32_t base = 0; base < ngroups; base += 8 * THREADS) {
+      uint32_t b[8], v[8][4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = gbits(base + j * THREADS + t);
+      load_values(base, b, v);
+      list_values(base, b, v);
+    }
   }
 
-  // ---- the largest candidate and the candidate count; a wave whose
-  // region overflowed sends the row to the histogram search
+  // ---- the largest candidate and the candidate count (a wave whose region
+  // overflowed sends the row to the histogram search); meanwhile both
+  // digits' histograms of the select are cleared
   uint32_t km = 0;
   for (uint32_t i = static_cast<uint32_t>(lane); i < min(nw, kPerWave); i += 64u)
     km = max(km, static_cast<uint32_t>(lkey[region + i]));
   km = wave_max(km);
+  for (int i = t; i < 512; i += THREADS) {
+    hn[i] = 0u;
+    hm[i] = 0ull;
+  }
   __syncthreads();
   if (lane == 0) {
     s_red[wave] = km;
@@ -973,8 +1000,7 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
   }
   if (over) return false;
   *nw_out = nw;
-  *cut16 = 0u;
-  if (km == 0u) {
+  if (km == 0u) {  // every allowed token non-finite
     *best = -__builtin_inff();
     return true;
   }
@@ -984,43 +1010,32 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
     return fixed_mass(D::value(static_cast<typename D::Bits>(bits_of_key16(k))), inv_t, zmax);
   };
 
-  // ---- the cuts: a radix select over the list, top-k by counts, top-p by masses
-  unsigned long long z = 0;
-  if (use_p) {
-    for (uint32_t i = static_cast<uint32_t>(lane); i < nw; i += 64u) z += mass(lkey[region + i]);
-    z = lane63(wave_prefix_sum(z));
-    __syncthreads();
-    if (lane == 0) s_redm[wave] = z;
-    __syncthreads();
-    z = 0;
-    for (int w = 0; w < kWaves; ++w) z += s_redm[w];
-  }
+  // ---- the cuts: a radix select over the list (the high digit of the
+  // 16-bit key, then the low one under the chosen prefix), top-k by counts,
+  // top-p by masses; the first digit's mass histogram holds every
+  // candidate, so its total is Z
   const bool do_k = use_k && static_cast<uint32_t>(top_k) <= ntot;  // k beyond the candidates keeps all
-  const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(z);
-  const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
-  const unsigned long long need_p = target ? target : 1ull;  // p <= 0 keeps just the largest value
   if (!do_k && !use_p) return true;
-  if (t == 0) s_ss = SelectState{0u, static_cast<uint32_t>(top_k), need_p, 0u};
-  for (int shift = 8; shift >= 0; shift -= 8) {
-    const uint32_t pmask = shift == 8 ? 0u : 0xFF00u;
-    for (int i = t; i < 256; i += THREADS) {
-      hn[i] = 0u;
-      hm[i] = 0ull;
-    }
-    __syncthreads();
-    const uint32_t pk = s_ss.prefix_k, pp = s_ss.prefix_p;
+  if (t == 0) s_ss = SelectState{0u, static_cast<uint32_t>(top_k), 0ull, 0u};
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 8 : 0;
+    const uint32_t pmask = pass == 0 ? 0u : 0xFF00u;
+    uint32_t* h_n = hn + 256 * pass;
+    unsigned long long* h_m = hm + 256 * pass;
+    const uint32_t pk = pass == 0 ? 0u : s_ss.prefix_k, pp = pass == 0 ? 0u : s_ss.prefix_p;
     for (uint32_t i = static_cast<uint32_t>(lane); i < nw; i += 64u) {
       const uint32_t key = lkey[region + i];
       const uint32_t d = (key >> shift) & 255u;
-      if (do_k && (key & pmask) == pk) atomicAdd(&hn[d], 1u);
+      if (do_k && (key & pmask) == pk) atomicAdd(&h_n[d], 1u);
       if (use_p && (key & pmask) == pp) {
         const uint32_t m = mass(key);
-        if (m) atomicAdd(&hm[d], static_cast<unsigned long long>(m));
+        if (m) atomicAdd(&h_m[d], static_cast<unsigned long long>(m));
       }
     }
     __syncthreads();
     if (do_k && wave == 0) {
-      const WaveSuffix<uint32_t> ws(hn);
+      const WaveSuffix<uint32_t> ws(h_n);
       int d;
       uint32_t ab;
       ws.pick(s_ss.need_k, &d, &ab);
@@ -1030,13 +1045,20 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
       }
     }
     if (use_p && wave == 1) {
-      const WaveSuffix<unsigned long long> ws(hm);
+      const WaveSuffix<unsigned long long> ws(h_m);
+      unsigned long long need = s_ss.need_p;
+      if (pass == 0) {
+        // p <= 0 keeps just the largest value, as p = 0 does: any mass reaches it
+        const double pz = fmax(static_cast<double>(top_p), 0.0) * static_cast<double>(ws.total());
+        const unsigned long long target = static_cast<unsigned long long>(ceil(pz));
+        need = target ? target : 1ull;
+      }
       int d;
       unsigned long long ab;
-      ws.pick(s_ss.need_p, &d, &ab);
+      ws.pick(need, &d, &ab);
       if (lane == 0) {
         s_ss.prefix_p |= static_cast<uint32_t>(d) << shift;
-        s_ss.need_p -= ab;
+        s_ss.need_p = need - ab;
       }
     }
     __syncthreads();
