@@ -876,6 +876,7 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
   // and the candidates listed in this wave's region: allowed tokens with
   // finite values
   uint32_t nw = 0;  // this wave's entries (the same in every lane)
+  uint32_t km = 0;  // the largest key this lane listed
   const uint32_t region = static_cast<uint32_t>(wave) * kPerWave;
   const auto load_values = [&](int32_t base, const uint32_t (&b)[8], uint32_t (&v)[8][4]) {
 #pragma unroll
@@ -926,13 +927,19 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
               lidx[region + pos] = static_cast<uint32_t>(8 * g + q);
               lkey[region + pos] = static_cast<uint16_t>(keys[q]);
             }
+            km = max(km, keys[q]);
             ++pos;
           }
         }
       }
     }
   };
-  // the count first, from the mask alone: a dense row reads no logits here
+  // the count first, from the mask alone: a dense row reads no logits here;
+  // meanwhile both digits' histograms of the select are cleared
+  for (int i = t; i < 512; i += THREADS) {
+    hn[i] = 0u;
+    hm[i] = 0ull;
+  }
   uint32_t allowed = 0;
   *cut16 = 0u;
   *nw_out = 0u;
@@ -974,16 +981,8 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
   }
 
   // ---- the largest candidate and the candidate count (a wave whose region
-  // overflowed sends the row to the histogram search); meanwhile both
-  // digits' histograms of the select are cleared
-  uint32_t km = 0;
-  for (uint32_t i = static_cast<uint32_t>(lane); i < min(nw, kPerWave); i += 64u)
-    km = max(km, static_cast<uint32_t>(lkey[region + i]));
+  // overflowed sends the row to the histogram search)
   km = wave_max(km);
-  for (int i = t; i < 512; i += THREADS) {
-    hn[i] = 0u;
-    hm[i] = 0ull;
-  }
   __syncthreads();
   if (lane == 0) {
     s_red[wave] = km;
