@@ -30,8 +30,11 @@
 //            blocks: one pass counts the tokens the mask allows under each
 //            of the 65536 16-bit keys (LDS, 16- or 8-bit counters); the
 //            maximum and both cuts follow from the counts (fine_search).
-//            The radix passes below remain for a row where one key holds
-//            more tokens than its counter can (65536 or 256);
+//            In 512-thread blocks a row whose mask allows at most 4096
+//            tokens lists its candidates instead and selects both cuts on
+//            the list (sparse_search).  The radix passes below remain for a
+//            row where one key holds more tokens than its counter can
+//            (65536 or 256);
 //   fp32     fp32 rows with top-k or top-p in 1024-thread blocks: one pass
 //            counts and sums mass under the top 12 bits of each order key
 //            (coarse_hist32), a search picks the cut's bucket, and the draw
