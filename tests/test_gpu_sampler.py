@@ -435,7 +435,8 @@ def test_sparse_rows_listed_search(dtype, V):
     the 65536-key histogram.  Rows allowing 0, 1, 7, 4095, 4096 (listed) and
     4097 (histogram) tokens; 2000 allowed tokens all in one wave's groups
     (its list region overflows: histogram); ties among the candidates, -0
-    and +0, NaN and infinities among the allowed tokens; k beyond the
+    and +0, NaN and infinities among the allowed tokens, and a row whose
+    allowed tokens are all NaN or infinite (no candidate: -1); k beyond the
     candidates, p = 0, min-p; a misaligned row pitch and a ragged vocab.
     Every row against the oracle, and the first 256 rows against the same
     rows drawn as a batch of 256 (the histogram search in 1024-thread
@@ -466,6 +467,11 @@ def test_sparse_rows_listed_search(dtype, V):
             bits[r, idx[6]] = inf
             bits[r, idx[7]] = inf | 0x8000
             bits[r, idx[8:12]] = bits[r, idx[12]] if idx.size > 12 else bits[r, idx[8]]
+    # a row whose allowed tokens are all NaN or infinite: no candidate
+    allowed[13] = False
+    only = rng.choice(V, 6, replace=False)
+    allowed[13, only] = True
+    bits[13, only] = [nan, inf, inf | 0x8000, nan, inf, nan]
     mask = workloads.pack_allowed(allowed, (cols + 31) // 32 + 1, rng)
     pitch = cols + 3                                # rows start off a 16-byte boundary
     padded = np.zeros((R, pitch), bits.dtype)
@@ -492,7 +498,7 @@ def test_sparse_rows_listed_search(dtype, V):
         assert tok[r] in det["candidates"], (r, tok[r], want)
         exact += int(tok[r] == want)
     assert exact >= 0.98 * R, f"only {exact}/{R} draws equal the oracle's"
-    assert tok[0] == -1 and (tok[allowed[:, :V].sum(1) == 0] == -1).all()
+    assert tok[0] == -1 and tok[13] == -1 and (tok[allowed[:, :V].sum(1) == 0] == -1).all()
 
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
