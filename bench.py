@@ -668,7 +668,9 @@ SAMPLER_MODES = (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperat
 
 def sampler_times(torch, dev, mb, workloads, stream, steps=200):
     """The fused apply + sampler at the two batch/vocab shapes the logits-processor page times,
-    and the first of them with fp32 logits.
+    the first of them with fp32 logits, and the first with sparse masks (each
+    token allowed with probability 0.005, about 640 per row: the grammar
+    masks of constrained decoding are often that sparse).
 
     Per launch: one token per row from the masked logits.  Bytes counted: one
     read of the logits of every row plus its mask words; the kernel reads the
@@ -682,9 +684,13 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
     import numpy as np
 
     out = {}
+    sparse = workloads.mixed_bf16(n_indices=0)
+    rng = np.random.default_rng(17)
+    sparse.mask[:] = workloads.pack_allowed(rng.random((sparse.rows, sparse.cols)) < 0.005, sparse.mask.shape[1], rng)
     for label, wl, fp32 in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0), False),
                             ("B1024_V32000_fp16", workloads.verify_fp16(), False),
-                            ("B256_V128000_fp32", workloads.mixed_bf16(n_indices=0), True)):
+                            ("B256_V128000_fp32", workloads.mixed_bf16(n_indices=0), True),
+                            ("B256_V128000_bf16_mask_density_0.005", sparse, False)):
         R, V = wl.rows, (wl.vocab_size or wl.cols)
         esize = 4 if fp32 else 2
         nbytes = R * V * esize + R * ((V + 31) // 32) * 4

@@ -30,9 +30,9 @@
 //            blocks: one pass counts the tokens the mask allows under each
 //            of the 65536 16-bit keys (LDS, 16- or 8-bit counters); the
 //            maximum and both cuts follow from the counts (fine_search).
-//            In 512-thread blocks a row whose mask allows at most 4096
-//            tokens lists its candidates instead and selects both cuts on
-//            the list (sparse_search).  The radix passes below remain for a
+//            A row whose mask allows at most 4096 tokens (and that is not
+//            held in registers) lists its candidates instead and selects
+//            both cuts on the list (sparse_search).  The radix passes below remain for a
 //            row where one key holds more tokens than its counter can
 //            (65536 or 256);
 //   fp32     fp32 rows with top-k or top-p in 1024-thread blocks: one pass
@@ -812,15 +812,16 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
   return true;
 }
 
-// ---- sparse 16-bit rows with top-k or top-p in 512-thread blocks (batches
-// of many rows): when the mask allows at most kSparseMax tokens below V,
-// the candidates are listed in LDS (token and 16-bit key) from the groups
-// the mask allows -- the logits of other groups are not read -- and both
-// cuts come from a radix select over the list (two 8-bit digits of the
-// key), counting for top-k and summing the same fixed-point masses for
-// top-p: the same cuts as fine_search's histogram over all 65536 keys,
-// whose clearing, filling and scanning cost as much for 1600 candidates as
-// for 32000.  The draw then runs on the list.
+// ---- sparse 16-bit rows with top-k or top-p (512- and 1024-thread blocks,
+// rows longer than those held in registers): when the mask allows at most
+// kSparseMax tokens below V, the candidates are listed in LDS (token and
+// 16-bit key) from the groups the mask allows -- the logits of other groups
+// are not read -- and both cuts come from a radix select over the list
+// (two 8-bit digits of the key), counting for top-k and summing the same
+// fixed-point masses for top-p: the same cuts as fine_search's histogram
+// over all 65536 keys, whose clearing, filling and scanning cost as much
+// for a few hundred candidates as for a full row.  The draw then runs on
+// the list.  A dense row pays one read of its mask words to find out.
 constexpr uint32_t kSparseMax = 4096;
 constexpr uint32_t kSparseSlots = 2 * kSparseMax;  // list slots, an equal region per wave
 constexpr size_t sparse_lds_bytes() { return kSparseSlots * (4 + 2) + 2 * 256 * (4 + 8); }
@@ -1567,9 +1568,9 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         for (int j = 0; j < 4; ++j) pre[j] = rv.template load_raw<false>(j * THREADS + t, j * THREADS + t < nfull);
       }
     }
-    // a sparse row of a batch of many rows: the cuts from a list of its
-    // candidates, which the draw then walks (sparse_search)
-    if constexpr (THREADS == 512) {
+    // a sparse row: the cuts from a list of its candidates, which the draw
+    // then walks (sparse_search)
+    if constexpr (THREADS == 512 || THREADS == 1024) {
       if ((use_k || use_p) && !from_split && !preloaded && rv.has_mask) {
         sparse = sparse_search<D, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p, top_p,
                                            &best, &cut16, &sparse_nw);

@@ -430,17 +430,18 @@ def test_tokens_independent_of_batch_size(dtype, R):
 
 @pytest.mark.parametrize("dtype,V", [("float16", 20003), ("bfloat16", 20003), ("bfloat16", 50001)])
 def test_sparse_rows_listed_search(dtype, V):
-    """Filtered 16-bit rows of a batch of more than 256 rows whose mask allows at
-    most 4096 tokens take their cuts from a list of the candidates instead of
-    the 65536-key histogram.  Rows allowing 0, 1, 7, 4095, 4096 (listed) and
-    4097 (histogram) tokens; 2000 allowed tokens all in one wave's groups
+    """Filtered 16-bit rows whose mask allows at most 4096 tokens take their
+    cuts from a list of the candidates instead of the 65536-key histogram.
+    Rows allowing 0, 1, 7, 4095, 4096 (listed) and 4097 (histogram) tokens;
+    2000 allowed tokens all in one wave's groups
     (its list region overflows: histogram); ties among the candidates, -0
     and +0, NaN and infinities among the allowed tokens, and a row whose
     allowed tokens are all NaN or infinite (no candidate: -1); k beyond the
     candidates, p = 0, min-p; a misaligned row pitch and a ragged vocab.
-    Every row against the oracle, and the first 256 rows against the same
-    rows drawn as a batch of 256 (the histogram search in 1024-thread
-    blocks): the same tokens.  A row of 50001 tokens is read in two batches
+    Every row against the oracle; the first 256 rows against the same rows
+    drawn as a batch of 256 (1024-thread blocks); and every row against the
+    histogram search on the same candidates (no mask, disallowed logits at
+    -inf): the same tokens.  A row of 50001 tokens is read in two batches
     of groups per thread, one of 20003 in one."""
     rng = np.random.default_rng((97 if dtype == "float16" else 101) + V)
     R, cols = 300, V + 8
@@ -489,6 +490,13 @@ def test_sparse_rows_listed_search(dtype, V):
     part = mb.mi_apply_bitmask_sample(dl[:256], dm[:256], V, seed=103, offset=9,
                                       **{n: v[:256] for n, v in targs.items()}).cpu().numpy()
     assert (part == tok[:256]).all(), f"{int((part != tok[:256]).sum())} of the first 256 rows differ"
+    # the same candidates without a mask, every disallowed logit at -inf: the
+    # histogram search (the list needs a mask), which must draw the same tokens
+    hist_bits = padded.copy()
+    hist_bits[:, :cols][~allowed] = {"float16": 0xFC00, "bfloat16": 0xFF80}[dtype]
+    tok_h = mb.mi_apply_bitmask_sample(dev_logits(hist_bits, dtype)[:, :cols], None, V, seed=103, offset=9,
+                                       **targs).cpu().numpy()
+    assert (tok_h == tok).all(), f"{int((tok_h != tok).sum())} rows differ from the histogram search"
     vals = values64(bits, dtype)
     exact = 0
     for r in range(R):
