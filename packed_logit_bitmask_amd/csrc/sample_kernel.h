@@ -947,20 +947,34 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
   uint32_t allowed = 0;
   *cut16 = 0u;
   *nw_out = 0u;
-  if (ngroups <= 8 * THREADS) {  // one batch: its mask bytes stay in registers
-    uint32_t b[8], v[8][4];
+  if (ngroups <= 16 * THREADS) {
+    // at most two batches of groups: their mask bytes, all requested at
+    // once, stay in registers from the count to the listing
+    const int nb = ngroups <= 8 * THREADS ? 1 : 2;
+    uint32_t b[2][8] = {};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = gbits(j * THREADS + t);
+    for (int h = 0; h < 2; ++h)
+      if (h < nb) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) allowed += __builtin_popcount(b[j]);
+        for (int j = 0; j < 8; ++j) b[h][j] = gbits((8 * h + j) * THREADS + t);
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) allowed += __builtin_popcount(b[h][j]);
     allowed = block_sum(allowed);
     if (allowed > kSparseMax) return false;
     if (allowed == 0u) {  // nothing allowed: no candidate
       *best = -__builtin_inff();
       return true;
     }
-    load_values(0, b, v);
-    list_values(0, b, v);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (h < nb) {
+        uint32_t v[8][4];
+        load_values(8 * h * THREADS, b[h], v);
+        list_values(8 * h * THREADS, b[h], v);
+      }
   } else {
     for (int32_t base = 0; base < ngroups; base += 8 * THREADS) {
       uint32_t b[8];

@@ -510,6 +510,46 @@ def test_sparse_rows_listed_search(dtype, V):
 
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_sparse_long_rows_one_block_each(dtype):
+    """Sparse rows longer than two batches of groups per thread of a 1024-thread
+    block (140 001 tokens: the count and the listing each walk three batches)
+    in a batch of 8 rows, one block per row (no workspace).  Rows allowing 0,
+    3, 600, 4096 and 4097 tokens (the last through the histogram search);
+    every row against the oracle and against the histogram search on the
+    same candidates (no mask, disallowed logits at -inf): the same tokens."""
+    rng = np.random.default_rng(107 if dtype == "float16" else 109)
+    R, V = 8, 140001
+    cols = V + 5
+    bits = random_logits(rng, dtype, R, cols, sigma=1.5)
+    allowed = np.zeros((R, cols), bool)
+    for r, n in enumerate([0, 3, 600, 4096, 4097, 1500, 50, 4000]):
+        allowed[r, rng.choice(V, n, replace=False)] = True
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    T = rng.choice([0.7, 1.0, 1.3], R).astype(np.float32)
+    k = np.array([5, 0, 100, 50, 50, 0, 2, 3000], np.int32)
+    p = np.array([1.0, 0.9, 0.5, 0.9, 0.9, 0.3, 1.0, 0.95], np.float32)
+    m = np.array([0.0, 0.0, 0.05, 0.0, 0.0, 0.02, 0.0, 0.0], np.float32)
+    say(f"[gpu] sampler sparse long rows {dtype}")
+    targs = dict(temperature=torch.from_numpy(T).cuda(), top_k=torch.from_numpy(k).cuda(),
+                 top_p=torch.from_numpy(p).cuda(), min_p=torch.from_numpy(m).cuda())
+    dm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda")
+    tok = mb.mi_apply_bitmask_sample(dev_logits(bits, dtype), dm, V, seed=113, offset=4, workspace=None,
+                                     **targs).cpu().numpy()
+    hist_bits = bits.copy()
+    hist_bits[~allowed] = {"float16": 0xFC00, "bfloat16": 0xFF80}[dtype]
+    tok_h = mb.mi_apply_bitmask_sample(dev_logits(hist_bits, dtype), None, V, seed=113, offset=4, workspace=None,
+                                       **targs).cpu().numpy()
+    assert (tok_h == tok).all(), (tok, tok_h)
+    vals = values64(bits, dtype)
+    for r in range(R):
+        al = S.allowed_tokens(mask[r], V, cols)
+        want, det = S.sample_row(vals[r], al, float(T[r]), int(k[r]), float(p[r]), float(m[r]), 113, 4, r,
+                                 margin=MARGIN)
+        assert tok[r] in det["candidates"], (r, tok[r], want)
+    assert tok[0] == -1 and (tok[1:] >= 0).all()
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_kept_tokens_crowding_one_wave_many_rows(dtype):
     """As the test above for 512-thread blocks (more rows than compute units):
     8 waves, each with a list region of 2048 entries.  6000 kept tokens all
