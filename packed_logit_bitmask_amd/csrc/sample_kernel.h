@@ -103,12 +103,14 @@ struct BF16Bits {
   using Bits = uint16_t;
   static constexpr int kZeroLowBits = 16;
   static constexpr uint32_t kKey16Lo = 0x0080u, kKey16Hi = 0xFF7Fu;  // 16-bit order keys of -max, +max
+  static constexpr uint32_t kExp16 = 0x7F80u;                           // exponent field
   static __device__ __forceinline__ float value(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 };
 struct F16Bits {
   using Bits = uint16_t;
   static constexpr int kZeroLowBits = 13;
   static constexpr uint32_t kKey16Lo = 0x0400u, kKey16Hi = 0xFBFFu;  // 16-bit order keys of -max, +max
+  static constexpr uint32_t kExp16 = 0x7C00u;                           // exponent field
   static __device__ __forceinline__ float value(uint16_t b) { return static_cast<float>(__builtin_bit_cast(_Float16, b)); }
 };
 
@@ -904,37 +906,44 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
       }
     }
   };
+  // Per group, the candidates as 8 bits: allowed, and finite (exponent
+  // field not all ones, tested on both halves of a word at once: adding the
+  // field's lowest bit to the field carries into the half's top bit only
+  // when the field is full).  One prefix sum over the batch places each
+  // lane's entries; then each lane walks its own candidates, so a group
+  // costs its wave one step per candidate of its busiest lane rather than
+  // one per token.
   const auto list_values = [&](int32_t base, const uint32_t (&b)[8], const uint32_t (&v)[8][4]) {
+    constexpr uint32_t kE = D::kExp16 * 0x00010001u;                     // both halves' exponent fields
+    constexpr uint32_t kL = (D::kExp16 & (~D::kExp16 + 1u)) * 0x00010001u;  // and their lowest bits
+    uint32_t cand[8];
+    uint32_t cnt = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int32_t g = base + j * THREADS + t;
-      uint32_t keys[8];
-      uint32_t cand = 0;
+      uint32_t nf = 0;  // word q2's low token non-finite: bit 2 q2; its high token: bit 16 + 2 q2
 #pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const uint32_t k2 = order_key16x2(v[j][q2]);
-        keys[2 * q2] = k2 & 0xFFFFu;
-        keys[2 * q2 + 1] = k2 >> 16;
-      }
+      for (int q2 = 0; q2 < 4; ++q2) nf |= (((v[j][q2] & kE) + kL) & 0x80008000u) >> (15 - 2 * q2);
+      cand[j] = b[j] & ~(nf | (nf >> 15));
+      cnt += static_cast<uint32_t>(__builtin_popcount(cand[j]));
+    }
+    if (!__ballot(cnt != 0u)) return;
+    const uint32_t incl = wave_prefix_sum(cnt);  // this lane's entries go after those of the lanes below it
+    uint32_t pos = nw + incl - cnt;
+    nw += lane63(incl);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        cand |= (((b[j] >> q) & 1u) && keys[q] - D::kKey16Lo <= D::kKey16Hi - D::kKey16Lo ? 1u : 0u) << q;
-      if (__ballot(cand != 0u)) {  // this lane's entries go after those of the lanes below it
-        const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(cand));
-        const uint32_t incl = wave_prefix_sum(cnt);
-        uint32_t pos = nw + incl - cnt;
-        nw += lane63(incl);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if ((cand >> q) & 1u) {
-            if (pos < kPerWave) {
-              lidx[region + pos] = static_cast<uint32_t>(8 * g + q);
-              lkey[region + pos] = static_cast<uint16_t>(keys[q]);
-            }
-            km = max(km, keys[q]);
-            ++pos;
-          }
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t g = static_cast<uint32_t>(base + j * THREADS + t);
+      for (uint32_t c = cand[j]; c != 0u; c &= c - 1u) {
+        const uint32_t q = static_cast<uint32_t>(__builtin_ctz(c));
+        const uint32_t lo = (q & 2u) ? v[j][1] : v[j][0];  // token q sits in word q / 2, half q % 2
+        const uint32_t hi = (q & 2u) ? v[j][3] : v[j][2];
+        const uint32_t key = order_key16x2((((q & 4u) ? hi : lo) >> ((q & 1u) * 16u)) & 0xFFFFu) & 0xFFFFu;
+        if (pos < kPerWave) {
+          lidx[region + pos] = 8u * g + q;
+          lkey[region + pos] = static_cast<uint16_t>(key);
         }
+        km = max(km, key);
+        ++pos;
       }
     }
   };
