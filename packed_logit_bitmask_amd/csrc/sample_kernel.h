@@ -153,8 +153,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
     // v_mul_hi_u32 / v_mul_lo_u32 pair (a third faster on gfx950)
     const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c[0];
     const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c[2];
-    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c[1] ^ k0;
-    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c[3] ^ k1;
+    // each three-way xor as one v_bitop3_b32 (truth table 0x96: a ^ b ^ c),
+    // which the compiler does not form by itself here
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p1 >> 32), c[1], k0, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(static_cast<uint32_t>(p0 >> 32), c[3], k1, 0x96);
     c[0] = n0;
     c[1] = static_cast<uint32_t>(p1);
     c[2] = n2;
