@@ -56,8 +56,9 @@
 //            16-bit type's key are the same for every token of a prefix);
 //            each digit is picked by a wave-parallel suffix scan;
 //   min-p    z - z_max >= ln(min_p), no pass of its own;
-//   draw     Gumbel-max over the kept tokens: key = z - ln(-ln u) (logarithms
-//            by the hardware log2 instruction, rescaled), u from
+//   draw     Gumbel-max over the kept tokens: the largest z - ln(-ln u),
+//            compared as z log2(e) - log2(-log2 u) (the same order; two
+//            hardware log2 instructions), u from
 //            Philox4x32-10 (counter (i / 4, row, offset lo, offset hi), key
 //            (seed lo, seed hi), word i % 4; u = (floor(x / 2^9) + 1/2) / 2^23),
 //            ties to the lowest index.  A pass of its own, except where the
@@ -164,8 +165,9 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32
   }
 }
 
+// (k + 1/2) 2^-23 for the top 23 bits k of x: exact in binary32, so one fma
 __device__ __forceinline__ float unit_uniform(uint32_t x) {
-  return (static_cast<float>(x >> 9) + 0.5f) * (1.0f / 8388608.0f);
+  return fmaf(static_cast<float>(x >> 9), 1.0f / 8388608.0f, 0.5f / 8388608.0f);
 }
 
 __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) & 63; }
@@ -1714,14 +1716,17 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // min_p >= 1 keeps just the largest value and its ties (the cut never passes z_max)
   const float ln_min_p = use_min_p ? fminf(logf(min_p), 0.f) : 0.f;
 
-  // Gumbel-max over the kept tokens: key = z - ln(-ln u) for each kept token
-  // of a group, u from the token's Philox word; sink(q, key) receives them.
-  // -ln(-ln u) through the hardware base-2 logarithm: -ln u = -log2(u) ln 2,
-  // then -ln(that) = -log2(that) ln 2; clamped so an overflowed z (a tiny
-  // temperature) still draws a token
+  // Gumbel-max over the kept tokens: the token with the largest
+  // z - ln(-ln u), u from the token's Philox word; sink(q, key) receives
+  // each kept token's key.  The key is kept in base 2: since ln(-ln u) =
+  // ln 2 (log2(-log2 u) + log2(ln 2)), z - ln(-ln u) is a positive multiple
+  // of z log2(e) - log2(-log2 u) plus a constant, so both pick the same
+  // token, and the base-2 form takes the two hardware logarithms and one
+  // fma.  Clamped so an overflowed z (a tiny temperature) still draws a
+  // token.
+  const float inv_t_log2e = inv_t * 1.4426950408889634f;
   const auto gumbel_key = [&](float x, uint32_t word) {
-    const float e = -__log2f(unit_uniform(word)) * 0.6931471805599453f;
-    return fmaxf(x * inv_t - __log2f(e) * 0.6931471805599453f, -__FLT_MAX__);
+    return fmaxf(fmaf(x, inv_t_log2e, -__log2f(-__log2f(unit_uniform(word)))), -__FLT_MAX__);
   };
   const auto gumbel_group = [&](int32_t i0, const float* x, uint32_t kept, auto&& sink) {
     uint32_t c0[4] = {static_cast<uint32_t>((tok0 + i0) >> 2), static_cast<uint32_t>(row_base + r), a.offset_lo,
