@@ -131,11 +131,13 @@ __device__ __forceinline__ uint32_t bits_of_key16(uint32_t k) {
 }
 
 // Softmax mass of a token in fixed point, 2^31 exp(z - z_max) with z = x / T,
-// in [0, 2^31] for x at or below the maximum: the hardware base-2
-// exponential, converted through u32 (exact in that range).  Every top-p
-// search sums these, so equal inputs always give equal sums.
+// about 2^31 at the maximum and less below it: the hardware base-2
+// exponential of x log2(e) / T - z_max log2(e) (one fma per token: the two
+// products are the same for the whole row), converted through u32.  Every
+// top-p search sums these, so equal inputs always give equal sums.
 __device__ __forceinline__ uint32_t fixed_mass(float x, float inv_t, float zmax) {
-  return static_cast<uint32_t>(__builtin_amdgcn_exp2f((x * inv_t - zmax) * 1.4426950408889634f) * 2147483648.0f);
+  const float a = inv_t * 1.4426950408889634f, b = -(zmax * 1.4426950408889634f);
+  return static_cast<uint32_t>(__builtin_amdgcn_exp2f(fmaf(x, a, b)) * 2147483648.0f);
 }
 
 // Whether an order key belongs to a finite value: keys of finite floats run
@@ -720,10 +722,17 @@ __device__ __forceinline__ bool fine_search(const RowView<D>& rv, uint32_t* fine
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           const uint32_t ka = KW * static_cast<uint32_t>((s0 + j) * THREADS + t);  // the word's first key
+          if (wb[j] && in_range(ka)) {  // a word holds finite keys only or none
+            // its keys have one sign, so their raw bits run from ka's up (a
+            // positive value) or down (a negative one)
+            const uint32_t b0 = bits_of_key16(ka), step = (ka & 0x8000u) ? 1u : ~0u;
 #pragma unroll
-          for (uint32_t e = 0; e < KW; ++e) {
-            const uint32_t n = count_in(wb[j], e);
-            if (n && in_range(ka + e)) mw[j] += static_cast<unsigned long long>(n) * mass(ka + e);
+            for (uint32_t e = 0; e < KW; ++e) {
+              const uint32_t n = count_in(wb[j], e);
+              if (n)
+                mw[j] += static_cast<unsigned long long>(n) *
+                         fixed_mass(D::value(static_cast<Bits>(b0 + e * step)), inv_t, zmax);
+            }
           }
         }
 #pragma unroll
@@ -1339,6 +1348,7 @@ __global__ __launch_bounds__(1024) void split_search(SampleArgs a, const uint32_
   using Bits = typename D::Bits;
   constexpr int kWaves = 16;
   constexpr uint32_t kSpan = D::kKey16Hi - D::kKey16Lo;
+  static_assert(D::kKey16Lo % 64 == 0 && (D::kKey16Hi + 1) % 64 == 0, "a thread's keys are all finite or none");
   __shared__ uint32_t s_kmax[kWaves], s_c[kWaves], s_cut[2], s_cross[2], s_above_n[2], s_kept[2];
   __shared__ unsigned long long s_m[kWaves], s_above[2];
   const int64_t r = blockIdx.x;
@@ -1411,17 +1421,20 @@ __global__ __launch_bounds__(1024) void split_search(SampleArgs a, const uint32_
   // ---- top-p masses per thread (the counts read again), then their suffix totals
   unsigned long long m = 0, sm = 0, tot_m = 0;
   if (use_p) {
-    if (marked && c) {
+    if (marked && c) {  // c > 0: the thread's 64 keys are finite (they share one sign and finiteness)
       uint4 q[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) q[u] = h4[u];
+      // raw bits run from k0's up (a positive value) or down (a negative one)
+      const uint32_t b0 = bits_of_key16(k0), step = (k0 & 0x8000u) ? 1u : ~0u;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const uint32_t n4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t k = k0 + 4u * u + e;
-          if (n4[e] && in_range(k)) m += static_cast<unsigned long long>(n4[e]) * mass(k);
+          if (n4[e])
+            m += static_cast<unsigned long long>(n4[e]) *
+                 fixed_mass(D::value(static_cast<Bits>(b0 + (4u * u + e) * step)), inv_t, zmax);
         }
       }
     }
