@@ -23,19 +23,17 @@ namespace {
 constexpr int64_t kMaxBlocksPerLaunch = (int64_t(1) << 24) - 1;  // blocks * 256 < 2^32
 
 // Shape of the 16-byte-vector kernels: vectors per lane (unroll) and the
-// store cache policy.  Picked from measurements on MI355X, cold from HBM,
-// in place:
-//  - below 48 MB of writes, two vectors per lane with device-scope
-//    write-through stores (the output streams out during the kernel instead
-//    of in one end-of-kernel L2 writeback);
-//  - from 48 MB to 1 GB, two vectors per lane with write-through
-//    non-temporal stores: 3-5 % ahead of one vector per lane up to 128 MB
-//    and 14-25 % ahead on rows of mixed kinds (all-ones, sparse, empty), at
-//    most 4 % behind one vector per lane on 256-512 MB of uniform density;
+// store cache policy.  Picked from measurements on MI355X, cold from HBM
+// (buffer sets rotated so that the bytes the launches touch cycle through
+// more than twice the 256 MB Infinity Cache), in place:
+//  - below 1 GB of writes, two vectors per lane with device-scope
+//    write-through non-temporal stores.  On the 34.8 MB bf16 launch of 128
+//    rows x 128000 tokens this took 13.9 us against 15.8 us with
+//    write-through stores that are not marked non-temporal, and against
+//    14.2-14.3 us with one or four vectors per lane; loads marked
+//    non-temporal or system-coherent were 1-2 % slower;
 //  - from 1 GB, four vectors per lane, non-temporal: 1-4 % ahead on the
-//    large mixed-kind workloads.  One vector per lane is never used: it
-//    launches 4x the blocks, which cost 36-40 % on rows that need little
-//    work.
+//    large mixed-kind workloads.
 // Out of place, two vectors per lane with write-through non-temporal stores
 // was best at every size measured.
 struct VecShape {
@@ -43,11 +41,9 @@ struct VecShape {
   int policy;
 };
 
-constexpr int64_t kSmallWriteBytes = int64_t(48) << 20;
 constexpr int64_t kLargeWriteBytes = int64_t(1) << 30;
 
 VecShape inplace_shape(int64_t write_bytes) {
-  if (write_bytes < kSmallWriteBytes) return {2, mi::kStoreDevice};
   if (write_bytes < kLargeWriteBytes) return {2, mi::kStoreDeviceStream};
   return {4, mi::kStoreDeviceStream};
 }
@@ -102,8 +98,7 @@ mi_status_t run_inplace(void* logits_v, int64_t ls, const int32_t* mask_i, int64
   mi::inplace_vec<T, UNROLL, POLICY><<<blocks, mi::kBlock, 0, stream>>>(logits, ls, mask, ms, V, W, map, s0, \
                                                                         ch, fill, any_out, nrep)
         // exactly the shapes inplace_shape returns
-        if (shape.unroll == 2 && shape.policy == mi::kStoreDevice) MI_INPLACE_VEC(2, mi::kStoreDevice);
-        else if (shape.unroll == 2) MI_INPLACE_VEC(2, mi::kStoreDeviceStream);
+        if (shape.unroll == 2) MI_INPLACE_VEC(2, mi::kStoreDeviceStream);
         else MI_INPLACE_VEC(4, mi::kStoreDeviceStream);
 #undef MI_INPLACE_VEC
       }, any_out != nullptr);

@@ -205,7 +205,7 @@ def test_named_large_fp32(large, variant):
 
 
 @pytest.mark.parametrize("dtype,rows,cols,vocab", [
-    ("bfloat16", 800, 40001, 39999),   # 48 MB - 1 GB of writes: two vectors per lane, streaming stores
+    ("bfloat16", 800, 40001, 39999),   # below 1 GB of writes: two vectors per lane, streaming stores
     ("float16", 700, 50003, None),
     ("float32", 500, 30001, 29990),
     ("float32", 4500, 60001, None),    # >= 1 GB of writes: four vectors per lane
