@@ -704,7 +704,11 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
         R, V = wl.rows, (wl.vocab_size or wl.cols)
         esize = 4 if fp32 else 2
         nbytes = R * V * esize + R * ((V + 31) // 32) * 4
-        nsets = max(2, math.ceil(2 * INFINITY_CACHE / (wl.logits.nbytes * esize // 2 + wl.mask.nbytes)))
+        # the least a launch touches: every mask word of the rows and each
+        # 128-byte line of logits that holds an allowed token (a sparse row's
+        # filtered draw reads no other line); greedy and unfiltered rows read
+        # more, so the rotation is cold for them too
+        nsets = cold_sets(touched_lines(wl, esize))
         tdt = torch.bfloat16 if wl.dtype == "bfloat16" else torch.float16
         sets = []
         for _ in range(nsets):
@@ -724,6 +728,18 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
         del sets
         torch.cuda.empty_cache()
     return out
+
+
+def touched_lines(wl, esize):
+    """Mask bytes of every row plus 128 bytes per logits line holding an allowed token (tokens below V)."""
+    import numpy as np
+
+    V = wl.vocab_size or wl.cols
+    bits = np.unpackbits(wl.mask.view(np.uint8), axis=1, bitorder="little")[:, :V].astype(bool)
+    per_line = 128 // esize
+    pad = (-V) % per_line
+    lines = np.pad(bits, ((0, 0), (0, pad))).reshape(wl.rows, -1, per_line).any(axis=2).sum()
+    return int(wl.mask.nbytes + lines * 128)
 
 
 def sampler_small_batch(torch, dev, mb, workloads, stream, steps=200):

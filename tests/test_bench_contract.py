@@ -55,3 +55,26 @@ def test_cpu_baseline_runs_the_oracle():
     eff = bench.effective_bytes(len(wl.indices), wl.vocab_size, 2)
     r = bench.cpu_baseline(wl, eff, 0.2)
     assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "GB/s" and r["value"] > 0
+
+
+def test_cold_rotation_counts_touched_bytes():
+    # a launch of the headline touches its 128 indexed rows and their mask
+    # words only: the rotation must cycle more than twice the Infinity Cache
+    # in those bytes, not in the bytes each buffer set holds
+    eff = bench.effective_bytes(128, 128000, 2)
+    n = bench.cold_sets(eff)
+    assert n * eff > 2 * bench.INFINITY_CACHE and (n - 1) * eff <= 2 * bench.INFINITY_CACHE
+    assert bench.cold_sets(10 ** 12) == 2 and bench.cold_sets(1000, cap=64) == 64
+
+
+def test_touched_lines_of_a_sparse_mask():
+    # one allowed token per row in the first 128-byte line, one in the last:
+    # two lines of logits per row plus the whole mask
+    rows, V = 4, 1000
+    bits = np.zeros((rows, V), dtype=bool)
+    bits[:, 3] = True
+    bits[:, V - 1] = True
+    wl = workloads.Workload(name="t", dtype="bfloat16", logits=np.zeros((rows, V), np.uint16),
+                            mask=workloads.pack_allowed(bits, (V + 31) // 32, np.random.default_rng(0)),
+                            vocab_size=V, indices=None, fill_value=-math.inf, op="inplace")
+    assert bench.touched_lines(wl, 2) == wl.mask.nbytes + rows * 2 * 128
