@@ -687,9 +687,9 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
     row once per pass (greedy 1, unfiltered 1; with top-k or top-p, 16-bit
     rows take 2 -- the key histogram and the draw -- or 1 when a short row is
     held in registers between them; fp32 rows take 2 -- the coarse 12-bit
-    bucket pass and the draw that lists the cut's bucket -- plus the maximum
-    for top-p and min-p).  The fp32 shape holds the bf16 shape's values
-    widened.  Cold: rotating buffer sets.
+    bucket pass, which also finds the maximum, and the draw that lists the
+    cut's bucket).  The fp32 shape holds the bf16 shape's values widened.
+    Cold: rotating buffer sets.
     """
     import numpy as np
 

@@ -1117,10 +1117,12 @@ __device__ __forceinline__ bool sparse_search(const RowView<D>& rv, uint32_t* ld
 // candidate below it, and lists the candidates inside it (order key and
 // index) in LDS; a radix select over the list's low 20 key bits, three
 // digits, gives the exact cut, and the listed tokens at or above it join the
-// draw.  Three passes over the row for top-p (the maximum first), two for
-// top-k alone -- against five and three for a radix search over the row.  A
-// bucket holding more candidates than the list has room for sends the row to
-// the radix search.
+// draw.  Two passes over the row for top-k and top-p alike -- against five and
+// three for a radix search over the row: where top-p or min-p needs the row's
+// maximum, the coarse pass finds it too, summing each bucket's masses
+// relative to the bucket's largest value (edge_mass) and rescaling the sums
+// to the maximum afterwards (edge_to_max_units).  A bucket holding more
+// candidates than the list has room for sends the row to the radix search.
 constexpr int kCoarseBuckets = 4096;
 constexpr uint32_t kCoarseShift = 20;  // bucket = order key >> 20
 // The list: one region per wave of the 1024-thread block, each wave appending
@@ -1145,27 +1147,57 @@ __device__ __forceinline__ float value_of_key(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// A candidate's softmax mass relative to the largest value e of its coarse
+// bucket, in fixed point: 2^45 exp((x - e) / T), computed as the hardware
+// base-2 exponential of (x - e) log2(e) / T.  x - e is exact (the two share
+// a binade).  A mass of at most 2^45 summed over at most 2^18 candidates
+// stays below 2^63.
+constexpr int kEdgeMassBits = 45;
+constexpr int32_t kEdgeMassMaxTokens = 1 << 18;
+__device__ __forceinline__ unsigned long long edge_mass(float x, float e, float c) {
+  // f in [0, 1]; floor(2^45 f) is its 24-bit significand placed 32 bits up
+  // and shifted right by 10 - (f's exponent): a shift past 63 (f below
+  // 2^-53, a subnormal or 0, or NaN) leaves 0
+  const uint32_t b = __float_as_uint(__builtin_amdgcn_exp2f((x - e) * c));
+  const uint32_t sh = 137u - (b >> 23);
+  const unsigned long long sig = static_cast<unsigned long long>((b & 0x7FFFFFu) | 0x800000u) << 32;
+  return sh < 64u ? sig >> sh : 0ull;
+}
+
 // One pass over an fp32 row: every candidate (mask bit set, finite) adds 1
 // to cc[bucket] when use_k and its fixed-point mass to cm[bucket] when use_p,
-// from a cleared start.  Ends with a barrier.
+// from a cleared start.  The mass is 2^31 exp(z - z_max) (fixed_mass) when
+// the maximum is known (edge == false), else edge_mass, relative to the
+// largest value of the candidate's own bucket, and the pass also finds the
+// largest candidate.  Returns the order key of the largest candidate (0 when
+// there is none; edge mode only).  Ends with a barrier.
 template <int THREADS>
-__device__ __forceinline__ void coarse_hist32(const RowView<F32Bits>& rv, unsigned long long* cm, uint32_t* cc,
-                                              bool use_k, bool use_p, float inv_t, float zmax) {
+__device__ __forceinline__ uint32_t coarse_hist32(const RowView<F32Bits>& rv, unsigned long long* cm, uint32_t* cc,
+                                                  bool use_k, bool use_p, float inv_t, float zmax, bool edge) {
+  __shared__ uint32_t s_kmax[THREADS / 64];
   const int t = static_cast<int>(threadIdx.x);
   for (int i = t; i < kCoarseBuckets; i += THREADS) {
     cm[i] = 0ull;
     cc[i] = 0u;
   }
   __syncthreads();
+  const float c = inv_t * 1.4426950408889634f;
+  uint32_t kmax = 0;  // every finite value's key is at least 0x00800000
   const auto add = [&](uint32_t xb, uint32_t bit) {
     const float x = __uint_as_float(xb);
     const uint32_t key = order_key(x);
     if (bit && finite_key(key)) {
       const uint32_t b = key >> kCoarseShift;
+      if (edge) kmax = max(kmax, key);
       if (use_k) atomicAdd(&cc[b], 1u);
       if (use_p) {
-        const uint32_t m = fixed_mass(x, inv_t, zmax);  // one that truncates to 0 adds nothing
-        if (m) atomicAdd(&cm[b], static_cast<unsigned long long>(m));
+        if (edge) {
+          const unsigned long long m = edge_mass(x, value_of_key(key | ((1u << kCoarseShift) - 1u)), c);
+          if (m) atomicAdd(&cm[b], m);
+        } else {
+          const uint32_t m = fixed_mass(x, inv_t, zmax);  // one that truncates to 0 adds nothing
+          if (m) atomicAdd(&cm[b], static_cast<unsigned long long>(m));
+        }
       }
     }
   };
@@ -1177,6 +1209,36 @@ __device__ __forceinline__ void coarse_hist32(const RowView<F32Bits>& rv, unsign
   if ((rv.V & 7) && t == 0) {  // the partial last group, by plain loads
     for (int32_t i = rv.V & ~7; i < rv.V; ++i)
       add(rv.row[i], rv.has_mask ? (load_word(rv.rm, (i >> 5) * 4) >> (i & 31)) & 1u : 1u);
+  }
+  if (edge) {
+    kmax = wave_max(kmax);
+    if (lane_id() == 0) s_kmax[t >> 6] = kmax;
+  }
+  __syncthreads();
+  if (edge) {
+    kmax = 0;
+    for (int w = 0; w < THREADS / 64; ++w) kmax = max(kmax, s_kmax[w]);
+  }
+  return kmax;
+}
+
+// After coarse_hist32 in edge mode, with the largest candidate xmax known:
+// each bucket's mass sum rescaled to 2^31 exp(z - z_max) units, the units
+// of fixed_mass, by exp((e_b - xmax) / T) 2^(31 - 45) in double precision
+// (e_b the bucket's largest value), thread t of 1024 taking buckets 4t ..
+// 4t + 3.  Ends with a barrier.
+__device__ __forceinline__ void edge_to_max_units(unsigned long long* cm, float inv_t, float xmax) {
+  const double c = static_cast<double>(inv_t * 1.4426950408889634f);
+  const int t = static_cast<int>(threadIdx.x);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t b = 4u * static_cast<uint32_t>(t) + static_cast<uint32_t>(j);
+    const unsigned long long m = cm[b];
+    if (m) {
+      const double e = static_cast<double>(value_of_key((b << kCoarseShift) | ((1u << kCoarseShift) - 1u)));
+      const double f = exp2((e - static_cast<double>(xmax)) * c + static_cast<double>(31 - kEdgeMassBits));
+      cm[b] = static_cast<unsigned long long>(static_cast<double>(m) * f);
+    }
   }
   __syncthreads();
 }
@@ -1638,7 +1700,12 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
       }
     }
   }
-  if (first_pass && !have_best) {
+  // fp32 rows with top-k or top-p in 1024-thread blocks that need the
+  // maximum (top-p, min-p): the coarse pass finds it too (coarse_hist32 in
+  // edge mode)
+  const bool fused_max = first_pass && sizeof(typename D::Bits) == 4 && THREADS == 1024 && (use_k || use_p) &&
+                         !have_cut && !split && rv.V <= kEdgeMassMaxTokens;
+  if (first_pass && !have_best && !fused_max) {
     int32_t besti = 0x7FFFFFFF;
     int32_t bestg = -1;
     typename RowView<D>::Raw braw{};  // the best group's words, kept so it need not be read again
@@ -1724,7 +1791,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     }
   }
 
-  const float zmax = best * inv_t;  // used only when the maximum is known
+  float zmax = best * inv_t;  // used only when the maximum is known (set again after a fused maximum)
   const bool use_min_p = min_p > 0.f;
   // min_p >= 1 keeps just the largest value and its ties (the cut never passes z_max)
   const float ln_min_p = use_min_p ? fminf(logf(min_p), 0.f) : 0.f;
@@ -1782,7 +1849,28 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     if ((use_k || use_p) && !have_cut) {
       unsigned long long* cm = reinterpret_cast<unsigned long long*>(s_dyn);
       uint32_t* cc = reinterpret_cast<uint32_t*>(cm + kCoarseBuckets);
-      coarse_hist32<THREADS>(rv, cm, cc, use_k, use_p, inv_t, zmax);
+      if (fused_max) {
+        const uint32_t kmax = coarse_hist32<THREADS>(rv, cm, cc, use_k, use_p, inv_t, 0.f, true);
+        if (kmax == 0u) {  // no candidate
+          if (t == 0) out[r] = -1;
+          return;
+        }
+        best = value_of_key(kmax);
+        zmax = best * inv_t;
+        // the bucket holding the maximum: its sum is rescaled by exp((e - xmax) / T)
+        // >= 1, so its rounding error grows by that factor; past 2^14 (the
+        // precision fixed_mass gives) the pass runs again relative to z_max
+        const float e_top = value_of_key(kmax | ((1u << kCoarseShift) - 1u));
+        if (use_p && (static_cast<double>(e_top) - static_cast<double>(best)) *
+                             static_cast<double>(inv_t * 1.4426950408889634f) > 14.0) {
+          __syncthreads();  // every thread has read the pass's results
+          coarse_hist32<THREADS>(rv, cm, cc, use_k, use_p, inv_t, zmax, false);
+        } else if (use_p) {
+          edge_to_max_units(cm, inv_t, best);
+        }
+      } else {
+        coarse_hist32<THREADS>(rv, cm, cc, use_k, use_p, inv_t, zmax, false);
+      }
       uint32_t n_above = 0, need_k = 0;
       unsigned long long m_above = 0, need_p = 0;
       const uint32_t bk_ = use_k ? coarse_search<uint32_t>(

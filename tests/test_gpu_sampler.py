@@ -1045,3 +1045,50 @@ def test_split_filtered_rows_in_a_graph():
             assert torch.equal(outs[k].cpu(), want[k]), (rep, modes[k])
         (dl.float() * 2).sum().item()
     del g
+
+
+@pytest.mark.parametrize("T", [1.0, 0.11, 0.1, 0.02])
+def test_fp32_fused_maximum_rescale_and_fallback(T):
+    """fp32 rows of 1024-thread blocks take the row maximum from the coarse
+    pass itself: each bucket's masses are summed relative to the bucket's
+    largest value and rescaled to the maximum after the pass.  Row 0 holds
+    its maximum 8.0 at the bottom of the bucket [8, 9): at T = 0.11 the top
+    bucket's rescale is 2^13.1, at T = 0.1 it is 2^14.4, past the 2^14 at
+    which the pass runs again relative to the maximum.  Row 1 has logits
+    around 600 (buckets 64 wide: the pass runs again at every temperature
+    here), row 2 negative logits with the maximum at a bucket's top edge,
+    row 3 the maximum 500 times, row 4 a wide spread, row 5 no candidate.
+    Against the oracle."""
+    rng = np.random.default_rng(217)
+    R, cols = 6, 20000
+    x = rng.standard_normal((R, cols)).astype(np.float32)
+    x[0] = rng.uniform(5.0, 7.99, cols).astype(np.float32)
+    x[0, rng.choice(cols, 3, replace=False)] = np.float32(8.0)
+    x[1] = np.float32(600.0) + rng.standard_normal(cols).astype(np.float32) * np.float32(3.0)
+    x[2] = -np.abs(x[2]) - np.float32(1.0)
+    x[2, 17] = np.float32(-1.0)
+    x[3, rng.choice(cols, 500, replace=False)] = np.float32(4.5)
+    x[4] *= np.float32(4.0)
+    bits = x.view(np.uint32)
+    allowed = rng.random((R, cols)) < 0.95
+    allowed[:5, 0] = True
+    allowed[0, x[0] == 8.0] = True
+    allowed[5] = False
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    for i, (k, p, m) in enumerate(((0, 0.9, 0.0), (0, 0.5, 0.0), (50, 0.9, 0.0), (0, 0.9, 0.05), (20, 1.0, 0.1))):
+        say(f"[gpu] fp32 fused maximum T={T} k={k} p={p} m={m}")
+        tok = check_rows(bits, "float32", mask, None, T, k, p, m, seed=31 + i, offset=i, min_exact=0.8)
+        assert tok[5] == -1
+
+
+def test_fp32_rows_past_the_fused_maximum_limit():
+    """fp32 rows longer than 2^18 tokens (the most whose fixed-point bucket
+    masses relative to the bucket's top fit 64 bits) take the maximum in a
+    pass of its own before the coarse pass.  Against the oracle."""
+    rng = np.random.default_rng(219)
+    R, cols = 2, 300001
+    x = rng.standard_normal((R, cols)).astype(np.float32) * np.float32(2.0)
+    bits = x.view(np.uint32)
+    for i, (k, p, m) in enumerate(((0, 0.9, 0.0), (50, 0.9, 0.02))):
+        say(f"[gpu] fp32 rows of {cols} tokens k={k} p={p} m={m}")
+        check_rows(bits, "float32", None, None, 1.0, k, p, m, seed=41 + i, offset=i, min_exact=0.5)
