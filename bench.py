@@ -141,7 +141,7 @@ def sampler_calls(n):
     import torch
 
     import packed_logit_bitmask_amd as mb
-    from packed_logit_bitmask_amd import workloads
+    import workloads
 
     dev = torch.device("cuda:0")
     for label, wl, fp32 in (("B256_V128000_bf16", workloads.mixed_bf16(n_indices=0), False),
@@ -172,7 +172,7 @@ def split_calls(n):
     import torch
 
     import packed_logit_bitmask_amd as mb
-    from packed_logit_bitmask_amd import workloads
+    import workloads
 
     dev = torch.device("cuda:0")
     wl = workloads.mixed_bf16(n_indices=0)
@@ -205,7 +205,7 @@ def all_configs():
     import torch
 
     import packed_logit_bitmask_amd as mb
-    from packed_logit_bitmask_amd import workloads
+    import workloads
 
     mb.load_library()
     dev = torch.device("cuda:0")
@@ -299,7 +299,7 @@ def main():
     import torch
 
     import packed_logit_bitmask_amd as mb
-    from packed_logit_bitmask_amd import workloads
+    import workloads
 
     mb.load_library()
     dev = torch.device("cuda:0")
@@ -926,7 +926,7 @@ def cpu_baseline_python():
     whole (conversion to and from lists included).
     """
     import oracle
-    from packed_logit_bitmask_amd import workloads
+    import workloads
 
     out = {}
     for wl in (workloads.tiny(), workloads.tail_bf16()):

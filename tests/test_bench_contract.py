@@ -17,7 +17,7 @@ ROOT = pathlib.Path(__file__).resolve().parents[1]
 sys.path.insert(0, str(ROOT))
 
 import bench  # noqa: E402
-from packed_logit_bitmask_amd import workloads  # noqa: E402
+import workloads  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():

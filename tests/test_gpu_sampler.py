@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 from oracle import sampler as S
-from packed_logit_bitmask_amd import workloads
+import workloads
 import packed_logit_bitmask_amd as mb
 
 torch = pytest.importorskip("torch")

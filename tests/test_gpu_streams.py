@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from packed_logit_bitmask_amd import workloads
+import workloads
 import packed_logit_bitmask_amd as mb
 
 torch = pytest.importorskip("torch")

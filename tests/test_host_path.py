@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import packed_logit_bitmask_amd as mb
-from packed_logit_bitmask_amd import workloads
+import workloads
 
 TORCH = {"float32": (torch.int32, np.int32, torch.float32), "float16": (torch.int16, np.int16, torch.float16),
          "bfloat16": (torch.int16, np.int16, torch.bfloat16)}

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from packed_logit_bitmask_amd import workloads
+import workloads
 
 CASES = [
     ("tiny", {}),

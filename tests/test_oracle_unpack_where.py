@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from packed_logit_bitmask_amd import workloads
+import workloads
 
 DTYPES = ["float32", "float16", "bfloat16"]
 

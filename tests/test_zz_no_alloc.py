@@ -14,7 +14,8 @@ import sys
 import numpy as np
 import pytest
 
-from packed_logit_bitmask_amd import _binding, workloads
+from packed_logit_bitmask_amd import _binding
+import workloads
 import packed_logit_bitmask_amd as mb
 
 torch = pytest.importorskip("torch")
