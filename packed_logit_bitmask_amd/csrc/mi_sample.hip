@@ -280,6 +280,35 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
     } else if (nseg > 1) {
       mi::clear_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
     }
+    if (greedy_only && !sinfo) {
+      // every row greedy: the max pass alone, in its own kernel (greedy_rows),
+      // 128 bytes in flight per thread; measured on MI355X (cold, graph
+      // replay): one 512-thread block per row for at most 256 rows (B=256
+      // bf16 18.1 -> 16.2 us, fp32 28.9 -> 26.4 us against the 1024-thread
+      // sample_rows), 128-thread blocks beyond (B=1024 fp16 16.2 -> 15.8 us),
+      // 256-thread blocks per segment of a split row
+#define MI_GREEDY(TAG, BITS, THREADS)                                                                             \
+  mi::greedy_rows<TAG, 128, THREADS><<<static_cast<uint32_t>(n) * nseg, THREADS, 0, stream>>>(                      \
+      reinterpret_cast<const BITS*>(lg), logits_row_stride, mk, mask_row_stride, V, tokens + r0, nseg, seg_len)
+#define MI_GREEDY_SHAPES(TAG, BITS)                    \
+  if (nseg > 1) MI_GREEDY(TAG, BITS, 256);             \
+  else if (n <= 256) MI_GREEDY(TAG, BITS, 512);        \
+  else MI_GREEDY(TAG, BITS, 128)
+      switch (dtype) {
+        case MI_DTYPE_F32:
+          MI_GREEDY_SHAPES(mi::F32Bits, uint32_t);
+          break;
+        case MI_DTYPE_F16:
+          MI_GREEDY_SHAPES(mi::F16Bits, uint16_t);
+          break;
+        default:
+          MI_GREEDY_SHAPES(mi::BF16Bits, uint16_t);
+      }
+#undef MI_GREEDY_SHAPES
+#undef MI_GREEDY
+      if (nseg > 1) mi::finish_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
+      continue;
+    }
 #define MI_SAMPLE(TAG, BITS, BYTES, THREADS, SPLITF)                                                           \
   mi::sample_rows<TAG, BYTES, THREADS, SPLITF><<<static_cast<uint32_t>(n) * nseg, THREADS, lds, stream>>>(      \
       reinterpret_cast<const BITS*>(lg), logits_row_stride, mk, mask_row_stride, V, ar, r0, tokens + r0, nseg,     \

@@ -1563,6 +1563,129 @@ __global__ __launch_bounds__(1024) void split_search(SampleArgs a, const uint32_
   }
 }
 
+// The row's largest candidate and the lowest index holding it (-inf and
+// 0x7FFFFFFF when there is none), in every thread; every thread of the
+// block calls it (barriers).
+//
+// Fast form: each group's tokens are gated by their mask bits (others
+// -inf) and reduced by a max tree; a thread keeps its best value and the
+// words of the group holding it, and decodes that one group at the end
+// for the lowest index with that value.  A group maximum that is NaN or
+// +inf (possible only for rows holding such logits, which are not
+// candidates) sends the whole block through the exact per-token form.
+template <int BYTES, int THREADS, typename D>
+__device__ __forceinline__ void row_max(const RowView<D>& rv, float* best_out, int32_t* besti_out) {
+  constexpr int kWaves = THREADS / 64;
+  __shared__ float s_best[kWaves];
+  __shared__ int32_t s_besti[kWaves];
+  const int t = static_cast<int>(threadIdx.x);
+  float best = -__builtin_inff();
+  int32_t besti = 0x7FFFFFFF;
+  int32_t bestg = -1;
+  typename RowView<D>::Raw braw{};  // the best group's words, kept so it need not be read again
+  bool odd = false;
+  walk_row_raw<BYTES, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
+    float xv[8];
+    rv.gated(raw, g, full, xv);
+    const float gm = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
+                           fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
+    odd |= !(gm < __builtin_inff()) && gm != -__builtin_inff();  // NaN or +inf
+    if (gm > best) {  // strictly greater: each thread sees its groups in order
+      best = gm;
+      bestg = g;
+      braw = raw;
+    }
+  });
+  const int32_t tail_g = rv.V >> 3;  // the partial last group, if V % 8 != 0 (thread 0's)
+  float tx[8] = {};
+  const uint32_t tok = (rv.V & 7) && t == 0 ? rv.load_tail(tx) : 0u;
+  if (tok) {
+    float gm = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if ((tok >> q) & 1u) gm = fmaxf(gm, tx[q]);
+    if (gm > best) {
+      best = gm;
+      bestg = tail_g;
+    }
+  }
+  if (__syncthreads_or(odd)) {
+    best = -__builtin_inff();
+    walk_row<BYTES, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (((ok >> q) & 1u) && x[q] > best) {
+          best = x[q];
+          besti = i0 + q;
+        }
+    });
+  } else if (bestg >= 0) {
+    float x[8];
+    uint32_t ok;
+    if (bestg == tail_g && (rv.V & 7)) {
+      ok = tok;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = tx[q];
+    } else {
+      ok = rv.decode(braw, bestg, true, x);
+    }
+    for (int q = 7; q >= 0; --q)  // the lowest index holding the best value
+      if (((ok >> q) & 1u) && x[q] == best) besti = 8 * bestg + q;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(best, o);
+    const int32_t oi = __shfl_xor(besti, o);
+    if (ob > best || (ob == best && oi < besti)) {
+      best = ob;
+      besti = oi;
+    }
+  }
+  if (lane_id() == 0) {
+    s_best[t >> 6] = best;
+    s_besti[t >> 6] = besti;
+  }
+  __syncthreads();
+  best = s_best[0];
+  besti = s_besti[0];
+  for (int w = 1; w < kWaves; ++w) {
+    if (s_best[w] > best || (s_best[w] == best && s_besti[w] < besti)) {
+      best = s_best[w];
+      besti = s_besti[w];
+    }
+  }
+  *best_out = best;
+  *besti_out = besti;
+}
+
+// Greedy rows only (no row has a positive temperature): the max pass of
+// sample_rows alone, in a kernel without the filtered paths, so it holds
+// few registers and keeps BYTES of logits in flight per thread.  The same
+// rows, segments, output and atomic merge as sample_rows.
+template <typename D, int BYTES, int THREADS>
+__global__ __launch_bounds__(THREADS) void greedy_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
+                                                       const uint32_t* __restrict__ mask, int64_t ms, int32_t V,
+                                                       int64_t* __restrict__ out, int32_t nseg, int32_t seg_len) {
+  const bool split = nseg > 1;
+  const int64_t r = split ? blockIdx.x / nseg : blockIdx.x;
+  const int32_t tok0 = split ? static_cast<int32_t>(blockIdx.x % nseg) * seg_len : 0;  // segment start
+  const RowView<D> rv(logits + r * ls + tok0, mask ? mask + r * ms + tok0 / 32 : nullptr,
+                      split ? min(seg_len, V - tok0) : V);
+  float best;
+  int32_t besti;
+  row_max<BYTES, THREADS>(rv, &best, &besti);
+  if (threadIdx.x == 0) {
+    const bool none = best == -__builtin_inff();  // candidates are finite
+    if (!split) {
+      out[r] = none ? -1 : besti;
+    } else if (!none) {
+      const unsigned long long packed = (static_cast<unsigned long long>(order_key(best)) << 32) |
+                                        static_cast<uint32_t>(~static_cast<uint32_t>(tok0 + besti));
+      atomicMax(reinterpret_cast<unsigned long long*>(out) + r, packed);
+    }
+  }
+}
+
 // One block of THREADS threads per row, 128 bytes of logits in flight per
 // thread: 1024 threads when each compute unit holds one row at a time; 256
 // so several rows share a compute unit when there are many rows.  The draw,
@@ -1615,14 +1738,7 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // rows need the argmax, top-p and min-p need the max logit (their masses
   // and cutoffs are relative to it); without those the pass is skipped: the
   // Gumbel keys need no max, and top-k needs no count of candidates (a k at
-  // or above it comes out of the radix search as "keep all").
-  //
-  // Fast form: each group's tokens are gated by their mask bits (others
-  // -inf) and reduced by a max tree; a thread keeps its best value and the
-  // words of the group holding it, and decodes that one group at the end
-  // for the lowest index with that value.  A group maximum that is NaN or
-  // +inf (possible only for rows holding such logits, which are not
-  // candidates) sends the whole block through the exact per-token form.
+  // or above it comes out of the radix search as "keep all" (row_max).
   const bool first_pass = !(temp > 0.f) || top_p < 1.0f || min_p > 0.f;
   const float inv_t = 1.0f / temp;  // used only when temp > 0
   // An infinite temperature makes every z equal: each filter then keeps all
@@ -1706,80 +1822,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   const bool fused_max = first_pass && sizeof(typename D::Bits) == 4 && THREADS == 1024 && (use_k || use_p) &&
                          !have_cut && !split && rv.V <= kEdgeMassMaxTokens;
   if (first_pass && !have_best && !fused_max) {
-    int32_t besti = 0x7FFFFFFF;
-    int32_t bestg = -1;
-    typename RowView<D>::Raw braw{};  // the best group's words, kept so it need not be read again
-    bool odd = false;
-    walk_row_raw<BYTES, THREADS>(rv, [&](int32_t g, const typename RowView<D>::Raw& raw, bool full) {
-      float xv[8];
-      rv.gated(raw, g, full, xv);
-      const float gm = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
-                             fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
-      odd |= !(gm < __builtin_inff()) && gm != -__builtin_inff();  // NaN or +inf
-      if (gm > best) {  // strictly greater: each thread sees its groups in order
-        best = gm;
-        bestg = g;
-        braw = raw;
-      }
-    });
-    const int32_t tail_g = rv.V >> 3;  // the partial last group, if V % 8 != 0 (thread 0's)
-    float tx[8] = {};
-    const uint32_t tok = (rv.V & 7) && t == 0 ? rv.load_tail(tx) : 0u;
-    if (tok) {
-      float gm = -__builtin_inff();
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if ((tok >> q) & 1u) gm = fmaxf(gm, tx[q]);
-      if (gm > best) {
-        best = gm;
-        bestg = tail_g;
-      }
-    }
-    if (__syncthreads_or(odd)) {
-      best = -__builtin_inff();
-      walk_row<BYTES, THREADS>(rv, [&](int32_t i0, const float* x, uint32_t ok) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (((ok >> q) & 1u) && x[q] > best) {
-            best = x[q];
-            besti = i0 + q;
-          }
-      });
-    } else if (bestg >= 0) {
-      float x[8];
-      uint32_t ok;
-      if (bestg == tail_g && (rv.V & 7)) {
-        ok = tok;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) x[q] = tx[q];
-      } else {
-        ok = rv.decode(braw, bestg, true, x);
-      }
-      for (int q = 7; q >= 0; --q)  // the lowest index holding the best value
-        if (((ok >> q) & 1u) && x[q] == best) besti = 8 * bestg + q;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int32_t oi = __shfl_xor(besti, o);
-      if (ob > best || (ob == best && oi < besti)) {
-        best = ob;
-        besti = oi;
-      }
-    }
-    if (lane_id() == 0) {
-      s_best[wave] = best;
-      s_besti[wave] = besti;
-    }
-    __syncthreads();
-    best = s_best[0];
-    besti = s_besti[0];
-    for (int w = 1; w < kWaves; ++w) {
-      if (s_best[w] > best || (s_best[w] == best && s_besti[w] < besti)) {
-        best = s_best[w];
-        besti = s_besti[w];
-      }
-    }
+    int32_t besti;
+    row_max<BYTES, THREADS>(rv, &best, &besti);
     // candidates are finite, so the max is -inf only when there is none
     const bool none = best == -__builtin_inff();
     if (none || !(temp > 0.f)) {  // no candidate, or greedy
