@@ -1092,3 +1092,27 @@ def test_fp32_rows_past_the_fused_maximum_limit():
     for i, (k, p, m) in enumerate(((0, 0.9, 0.0), (50, 0.9, 0.02))):
         say(f"[gpu] fp32 rows of {cols} tokens k={k} p={p} m={m}")
         check_rows(bits, "float32", None, None, 1.0, k, p, m, seed=41 + i, offset=i, min_exact=0.5)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "bfloat16"])
+def test_greedy_many_rows(dtype):
+    """Greedy batches of more than 256 rows run the max-pass kernel in
+    128-thread blocks: 300 ragged rows of 3001 tokens with ties, masks, a row
+    without candidates, and NaN and infinite logits among the allowed
+    tokens (never candidates).  Exact against the oracle's argmax (lowest
+    index among ties)."""
+    rng = np.random.default_rng(223)
+    R, cols = 300, 3001
+    bits = random_logits(rng, dtype, R, cols, ties=True)
+    pos_inf, qnan = {"float32": (0x7F800000, 0x7FC00000), "float16": (0x7C00, 0x7E00),
+                     "bfloat16": (0x7F80, 0x7FC0)}[dtype]
+    for r in range(0, R, 7):
+        bits[r, rng.choice(cols, 5, replace=False)] = [qnan, pos_inf, qnan, pos_inf, qnan]
+    allowed = rng.random((R, cols)) < 0.3
+    allowed[11] = False                                  # no candidate: -1
+    mask = workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    say(f"[gpu] greedy, {R} rows {dtype}")
+    with np.errstate(invalid="ignore"):
+        tok = check_rows(bits, dtype, mask, None, 0.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
+        assert tok[11] == -1
+        check_rows(bits, dtype, None, 2990, -2.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
