@@ -2336,18 +2336,21 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
         // region room for its share plus 256 (or 512).
         uint32_t* list = reinterpret_cast<uint32_t*>(s_dyn) + wave * kListPerWave;
         uint32_t nw = 0;  // the same in every lane of the wave
+        // per group: one prefix sum of the lanes' kept counts places each
+        // lane's entries, then each lane writes its own kept tokens, so a
+        // group costs its wave one step per kept token of its busiest lane
+        // (the draw below does not depend on the list's order)
         walk16([&](int32_t i0, const typename RowView<D>::Raw& raw, uint32_t bits) {
           float x[8];
           const uint32_t keep = keep_of(raw, bits, x);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint64_t b = __ballot((keep >> q) & 1u);
-            if (b) {
-              const uint32_t pos = nw + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
-                                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0u));
-              if (((keep >> q) & 1u) && pos < kListPerWave) list[pos] = static_cast<uint32_t>(i0 + q);
-              nw += static_cast<uint32_t>(__popcll(b));
-            }
+          const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(keep));
+          if (!__ballot(cnt != 0u)) return;
+          const uint32_t incl = wave_prefix_sum(cnt);
+          uint32_t pos = nw + incl - cnt;
+          nw += lane63(incl);
+          for (uint32_t c = keep; c != 0u; c &= c - 1u) {
+            if (pos < kListPerWave) list[pos] = static_cast<uint32_t>(i0 + __builtin_ctz(c));
+            ++pos;
           }
         });
         // a wave whose region filled up sends the row through the walk below
