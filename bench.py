@@ -743,11 +743,11 @@ def touched_lines(wl, esize):
 
 
 def sampler_small_batch(torch, dev, mb, workloads, stream, steps=200):
-    """Every mode on the first B rows of the B=256 bf16 sampler shape, B = 1, 16, 64.
+    """Every mode on the first B rows of the B=256 bf16 sampler shape, B = 1, 16, 32, 64.
 
     With few rows the library splits each row over several blocks: rows
     without a filter by themselves, filtered rows through a workspace (the
-    default); these are the batch sizes where that matters.  The filtered
+    default, up to 32 rows); these are the batch sizes where that matters.  The filtered
     modes are timed without the workspace too ("one_block_per_row").  The
     rows rotate over buffer sets sized for the full batch, but B rows of
     256 KB (at most 16.8 MB a set) stay in the caches across the rotation:
@@ -761,7 +761,7 @@ def sampler_small_batch(torch, dev, mb, workloads, stream, steps=200):
     sets = [(torch.from_numpy(wl.logits.view(np.int16)).to(dev).view(torch.bfloat16), torch.from_numpy(wl.mask).to(dev))
             for _ in range(nsets)]
     out = {}
-    for B in (1, 16, 64):
+    for B in (1, 16, 32, 64):
         tok = torch.empty(B, dtype=torch.int64, device=dev)
         res = {}
         for mode, kw in (("greedy", dict(temperature=0.0)), ("unfiltered", dict(temperature=1.0)),

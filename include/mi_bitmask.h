@@ -231,7 +231,7 @@ mi_status_t mi_apply_bitmask_sample(
  * workspace that lets a small batch spread its filtered rows over many
  * compute units.  Without it, each row with top-k, top-p or min-p is drawn
  * by one block, so a batch of a few such rows leaves most of the GPU idle.
- * With it, a batch of at most 64 bf16 or fp16 rows of at least 8192 tokens
+ * With it, a batch of at most 32 bf16 or fp16 rows of at least 8192 tokens
  * splits each such row into segments: one kernel counts every segment's
  * allowed tokens under their 16-bit keys into the row's histogram in the
  * workspace, one finds the row's cut from it, and one draws over the
@@ -267,12 +267,11 @@ mi_status_t mi_apply_bitmask_sample_ws(
  * if the stream's device is not current); the call itself allocates
  * nothing and frees nothing.
  *
- * A batch whose split would need more than that array -- more than 32 bf16
- * or fp16 rows (at most 64) of at least 8192 tokens, with top-k, top-p or
- * min-p in force for some row -- is rejected with MI_ERR_BAD_SHAPE and
- * enqueues nothing; split it, or give mi_apply_bitmask_sample_ws a
- * workspace.  Every other batch runs as mi_apply_bitmask_sample_ws would,
- * with the same tokens.
+ * The array holds the workspace of the largest batch that splits (32 bf16
+ * or fp16 rows), so every batch runs as mi_apply_bitmask_sample_ws would
+ * with a workspace, with the same tokens.  A batch whose split would need
+ * more than the array (none under these limits) is rejected with
+ * MI_ERR_BAD_SHAPE and enqueues nothing.
  *
  * All calls on one GPU share its array, and each clears what it uses on its
  * own stream before using it: calls that overlap in time on one GPU (on

@@ -323,7 +323,7 @@ def test_sample_ws_rejections(name, kw, code):
 
 def test_sample_ws_checks_only_a_workspace_it_uses():
     """A workspace that is too small, or a batch that cannot split (fp32, more
-    than 64 rows, fewer than 8192 tokens), leaves the workspace unused: its
+    than 32 rows, fewer than 8192 tokens), leaves the workspace unused: its
     placement is not checked, and with zero rows nothing is launched."""
     assert sample_ws_call(LOGITS + 4096, WS_BYTES - 1, rows=0) == OK
     assert sample_ws_call(LOGITS + 4096, WS_BYTES, dtype=0, rows=0) == OK
@@ -335,8 +335,8 @@ def test_sample_workspace_bytes():
     lib = mb.load_library()
     per_row = 65536 * 4 + 128 + 16
     assert lib.mi_sample_workspace_bytes(2, 1, 128000) == per_row
-    assert lib.mi_sample_workspace_bytes(1, 64, 8192) == 64 * per_row
-    assert lib.mi_sample_workspace_bytes(1, 65, 8192) == 0       # more rows than the split takes
+    assert lib.mi_sample_workspace_bytes(1, 32, 8192) == 32 * per_row
+    assert lib.mi_sample_workspace_bytes(1, 33, 8192) == 0       # more rows than the split takes
     assert lib.mi_sample_workspace_bytes(2, 16, 8191) == 0       # rows too short to split
     assert lib.mi_sample_workspace_bytes(0, 16, 128000) == 0     # fp32 rows are not split
     assert lib.mi_sample_workspace_bytes(7, 16, 128000) == 0     # invalid dtype

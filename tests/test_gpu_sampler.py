@@ -884,15 +884,15 @@ def test_split_filtered_rows_equal_one_block_per_row(dtype):
     """A small batch of filtered 16-bit rows split over several blocks (the
     workspace) draws the same tokens as one block per row, bit for bit: the
     cut comes from the same counts and the draw from the same Gumbel keys.
-    Batch sizes 1 to 64, ragged and masked rows, rows with no candidate,
+    Batch sizes 1 to 32, ragged and masked rows, rows with no candidate,
     heavy ties, every filter alone and together, and per-row parameters that
     mix greedy, unfiltered and filtered rows in one batch."""
     rng = np.random.default_rng(67 if dtype == "float16" else 71)
-    shapes = ((1, 128000, None), (3, 50257, None), (16, 32000, 31990), (64, 8192, None), (5, 70003, 70000))
+    shapes = ((1, 128000, None), (3, 50257, None), (16, 32000, 31990), (32, 8192, None), (5, 70003, 70000))
     modes = (dict(top_k=50), dict(top_p=0.9), dict(min_p=0.05), dict(top_k=50, top_p=0.9, min_p=0.05),
              dict(top_k=1), dict(top_p=0.0), dict(top_k=1 << 20, top_p=0.999), dict(top_k=3000, temperature=0.5))
     for R, cols, V in shapes:
-        ties = R in (3, 64)
+        ties = R in (3, 32)
         bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([0.5, 2.0, 6.0])), ties=ties)
         allowed = rng.random((R, cols)) < rng.uniform(0.001, 0.9, (R, 1))
         if R > 2:
@@ -918,13 +918,13 @@ def test_split_filtered_rows_equal_one_block_per_row(dtype):
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_split_fuzz_equal_one_block(dtype):
-    """Seeded random small batches (1 to 64 rows of 8192 to 200 000 tokens,
+    """Seeded random small batches (1 to 32 rows of 8192 to 200 000 tokens,
     ragged vocab, masks of random density, value spreads with and without
     heavy ties, per-row parameters mixing every mode): the split path and one
     block per row draw the same tokens."""
     rng = np.random.default_rng(97 if dtype == "float16" else 101)
     for case in range(8):
-        R = int(rng.integers(1, 65))
+        R = int(rng.integers(1, 33))
         cols = int(rng.integers(8192, 200001))
         V = int(rng.integers(8192, cols + 1))
         ties = bool(rng.integers(0, 2))

@@ -74,7 +74,7 @@ CASES = [
     # name, dtype, V, sigma, rows, calls, filters, mask density, tolerance
     ("bf16 1024-thread blocks", "bfloat16", 200, 2.0, 256, 4000, dict(temperature=0.8, top_k=40), None, 0.002),
     ("fp16 512-thread blocks", "float16", 300, 2.0, 1024, 1000, dict(temperature=1.0, top_p=0.8), 0.7, 0.002),
-    ("bf16 split path", "bfloat16", 8192, 3.0, 64, 16000, dict(temperature=1.0, top_k=50, min_p=0.02), None, 0.002),
+    ("bf16 split path", "bfloat16", 8192, 3.0, 32, 32000, dict(temperature=1.0, top_k=50, min_p=0.02), None, 0.002),
     ("fp32 coarse cut", "float32", 500, 2.0, 256, 4000, dict(temperature=1.0, top_k=30, top_p=0.9), None, 0.002),
     ("fp32 top-k alone", "float32", 700, 2.0, 256, 4000, dict(temperature=1.2, top_k=25), 0.8, 0.002),
     ("fp32 radix passes (above 256 rows)", "float32", 300, 2.0, 512, 2000, dict(temperature=1.0, top_p=0.7), None,
