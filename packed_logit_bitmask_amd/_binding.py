@@ -289,10 +289,11 @@ def mi_apply_bitmask_sample(logits, mask=None, vocab_size: Optional[int] = None,
     gets -1.
 
     ``workspace``: device memory that lets a small batch of filtered bf16 or
-    fp16 rows spread over many compute units (``mi_apply_bitmask_sample_ws``;
-    the tokens are the same either way).  "auto" allocates one when the call
-    can use it, None uses none, and a device tensor is used as it is (at
-    least ``sample_workspace_bytes`` bytes; calls sharing it must not overlap).
+    fp16 rows spread over many compute units, and a large one hand out its
+    dense rows first (``mi_apply_bitmask_sample_ws``; the tokens are the same
+    either way).  "auto" allocates one when the call can use it, None uses
+    none, and a device tensor is used as it is (at least
+    ``sample_workspace_bytes`` bytes; calls sharing it must not overlap).
     """
     torch = _torch()
     lib = load_library()

@@ -45,6 +45,13 @@ constexpr int64_t kFine8Vocab = 65536;
 // faster for top-k and for the filters together, and ties for top-p.
 constexpr int64_t kSplitFilteredRows = 32;
 constexpr int64_t kSplitHistBlocks = 256;
+
+// Filtered 16-bit batches of more rows than compute units, at most this
+// many, hand out their heavy rows first (row_classes, heavy_first_row in
+// sample_kernel.h) when the caller gives a workspace for one bit per row
+// (rounded up to 256 bytes).  Every wave of sample_rows then ranks the
+// batch's flags in its prologue, 128 rows per lane.
+constexpr int64_t kOrderMaxRows = 8192;
 constexpr int64_t kMaxHistSegments = 8;
 constexpr int64_t kSplitHistMaxSeg = 65280;
 
@@ -91,6 +98,24 @@ namespace {
 // over several blocks through the workspace): few rows, long enough to split.
 bool split_filtered_batch(mi_dtype_t dtype, int64_t rows, int64_t V) {
   return dtype != MI_DTYPE_F32 && rows >= 1 && rows <= kSplitFilteredRows && V >= 8192;
+}
+
+// Whether a batch may order its rows heavy first through the workspace: the
+// 16-bit rows of the 8-bit-counter search (more rows than kFine16Rows, at
+// most kFine8Vocab tokens), longer than a 512-thread block holds in
+// registers, so that a sparse row takes the listed search and costs far
+// less than a dense one.  (At 8192 tokens, where every row is held in
+// registers, ordering B=1024 fp16 rows cost 2.5 us more than it saved.)
+bool ordered_batch(mi_dtype_t dtype, int64_t rows, int64_t V) {
+  return dtype != MI_DTYPE_F32 && rows > kFine16Rows && rows <= kOrderMaxRows && V > 4 * 8 * 512 &&
+         V <= kFine8Vocab;
+}
+
+// Workspace bytes a batch can use (0: none).
+int64_t workspace_need(mi_dtype_t dtype, int64_t rows, int64_t V) {
+  if (split_filtered_batch(dtype, rows, V)) return mi::split_workspace_bytes(rows);
+  if (ordered_batch(dtype, rows, V)) return (mi::row_class_bytes(rows) + 255) / 256 * 256;
+  return 0;
 }
 
 constexpr int kMaxDevices = 256;
@@ -158,14 +183,18 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
                         static_cast<const void*>(params->top_p), static_cast<const void*>(params->min_p)})
     if (reinterpret_cast<uintptr_t>(q) % 4) return fail(MI_ERR_MISALIGNED, "a per-row parameter array is not 4-byte aligned");
   // The workspace is used only when this batch can split its filtered rows
-  // and it is large enough; then it must not overlap anything else.
-  const int64_t ws_need = split_filtered_batch(dtype, rows, p.V) ? mi::split_workspace_bytes(rows) : 0;
-  // whether any row may take a filter (only such batches split through a workspace)
+  // or order them heavy first, and it is large enough; then it must not
+  // overlap anything else.
+  const int64_t ws_need = workspace_need(dtype, rows, p.V);
+  // whether any row may take a filter (only such batches use a workspace)
   const bool params_filter = params->top_k || params->top_p || params->min_p || params->top_k_all > 0 ||
                              params->top_p_all < 1.0f || params->min_p_all > 0.f;
   if (use_scratch) {
-    // kNoAllocRows equals the split limit, so no batch needs more than the
-    // array holds; the check guards the two limits against drifting apart.
+    // kNoAllocRows equals the split limit, and the flags of the largest
+    // ordered batch take far less, so no batch needs more than the array
+    // holds; the check guards the limits against drifting apart.
+    static_assert((mi::row_class_bytes(kOrderMaxRows) + 255) / 256 * 256 <= kScratchBytes,
+                  "the scratch holds the flags of the largest ordered batch");
     if (params_filter && ws_need > kScratchBytes)
       return fail(MI_ERR_BAD_SHAPE,
                   "%lld rows of %lld tokens need %lld bytes of scratch; the no-alloc entry point holds %lld "
@@ -238,7 +267,7 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
     const bool greedy_only = !ar.temperature && !(ar.temperature_all > 0.f);
     // With a workspace, a small batch that may filter splits its rows too
     // (split_hist, split_search, then a segmented draw).
-    const bool split_filtered = use_ws && (may_filter || may_min_p);
+    const bool split_filtered = use_ws && split_filtered_batch(dtype, rows, p.V) && (may_filter || may_min_p);
     int32_t nseg = 1, seg_len = V;
     if ((split_filtered || (!may_filter && !may_min_p && n <= (greedy_only ? kSplitRowsGreedy : kSplitRows))) &&
         V >= 8192) {
@@ -247,6 +276,18 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
       nseg = (V + seg_len - 1) / seg_len;
     }
     const bool fine8 = fine && n > kFine16Rows && V <= kFine8Vocab;
+    // heavy rows first: with top-p or min-p, whose draws over a dense row
+    // may take most of its tokens (top-k's keep few), and a mask to tell
+    // dense rows from sparse ones
+    const bool may_p = ar.top_p || ar.top_p_all < 1.0f;
+    const uint32_t* heavy = nullptr;
+    if (use_ws && ordered_batch(dtype, rows, p.V) && fine8 && nseg == 1 && mk && (may_p || may_min_p)) {
+      static_assert(kOrderMaxRows <= 128 * 64, "heavy_first_row reads at most 128 rows' flags per lane");
+      static_assert(kFine8Vocab <= mi::kRowClassesMaxVocab, "row_classes reads the whole mask row");
+      uint16_t* flags = static_cast<uint16_t*>(workspace);
+      mi::row_classes<<<(n + 15) / 16, 1024, 0, stream>>>(mk, mask_row_stride, V, static_cast<int32_t>(n), flags);
+      heavy = reinterpret_cast<const uint32_t*>(flags);
+    }
     const bool deep = (n <= 256 || fine) && nseg == 1;
     const int threads = fine8 ? 512 : deep ? 1024 : 256;
     // the 16-bit counters: filtered 16-bit rows, and fp32 rows in 1024-thread
@@ -315,26 +356,28 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
       if (nseg > 1) mi::finish_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
       continue;
     }
-#define MI_SAMPLE(TAG, BITS, BYTES, THREADS, SPLITF)                                                           \
-  mi::sample_rows<TAG, BYTES, THREADS, SPLITF><<<static_cast<uint32_t>(n) * nseg, THREADS, lds, stream>>>(      \
+#define MI_SAMPLE(TAG, BITS, BYTES, THREADS, SPLITF, HEAVY)                                                    \
+  mi::sample_rows<TAG, BYTES, THREADS, SPLITF, HEAVY><<<static_cast<uint32_t>(n) * nseg, THREADS, lds, stream>>>( \
       reinterpret_cast<const BITS*>(lg), logits_row_stride, mk, mask_row_stride, V, ar, r0, tokens + r0, nseg,     \
-      seg_len, sinfo)
+      seg_len, sinfo, heavy)
     switch (dtype) {
       case MI_DTYPE_F32:
-        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024, false);
-        else MI_SAMPLE(mi::F32Bits, uint32_t, 128, 256, false);
+        if (deep) MI_SAMPLE(mi::F32Bits, uint32_t, 128, 1024, false, false);
+        else MI_SAMPLE(mi::F32Bits, uint32_t, 128, 256, false, false);
         break;
       case MI_DTYPE_F16:
-        if (sinfo) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, true);
-        else if (fine8) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512, false);
-        else if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024, false);
-        else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, false);
+        if (sinfo) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, true, false);
+        else if (fine8 && heavy) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512, false, true);
+        else if (fine8) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512, false, false);
+        else if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024, false, false);
+        else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, false, false);
         break;
       default:
-        if (sinfo) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, true);
-        else if (fine8) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512, false);
-        else if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024, false);
-        else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, false);
+        if (sinfo) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, true, false);
+        else if (fine8 && heavy) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512, false, true);
+        else if (fine8) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512, false, false);
+        else if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024, false, false);
+        else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, false, false);
     }
 #undef MI_SAMPLE
     if (nseg > 1) mi::finish_tokens<<<(n + 255) / 256, 256, 0, stream>>>(tokens + r0, n);
@@ -372,5 +415,5 @@ MI_API mi_status_t mi_apply_bitmask_sample_noalloc(const void* logits, mi_dtype_
 
 MI_API int64_t mi_sample_workspace_bytes(mi_dtype_t dtype, int64_t rows, int64_t vocab) {
   if (!valid_dtype(static_cast<int>(dtype)) || rows < 0 || vocab < 0 || vocab > kMaxSampleVocab) return 0;
-  return split_filtered_batch(dtype, rows, vocab) ? mi::split_workspace_bytes(rows) : 0;
+  return workspace_need(dtype, rows, vocab);
 }

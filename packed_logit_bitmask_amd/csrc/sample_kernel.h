@@ -16,7 +16,9 @@
 // block per segment of a row, the segments merging by an atomic maximum.  A
 // few filtered 16-bit rows split the same way when the caller gives a
 // workspace: their cuts come first from merged per-segment histograms
-// (split_hist, split_search below).
+// (split_hist, split_search below).  Given a workspace, a large batch of
+// filtered 16-bit rows hands out its dense rows first (row_classes,
+// heavy_first_row below), so that they spread over the compute units.
 // Each pass walks the row in groups of 8 consecutive tokens per thread
 // through raw buffer loads (16-byte vectors when the row start is aligned),
 // several groups in flight per thread; trip counts are uniform across the
@@ -1684,6 +1686,99 @@ __global__ __launch_bounds__(THREADS) void greedy_rows(const typename D::Bits* _
   }
 }
 
+// ---- Heavy rows first, for large filtered batches.  A block's time on a
+// filtered row grows with what its mask allows: a row allowing more than
+// kSparseMax tokens builds the full key histogram and, under top-p or
+// min-p, may draw over most of its tokens, while a sparse row lists a few
+// thousand candidates.  With more rows than resident blocks, blocks start
+// in grid order and the hardware fills each compute unit's slots as they
+// free up, so in a batch that mixes the two kinds at random some units get
+// two heavy rows at once, or a heavy row late, and set the launch's end.
+// row_classes marks the heavy rows; sample_rows then hands them out first,
+// in row order, then the rest.  Rows are independent, so the tokens do not
+// change with the order.
+
+// Bit r of the flags (32-bit words, bit r % 32 of word r / 32) = row r's
+// mask allows more than kSparseMax tokens below V.  One wave per row, 16
+// rows to a 1024-thread block, which stores their 16 bits as one 16-bit
+// word; a row has at most 65536 tokens (kRowClassesMaxVocab), 2048 mask
+// words, 32 per lane, all requested at once through a buffer resource
+// that ends at the row's last word (loads past it return 0).
+constexpr int32_t kRowClassesMaxVocab = 65536;
+__global__ __launch_bounds__(1024) void row_classes(const uint32_t* __restrict__ mask, int64_t ms, int32_t V,
+                                                    int32_t rows, uint16_t* __restrict__ flags) {
+  constexpr int kPerLane = kRowClassesMaxVocab / 32 / 64;
+  __shared__ uint32_t s_flag[16];
+  const int32_t wave = static_cast<int32_t>(threadIdx.x >> 6);
+  const int32_t r = static_cast<int32_t>(blockIdx.x) * 16 + wave;
+  const int32_t lane = static_cast<int32_t>(threadIdx.x & 63u);
+  const int32_t W = (V + 31) / 32;
+  // a wave past the last row reads nothing (a resource of size 0)
+  const Rsrc rm = make_rsrc(r < rows ? mask + static_cast<int64_t>(r) * ms : mask,
+                            r < rows ? static_cast<uint32_t>(W) * 4u : 0u);
+  uint32_t x[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) x[j] = load_word(rm, (lane + 64 * j) * 4);
+  const uint32_t tail = (V & 31) ? (1u << (V & 31)) - 1u : ~0u;  // bits of the last word below V
+  uint32_t n = 0;
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) n += __builtin_popcount(lane + 64 * j == W - 1 ? x[j] & tail : x[j]);
+  n = lane63(wave_prefix_sum(n));
+  if (lane == 0) s_flag[wave] = n > kSparseMax ? 1u : 0u;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) bits |= s_flag[w] << w;
+    flags[blockIdx.x] = static_cast<uint16_t>(bits);
+  }
+}
+
+// Bytes of the flags of n rows as row_classes stores them.
+constexpr int64_t row_class_bytes(int64_t n) { return (n + 15) / 16 * 2; }
+
+// The row block b takes when the heavy rows go first: the b-th heavy row
+// of the n, or the (b - heavy rows)-th of the others, each in row order.
+// Every wave works it out alone from the flag words (n <= 8192: lane l
+// reads words 4 l to 4 l + 3, rows 128 l to 128 l + 127, as one 16-byte
+// load; bits at or past n are ignored), with one wave prefix sum, so the
+// block needs no barrier.  The result is the same in every lane and kept
+// scalar, so that the row's addresses stay in scalar registers.
+__device__ __forceinline__ int64_t heavy_first_row(const uint32_t* __restrict__ flags, uint32_t n, uint32_t b) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint4 f = load16(make_rsrc(flags, static_cast<uint32_t>((row_class_bytes(n) + 15) / 16 * 16)),
+                         static_cast<int32_t>(16u * lane));
+  const uint32_t lo = min(n, 128u * lane);
+  const uint32_t w[4] = {f.x, f.y, f.z, f.w};
+  uint32_t m[4], c = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t valid = min(32u, n - min(n, lo + 32u * k));  // rows of word k below n
+    m[k] = valid == 32u ? ~0u : (1u << valid) - 1u;
+    c += static_cast<uint32_t>(__builtin_popcount(w[k] & m[k]));
+  }
+  const uint32_t rows_here = min(n, lo + 128u) - lo;
+  const uint32_t incl = wave_prefix_sum(c);
+  const uint32_t total = lane63(incl), hb = incl - c;  // heavy rows in all, and below lo
+  const bool heavy = b < total;
+  const uint32_t j = heavy ? b - hb : b - total - (lo - hb);  // rank among this lane's heavy / light rows
+  const bool mine = heavy ? (hb <= b && b < incl) : (b >= total && lo - hb <= b - total && j < rows_here - c);
+  // this lane's j-th heavy (or light) row
+  uint32_t row = 0, k_left = j;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t x = (heavy ? w[k] : ~w[k]) & m[k];
+    const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(x));
+    if (k_left < cnt && row == 0u) {
+      for (uint32_t q = k_left; q; --q) x &= x - 1u;
+      row = lo + 32u * k + static_cast<uint32_t>(__builtin_ctz(x)) + 1u;  // + 1: found
+    }
+    k_left = k_left >= cnt ? k_left - cnt : 0u;
+  }
+  const unsigned long long owner = __ballot(mine);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(row), __builtin_ctzll(owner))) - 1u;
+}
+
 // One block of THREADS threads per row, 128 bytes of logits in flight per
 // thread: 1024 threads when each compute unit holds one row at a time; 256
 // so several rows share a compute unit when there are many rows.  The draw,
@@ -1696,12 +1791,13 @@ __global__ __launch_bounds__(THREADS) void greedy_rows(const typename D::Bits* _
 // Gumbel key, inverted token index), so the largest wins and ties go to the
 // lowest index.  out must hold 0 beforehand (clear_tokens) and is turned
 // into token numbers afterwards (finish_tokens).
-template <typename D, int BYTES, int THREADS, bool SPLITF = false>
+template <typename D, int BYTES, int THREADS, bool SPLITF = false, bool HEAVY = false>
 __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* __restrict__ logits, int64_t ls,
                                                               const uint32_t* __restrict__ mask, int64_t ms,
                                                               int32_t V, SampleArgs a, int64_t row_base,
                                                               int64_t* __restrict__ out, int32_t nseg,
-                                                              int32_t seg_len, const SplitInfo* __restrict__ info) {
+                                                              int32_t seg_len, const SplitInfo* __restrict__ info,
+                                                              const uint32_t* __restrict__ heavy) {
   constexpr int kWaves = THREADS / 64;
   __shared__ float s_best[kWaves];
   __shared__ int32_t s_besti[kWaves];
@@ -1712,7 +1808,12 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   auto hist_m = reinterpret_cast<unsigned long long(*)[256]>(s_dyn);
   auto hist_n = reinterpret_cast<uint32_t(*)[256]>(s_dyn + kWaves * 256);
 
-  const int64_t r = nseg > 1 ? blockIdx.x / nseg : blockIdx.x;
+  // HEAVY: heavy rows first, by the flags of row_classes (one block per
+  // row); a separate instantiation, so that the other launches carry none
+  // of its code
+  int64_t r;
+  if constexpr (HEAVY) r = heavy_first_row(heavy, gridDim.x, blockIdx.x);
+  else r = nseg > 1 ? blockIdx.x / nseg : blockIdx.x;
   const int32_t tok0 = nseg > 1 ? static_cast<int32_t>(blockIdx.x % nseg) * seg_len : 0;  // segment start
   const bool split = nseg > 1;
   const int t = static_cast<int>(threadIdx.x);

@@ -1116,3 +1116,134 @@ def test_greedy_many_rows(dtype):
         tok = check_rows(bits, dtype, mask, None, 0.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
         assert tok[11] == -1
         check_rows(bits, dtype, None, 2990, -2.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
+
+
+def mixed_density_mask(rng, R, cols, V):
+    """Masks of R rows mixing the kinds a grammar batch holds: dense rows
+    (30 % to all of the tokens allowed), sparse rows (a few hundred to 4096
+    allowed), rows allowing exactly 4096 and 4097 tokens below V (either
+    side of the sparse-row limit) and rows allowing none."""
+    allowed = np.zeros((R, cols), dtype=bool)
+    kind = rng.choice(4, R, p=[0.25, 0.65, 0.05, 0.05])
+    for r in range(R):
+        if kind[r] == 0:
+            allowed[r] = rng.random(cols) < rng.uniform(0.3, 1.0)
+        elif kind[r] == 1:
+            allowed[r, rng.choice(V, int(rng.integers(200, 4097)), replace=False)] = True
+        elif kind[r] == 2:
+            allowed[r, rng.choice(V, 4096 + (r & 1), replace=False)] = True
+    return workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_heavy_rows_first_tokens_do_not_depend_on_the_order(dtype):
+    """Filtered batches of 257 to 8192 rows of more than 16 384 tokens,
+    given a workspace, hand out their dense rows first (a pass marks each
+    row dense or sparse from its mask; every wave then finds its block's row
+    by rank), so a row's block depends on the whole batch.  Its token must
+    not: the batch without a workspace (row order), and a prefix of it
+    (ordered differently, or not at all at 256 rows and fewer), draw the
+    same tokens, for every mode that orders (top-p, min-p, the filters
+    together, per-row parameters) and top-k alone, which does not; ragged
+    vocab, rows either side of the sparse-row limit and rows allowing
+    nothing."""
+    rng = np.random.default_rng(227 if dtype == "float16" else 229)
+    modes = (dict(top_p=0.9), dict(min_p=0.05, top_p=0.95), dict(top_k=50, top_p=0.9, min_p=0.05), dict(top_k=50),
+             dict(top_p=0.5, temperature=0.7))
+    for R, cols, V, prefixes in ((1024, 32000, None, (1000, 600, 256)), (600, 50257, 50000, (257, 200)),
+                                 (2048, 20000, 19999, (1500, 256))):
+        bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([1.0, 3.0])), ties=R == 600)
+        mask = mixed_density_mask(rng, R, cols, V or cols)
+        dl = dev_logits(bits, dtype)
+        dm = torch.from_numpy(mask).to("cuda")
+        T = torch.from_numpy(rng.choice([0.0, 0.8, 1.0, 1.5], R).astype(np.float32)).to("cuda")
+        k = torch.from_numpy(rng.choice([0, 1, 40, 3000], R).astype(np.int32)).to("cuda")
+        p = torch.from_numpy(rng.choice([1.0, 0.95, 0.6], R).astype(np.float32)).to("cuda")
+        m = torch.from_numpy(rng.choice([0.0, 0.0, 0.1], R).astype(np.float32)).to("cuda")
+        assert mb.sample_workspace_bytes(TORCH[dtype][1], R, V or cols) > 0
+        for i, kw in enumerate(modes + ("per-row",)):
+            say(f"[gpu] heavy rows first {dtype} R={R} cols={cols} V={V} {kw}")
+            if kw == "per-row":
+                call = lambda n, ws="auto": mb.mi_apply_bitmask_sample(
+                    dl[:n], dm[:n], V, temperature=T[:n], top_k=k[:n], top_p=p[:n], min_p=m[:n], seed=5, offset=1,
+                    workspace=ws).cpu().numpy()
+            else:
+                call = lambda n, ws="auto", kw=kw, i=i: mb.mi_apply_bitmask_sample(
+                    dl[:n], dm[:n], V, seed=17 + i, offset=R, workspace=ws, **kw).cpu().numpy()
+            whole = call(R)
+            natural = call(R, None)
+            assert np.array_equal(whole, natural), (R, kw, np.flatnonzero(whole != natural)[:8])
+            for n in prefixes:
+                part = call(n)
+                assert np.array_equal(whole[:n], part), (R, n, kw, np.flatnonzero(whole[:n] != part)[:8])
+        del dl, dm
+
+
+def test_heavy_rows_first_largest_batch():
+    """8192 rows (the most that are ordered) against 8193 (taken in row
+    order): the first 8192 tokens agree, with top-p and min-p."""
+    rng = np.random.default_rng(231)
+    R, cols = 8193, 16400
+    bits = random_logits(rng, "bfloat16", R, cols)
+    mask = mixed_density_mask(rng, R, cols, cols)
+    dl = dev_logits(bits, "bfloat16")
+    dm = torch.from_numpy(mask).to("cuda")
+    assert mb.sample_workspace_bytes(torch.bfloat16, R, cols) == 0
+    assert mb.sample_workspace_bytes(torch.bfloat16, 8192, cols) > 0
+    say("[gpu] heavy rows first: 8193 rows against their first 8192")
+    whole = mb.mi_apply_bitmask_sample(dl, dm, None, top_p=0.9, min_p=0.02, seed=9).cpu().numpy()
+    part = mb.mi_apply_bitmask_sample(dl[:8192], dm[:8192], None, top_p=0.9, min_p=0.02, seed=9).cpu().numpy()
+    assert np.array_equal(whole[:8192], part), np.flatnonzero(whole[:8192] != part)[:8]
+
+
+def test_heavy_rows_first_against_the_oracle():
+    """The ordered path against the oracle directly: 300 fp16 rows of 17 000
+    tokens of mixed density, top-p with min-p, and per-row parameters."""
+    rng = np.random.default_rng(233)
+    R, cols = 300, 17000
+    bits = random_logits(rng, "float16", R, cols)
+    mask = mixed_density_mask(rng, R, cols, cols)
+    say("[gpu] heavy rows first against the oracle, top-p 0.9 min-p 0.05")
+    check_rows(bits, "float16", mask, None, 1.0, 0, 0.9, 0.05, seed=3, offset=4)
+    T = rng.choice([0.0, 0.7, 1.3], R).astype(np.float32)
+    p = rng.choice([1.0, 0.8, 0.3], R).astype(np.float32)
+    say("[gpu] heavy rows first against the oracle, per-row parameters")
+    check_rows(bits, "float16", mask, None, T, 0, p, 0.0, seed=4, offset=5)
+
+
+def test_heavy_rows_first_dirty_workspace_and_graph():
+    """The ordering workspace, filled with garbage, serves two calls in a row
+    (the second with fewer rows); then the two kernels of the ordered path,
+    captured in a HIP graph with the workspace allocated during capture,
+    replay to the tokens of row order three times, with eager work in
+    between."""
+    rng = np.random.default_rng(239)
+    R, cols = 1024, 32000
+    bits = random_logits(rng, "bfloat16", R, cols)
+    dl = dev_logits(bits, "bfloat16")
+    dm = torch.from_numpy(mixed_density_mask(rng, R, cols, cols)).to("cuda")
+    ws = torch.full((mb.sample_workspace_bytes(torch.bfloat16, R, cols),), 0xFF, dtype=torch.uint8, device="cuda")
+    for n in (R, 300):
+        say(f"[gpu] ordering workspace reused, {n} rows")
+        want = mb.mi_apply_bitmask_sample(dl[:n], dm[:n], None, top_p=0.9, seed=3, workspace=None)
+        got = mb.mi_apply_bitmask_sample(dl[:n], dm[:n], None, top_p=0.9, seed=3, workspace=ws)
+        assert torch.equal(want, got)
+    modes = (dict(top_p=0.9), dict(top_k=50, top_p=0.9, min_p=0.05))
+    want = [mb.mi_apply_bitmask_sample(dl, dm, None, seed=11, workspace=None, **kw).cpu() for kw in modes]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        outs = [mb.mi_apply_bitmask_sample(dl, dm, None, seed=11, **kw) for kw in modes]   # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = [mb.mi_apply_bitmask_sample(dl, dm, None, seed=11, **kw) for kw in modes]
+    for rep in range(3):
+        say(f"[gpu] ordered path graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for k in range(len(modes)):
+            assert torch.equal(outs[k].cpu(), want[k]), (rep, modes[k])
+        (dl.float() * 2).sum().item()
+    del g

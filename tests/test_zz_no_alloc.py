@@ -6,7 +6,8 @@ the C ABI, its tokens must equal mi_apply_bitmask_sample_ws's (given a
 workspace it allocated) exactly: the same cut from the same counts, the same
 Gumbel keys.  Two calls in a row, the second smaller, so the second runs on
 what the first left in the array; then batches that need no workspace (the
-split path takes at most 32 rows, which the array holds) run as before.
+split path takes at most 32 rows, which the array holds) run as before, and
+large filtered batches keep their heavy-rows-first flags in the array.
 """
 
 import sys
@@ -99,3 +100,16 @@ def test_noalloc_batches_without_workspace():
     x, m, _ = case(6, "bfloat16", 16, 9000)
     need, a, b = both(x, m, temperature=0.0, top_k=5)
     assert torch.equal(a, b)
+
+
+def test_noalloc_orders_large_batches():
+    # more filtered 16-bit rows than compute units: the dense rows go first,
+    # their flags in the scratch; two calls in a row, the second smaller
+    for seed, dtype, rows in ((7, "float16", 1024), (8, "bfloat16", 300)):
+        say(f"[gpu] no-alloc sampler: {rows} {dtype} rows x 20000, top-p, heavy rows first")
+        x, m, _ = case(seed, dtype, rows, 20000)
+        dense = torch.rand(rows, device="cuda") < 0.3
+        m[dense] = -1                                   # all allowed: dense rows among sparse ones
+        need, a, b = both(x, m, temperature=1.0, top_p=0.9, min_p=0.02, seed=seed)
+        assert need > 0 and torch.equal(a, b)
+        assert (a >= 0).all()
