@@ -1118,11 +1118,12 @@ def test_greedy_many_rows(dtype):
         check_rows(bits, dtype, None, 2990, -2.0, 0, 1.0, 0.0, seed=1, offset=0, min_exact=1.0)
 
 
-def mixed_density_mask(rng, R, cols, V):
+def mixed_density_mask(rng, R, cols, V, pad_words=0):
     """Masks of R rows mixing the kinds a grammar batch holds: dense rows
     (30 % to all of the tokens allowed), sparse rows (a few hundred to 4096
     allowed), rows allowing exactly 4096 and 4097 tokens below V (either
-    side of the sparse-row limit) and rows allowing none."""
+    side of the sparse-row limit) and rows allowing none; pad_words more
+    words per row than the columns need, holding random bits."""
     allowed = np.zeros((R, cols), dtype=bool)
     kind = rng.choice(4, R, p=[0.25, 0.65, 0.05, 0.05])
     for r in range(R):
@@ -1132,7 +1133,7 @@ def mixed_density_mask(rng, R, cols, V):
             allowed[r, rng.choice(V, int(rng.integers(200, 4097)), replace=False)] = True
         elif kind[r] == 2:
             allowed[r, rng.choice(V, 4096 + (r & 1), replace=False)] = True
-    return workloads.pack_allowed(allowed, (cols + 31) // 32, rng)
+    return workloads.pack_allowed(allowed, (cols + 31) // 32 + pad_words, rng)
 
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
@@ -1145,15 +1146,15 @@ def test_heavy_rows_first_tokens_do_not_depend_on_the_order(dtype):
     (ordered differently, or not at all at 256 rows and fewer), draw the
     same tokens, for every mode that orders (top-p, min-p, the filters
     together, per-row parameters) and top-k alone, which does not; ragged
-    vocab, rows either side of the sparse-row limit and rows allowing
-    nothing."""
+    vocab, padded mask rows, rows either side of the sparse-row limit and
+    rows allowing nothing."""
     rng = np.random.default_rng(227 if dtype == "float16" else 229)
     modes = (dict(top_p=0.9), dict(min_p=0.05, top_p=0.95), dict(top_k=50, top_p=0.9, min_p=0.05), dict(top_k=50),
              dict(top_p=0.5, temperature=0.7))
     for R, cols, V, prefixes in ((1024, 32000, None, (1000, 600, 256)), (600, 50257, 50000, (257, 200)),
                                  (2048, 20000, 19999, (1500, 256))):
         bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([1.0, 3.0])), ties=R == 600)
-        mask = mixed_density_mask(rng, R, cols, V or cols)
+        mask = mixed_density_mask(rng, R, cols, V or cols, pad_words=3 if R == 2048 else 0)
         dl = dev_logits(bits, dtype)
         dm = torch.from_numpy(mask).to("cuda")
         T = torch.from_numpy(rng.choice([0.0, 0.8, 1.0, 1.5], R).astype(np.float32)).to("cuda")
