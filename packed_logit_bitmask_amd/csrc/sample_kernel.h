@@ -1743,8 +1743,11 @@ constexpr int64_t row_class_bytes(int64_t n) { return (n + 15) / 16 * 2; }
 // reads words 4 l to 4 l + 3, rows 128 l to 128 l + 127, as one 16-byte
 // load; bits at or past n are ignored), with one wave prefix sum, so the
 // block needs no barrier.  The result is the same in every lane and kept
-// scalar, so that the row's addresses stay in scalar registers.
-__device__ __forceinline__ int64_t heavy_first_row(const uint32_t* __restrict__ flags, uint32_t n, uint32_t b) {
+// scalar, so that the row's addresses stay in scalar registers.  *dense
+// says whether the row is a heavy one (its mask allows more than
+// kSparseMax tokens).
+__device__ __forceinline__ int64_t heavy_first_row(const uint32_t* __restrict__ flags, uint32_t n, uint32_t b,
+                                                   bool* dense) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint4 f = load16(make_rsrc(flags, static_cast<uint32_t>((row_class_bytes(n) + 15) / 16 * 16)),
                          static_cast<int32_t>(16u * lane));
@@ -1761,6 +1764,7 @@ __device__ __forceinline__ int64_t heavy_first_row(const uint32_t* __restrict__ 
   const uint32_t incl = wave_prefix_sum(c);
   const uint32_t total = lane63(incl), hb = incl - c;  // heavy rows in all, and below lo
   const bool heavy = b < total;
+  *dense = heavy;
   const uint32_t j = heavy ? b - hb : b - total - (lo - hb);  // rank among this lane's heavy / light rows
   const bool mine = heavy ? (hb <= b && b < incl) : (b >= total && lo - hb <= b - total && j < rows_here - c);
   // this lane's j-th heavy (or light) row
@@ -1812,7 +1816,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
   // row); a separate instantiation, so that the other launches carry none
   // of its code
   int64_t r;
-  if constexpr (HEAVY) r = heavy_first_row(heavy, gridDim.x, blockIdx.x);
+  bool known_dense = false;  // the row allows more than kSparseMax tokens (from row_classes)
+  if constexpr (HEAVY) r = heavy_first_row(heavy, gridDim.x, blockIdx.x, &known_dense);
   else r = nseg > 1 ? blockIdx.x / nseg : blockIdx.x;
   const int32_t tok0 = nseg > 1 ? static_cast<int32_t>(blockIdx.x % nseg) * seg_len : 0;  // segment start
   const bool split = nseg > 1;
@@ -1888,7 +1893,8 @@ __global__ __launch_bounds__(THREADS) void sample_rows(const typename D::Bits* _
     // a sparse row: the cuts from a list of its candidates, which the draw
     // then walks (sparse_search)
     if constexpr (THREADS == 512 || THREADS == 1024) {
-      if ((use_k || use_p) && !from_split && !preloaded && rv.has_mask) {
+      // (a row row_classes found dense would fail its count: skip it)
+      if ((use_k || use_p) && !from_split && !preloaded && rv.has_mask && !known_dense) {
         sparse = sparse_search<D, THREADS>(rv, reinterpret_cast<uint32_t*>(s_dyn), inv_t, use_k, top_k, use_p, top_p,
                                            &best, &cut16, &sparse_nw);
         if (sparse) {
