@@ -284,8 +284,11 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
     if (use_ws && ordered_batch(dtype, rows, p.V) && fine8 && nseg == 1 && mk && (may_p || may_min_p)) {
       static_assert(kOrderMaxRows <= 128 * 64, "heavy_first_row reads at most 128 rows' flags per lane");
       static_assert(kFine8Vocab <= mi::kRowClassesMaxVocab, "row_classes reads the whole mask row");
-      uint16_t* flags = static_cast<uint16_t*>(workspace);
-      mi::row_classes<<<(n + 15) / 16, 1024, 0, stream>>>(mk, mask_row_stride, V, static_cast<int32_t>(n), flags);
+      uint8_t* flags = static_cast<uint8_t*>(workspace);
+      if (V <= 64 * 16 * 32)
+        mi::row_classes<16><<<(n + 7) / 8, 512, 0, stream>>>(mk, mask_row_stride, V, static_cast<int32_t>(n), flags);
+      else
+        mi::row_classes<32><<<(n + 7) / 8, 512, 0, stream>>>(mk, mask_row_stride, V, static_cast<int32_t>(n), flags);
       heavy = reinterpret_cast<const uint32_t*>(flags);
     }
     const bool deep = (n <= 256 || fine) && nseg == 1;

@@ -1699,43 +1699,43 @@ __global__ __launch_bounds__(THREADS) void greedy_rows(const typename D::Bits* _
 // change with the order.
 
 // Bit r of the flags (32-bit words, bit r % 32 of word r / 32) = row r's
-// mask allows more than kSparseMax tokens below V.  One wave per row, 16
-// rows to a 1024-thread block, which stores their 16 bits as one 16-bit
-// word; a row has at most 65536 tokens (kRowClassesMaxVocab), 2048 mask
-// words, 32 per lane, all requested at once through a buffer resource
-// that ends at the row's last word (loads past it return 0).
+// mask allows more than kSparseMax tokens below V.  One wave per row, 8
+// rows to a 512-thread block, which stores their 8 bits as one byte; a row
+// has at most 64 PER_LANE mask words (PER_LANE 16: 32768 tokens, 32:
+// 65536), PER_LANE per lane, all requested at once through a buffer
+// resource that ends at the row's last word (loads past it return 0).
 constexpr int32_t kRowClassesMaxVocab = 65536;
-__global__ __launch_bounds__(1024) void row_classes(const uint32_t* __restrict__ mask, int64_t ms, int32_t V,
-                                                    int32_t rows, uint16_t* __restrict__ flags) {
-  constexpr int kPerLane = kRowClassesMaxVocab / 32 / 64;
-  __shared__ uint32_t s_flag[16];
+template <int PER_LANE>
+__global__ __launch_bounds__(512) void row_classes(const uint32_t* __restrict__ mask, int64_t ms, int32_t V,
+                                                   int32_t rows, uint8_t* __restrict__ flags) {
+  __shared__ uint32_t s_flag[8];
   const int32_t wave = static_cast<int32_t>(threadIdx.x >> 6);
-  const int32_t r = static_cast<int32_t>(blockIdx.x) * 16 + wave;
+  const int32_t r = static_cast<int32_t>(blockIdx.x) * 8 + wave;
   const int32_t lane = static_cast<int32_t>(threadIdx.x & 63u);
   const int32_t W = (V + 31) / 32;
   // a wave past the last row reads nothing (a resource of size 0)
   const Rsrc rm = make_rsrc(r < rows ? mask + static_cast<int64_t>(r) * ms : mask,
                             r < rows ? static_cast<uint32_t>(W) * 4u : 0u);
-  uint32_t x[kPerLane];
+  uint32_t x[PER_LANE];
 #pragma unroll
-  for (int j = 0; j < kPerLane; ++j) x[j] = load_word(rm, (lane + 64 * j) * 4);
+  for (int j = 0; j < PER_LANE; ++j) x[j] = load_word(rm, (lane + 64 * j) * 4);
   const uint32_t tail = (V & 31) ? (1u << (V & 31)) - 1u : ~0u;  // bits of the last word below V
   uint32_t n = 0;
 #pragma unroll
-  for (int j = 0; j < kPerLane; ++j) n += __builtin_popcount(lane + 64 * j == W - 1 ? x[j] & tail : x[j]);
+  for (int j = 0; j < PER_LANE; ++j) n += __builtin_popcount(lane + 64 * j == W - 1 ? x[j] & tail : x[j]);
   n = lane63(wave_prefix_sum(n));
   if (lane == 0) s_flag[wave] = n > kSparseMax ? 1u : 0u;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t bits = 0;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) bits |= s_flag[w] << w;
-    flags[blockIdx.x] = static_cast<uint16_t>(bits);
+    for (int w = 0; w < 8; ++w) bits |= s_flag[w] << w;
+    flags[blockIdx.x] = static_cast<uint8_t>(bits);
   }
 }
 
 // Bytes of the flags of n rows as row_classes stores them.
-constexpr int64_t row_class_bytes(int64_t n) { return (n + 15) / 16 * 2; }
+constexpr int64_t row_class_bytes(int64_t n) { return (n + 7) / 8; }
 
 // The row block b takes when the heavy rows go first: the b-th heavy row
 // of the n, or the (b - heavy rows)-th of the others, each in row order.
