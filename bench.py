@@ -135,7 +135,9 @@ def copy_calibration():
 def sampler_calls(n):
     """N eager calls of the fused sampler per mode on the three shapes the sampler figures use.
 
-    Under rocprofv3 --pmc each call is one dispatch, in the order printed.
+    Under rocprofv3 --pmc each call is one dispatch, in the order printed, or
+    two where a large batch hands out its dense rows first (row_classes, then
+    the draw).
     """
     import numpy as np
     import torch
@@ -689,7 +691,10 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
     held in registers between them; fp32 rows take 2 -- the coarse 12-bit
     bucket pass, which also finds the maximum, and the draw that lists the
     cut's bucket).  The fp32 shape holds the bf16 shape's values widened.
-    Cold: rotating buffer sets.
+    Cold: rotating buffer sets.  Calls take the binding's default workspace,
+    so at B=1024 the modes with top-p hand out their dense rows first (a
+    classifying launch, then the draw; both are timed); those modes are
+    timed in row order too ("row_order_us_per_call", no workspace).
     """
     import numpy as np
 
@@ -721,6 +726,11 @@ def sampler_times(torch, dev, mb, workloads, stream, steps=200):
                 sets[k % nsets][0], sets[k % nsets][1], wl.vocab_size, seed=1, offset=k, out=tok, **kw),
                 steps, stream)
             res[mode] = {"us_per_call": ms * 1e3, "GBps_one_read": nbytes / (ms * 1e-3) / 1e9}
+            if mb.sample_workspace_bytes(sets[0][0].dtype, R, V) > 0 and "top_p" in kw:
+                ms0 = graph_ms(torch, lambda k, kw=kw: mb.mi_apply_bitmask_sample(
+                    sets[k % nsets][0], sets[k % nsets][1], wl.vocab_size, seed=1, offset=k, out=tok, workspace=None,
+                    **kw), steps, stream)
+                res[mode]["row_order_us_per_call"] = ms0 * 1e3
             ref_ms = torch_sort_sampler_ms(torch, sets, wl.vocab_size or wl.cols, kw, stream)
             res[mode]["torch_sort_us_per_call"] = ref_ms * 1e3
             res[mode]["speedup_vs_torch_sort"] = ref_ms / ms
