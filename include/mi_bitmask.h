@@ -240,15 +240,16 @@ mi_status_t mi_apply_bitmask_sample(
  * tokens are the same as without the workspace: the cut comes from the same
  * counts and the draw from the same Gumbel keys.
  *
- * The workspace also serves large batches: with a mask and top-p or min-p in
- * force for some row, a batch of 257 to 8192 bf16 or fp16 rows of 16385 to
- * 65536 tokens hands out its dense rows first.  One kernel marks, in one
- * bit per row, each row whose mask allows more than 4096 tokens below V;
- * the draw's blocks then take those rows first, in row order, then the
- * rest.  A dense row costs several sparse ones, and in a batch that mixes
- * them at random some compute units would otherwise get two dense rows at
- * once, or one late, and end the launch last.  The tokens do not depend on
- * the order.
+ * The workspace also serves large batches: with a mask and a filter in
+ * force for some row (top-p or min-p for rows of at most 65536 tokens, any
+ * of the three for longer ones), a batch of 257 to 8192 bf16 or fp16 rows
+ * of more than 16384 tokens hands out its dense rows first.  One kernel
+ * marks, in one bit per row, each row whose mask allows more than 4096
+ * tokens below V; the draw's blocks then take those rows first, in row
+ * order, then the rest.  A dense row costs several sparse ones, and in a
+ * batch that mixes them at random some compute units would otherwise get
+ * two dense rows at once, or one late, and end the launch last.  The
+ * tokens do not depend on the order.
  *
  * workspace: device memory of workspace_bytes bytes, 16-byte aligned, not
  * overlapping logits, mask, tokens or the per-row parameter arrays; its
@@ -299,9 +300,9 @@ mi_status_t mi_apply_bitmask_sample_noalloc(
  * Workspace bytes mi_apply_bitmask_sample_ws uses for `rows` rows of `vocab`
  * tokens (the resolved vocab size) of `dtype`: rows * 262288 (a histogram of
  * 65536 32-bit counts, a 128-byte map of its nonzero runs and 16 bytes of
- * results per row) when the batch can split its filtered rows; one bit per
- * row, rounded up to 256 bytes, when it can order its rows dense first
- * (bf16 or fp16, 257 to 8192 rows of 16385 to 65536 tokens); else 0 (no
+ * results per row) when the batch can split its filtered rows; one bit
+ * per row, rounded up to 256 bytes, when it can order its rows dense first
+ * (bf16 or fp16, 257 to 8192 rows of more than 16384 tokens); else 0 (no
  * workspace is used).  0 for invalid arguments.  Pure host arithmetic; no
  * HIP call.
  */

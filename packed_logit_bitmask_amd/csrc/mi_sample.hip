@@ -100,15 +100,14 @@ bool split_filtered_batch(mi_dtype_t dtype, int64_t rows, int64_t V) {
   return dtype != MI_DTYPE_F32 && rows >= 1 && rows <= kSplitFilteredRows && V >= 8192;
 }
 
-// Whether a batch may order its rows heavy first through the workspace: the
-// 16-bit rows of the 8-bit-counter search (more rows than kFine16Rows, at
-// most kFine8Vocab tokens), longer than a 512-thread block holds in
-// registers, so that a sparse row takes the listed search and costs far
-// less than a dense one.  (At 8192 tokens, where every row is held in
-// registers, ordering B=1024 fp16 rows cost 2.5 us more than it saved.)
+// Whether a batch may order its rows heavy first through the workspace:
+// 16-bit rows, more of them than kFine16Rows (so more than the compute
+// units hold at once), longer than a 512-thread block holds in registers,
+// so that a sparse row takes the listed search and costs far less than a
+// dense one.  (At 8192 tokens, where every row is held in registers,
+// ordering B=1024 fp16 rows cost 2.5 us more than it saved.)
 bool ordered_batch(mi_dtype_t dtype, int64_t rows, int64_t V) {
-  return dtype != MI_DTYPE_F32 && rows > kFine16Rows && rows <= kOrderMaxRows && V > 4 * 8 * 512 &&
-         V <= kFine8Vocab;
+  return dtype != MI_DTYPE_F32 && rows > kFine16Rows && rows <= kOrderMaxRows && V > 4 * 8 * 512;
 }
 
 // Workspace bytes a batch can use (0: none).
@@ -276,19 +275,27 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
       nseg = (V + seg_len - 1) / seg_len;
     }
     const bool fine8 = fine && n > kFine16Rows && V <= kFine8Vocab;
-    // heavy rows first: with top-p or min-p, whose draws over a dense row
-    // may take most of its tokens (top-k's keep few), and a mask to tell
-    // dense rows from sparse ones
+    // heavy rows first, given a mask to tell dense rows from sparse ones:
+    // rows of at most kFine8Vocab tokens (512-thread blocks, two to a unit)
+    // with top-p or min-p, whose draws over a dense row may take most of its
+    // tokens (with top-k alone the order measured 2.5 us slower); longer
+    // rows (1024-thread blocks, one to a unit) with any filter: a dense one
+    // of those costs far more than a sparse one even for top-k
     const bool may_p = ar.top_p || ar.top_p_all < 1.0f;
+    const bool long_rows = fine && !fine8 && V > kFine8Vocab;
     const uint32_t* heavy = nullptr;
-    if (use_ws && ordered_batch(dtype, rows, p.V) && fine8 && nseg == 1 && mk && (may_p || may_min_p)) {
+    if (use_ws && ordered_batch(dtype, rows, p.V) && nseg == 1 && mk &&
+        ((fine8 && (may_p || may_min_p)) || long_rows)) {
       static_assert(kOrderMaxRows <= 128 * 64, "heavy_first_row reads at most 128 rows' flags per lane");
-      static_assert(kFine8Vocab <= mi::kRowClassesMaxVocab, "row_classes reads the whole mask row");
       uint8_t* flags = static_cast<uint8_t*>(workspace);
+      // one batch of 16, 32 or 64 loads per lane, as the row needs; batches
+      // of 64 beyond 131072 tokens
       if (V <= 64 * 16 * 32)
         mi::row_classes<16><<<(n + 7) / 8, 512, 0, stream>>>(mk, mask_row_stride, V, static_cast<int32_t>(n), flags);
-      else
+      else if (V <= 64 * 32 * 32)
         mi::row_classes<32><<<(n + 7) / 8, 512, 0, stream>>>(mk, mask_row_stride, V, static_cast<int32_t>(n), flags);
+      else
+        mi::row_classes<64><<<(n + 7) / 8, 512, 0, stream>>>(mk, mask_row_stride, V, static_cast<int32_t>(n), flags);
       heavy = reinterpret_cast<const uint32_t*>(flags);
     }
     const bool deep = (n <= 256 || fine) && nseg == 1;
@@ -372,6 +379,7 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
         if (sinfo) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, true, false);
         else if (fine8 && heavy) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512, false, true);
         else if (fine8) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 512, false, false);
+        else if (deep && heavy) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024, false, true);
         else if (deep) MI_SAMPLE(mi::F16Bits, uint16_t, 128, 1024, false, false);
         else MI_SAMPLE(mi::F16Bits, uint16_t, 128, 256, false, false);
         break;
@@ -379,6 +387,7 @@ mi_status_t sample_impl(const void* logits, mi_dtype_t dtype, int64_t rows, int6
         if (sinfo) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, true, false);
         else if (fine8 && heavy) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512, false, true);
         else if (fine8) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 512, false, false);
+        else if (deep && heavy) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024, false, true);
         else if (deep) MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 1024, false, false);
         else MI_SAMPLE(mi::BF16Bits, uint16_t, 128, 256, false, false);
     }

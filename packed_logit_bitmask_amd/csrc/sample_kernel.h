@@ -1700,11 +1700,11 @@ __global__ __launch_bounds__(THREADS) void greedy_rows(const typename D::Bits* _
 
 // Bit r of the flags (32-bit words, bit r % 32 of word r / 32) = row r's
 // mask allows more than kSparseMax tokens below V.  One wave per row, 8
-// rows to a 512-thread block, which stores their 8 bits as one byte; a row
-// has at most 64 PER_LANE mask words (PER_LANE 16: 32768 tokens, 32:
-// 65536), PER_LANE per lane, all requested at once through a buffer
-// resource that ends at the row's last word (loads past it return 0).
-constexpr int32_t kRowClassesMaxVocab = 65536;
+// rows to a 512-thread block, which stores their 8 bits as one byte.  A
+// wave requests 64 PER_LANE mask words at once (PER_LANE 16: 32768 tokens,
+// 32: 65536, 64: 131072) through a buffer resource that ends at the row's
+// last word (loads past it return 0), and a longer row in further such
+// batches until its count passes kSparseMax.
 template <int PER_LANE>
 __global__ __launch_bounds__(512) void row_classes(const uint32_t* __restrict__ mask, int64_t ms, int32_t V,
                                                    int32_t rows, uint8_t* __restrict__ flags) {
@@ -1716,15 +1716,18 @@ __global__ __launch_bounds__(512) void row_classes(const uint32_t* __restrict__ 
   // a wave past the last row reads nothing (a resource of size 0)
   const Rsrc rm = make_rsrc(r < rows ? mask + static_cast<int64_t>(r) * ms : mask,
                             r < rows ? static_cast<uint32_t>(W) * 4u : 0u);
-  uint32_t x[PER_LANE];
-#pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) x[j] = load_word(rm, (lane + 64 * j) * 4);
   const uint32_t tail = (V & 31) ? (1u << (V & 31)) - 1u : ~0u;  // bits of the last word below V
-  uint32_t n = 0;
+  uint32_t total = 0;
+  for (int32_t base = 0; base < W && total <= kSparseMax; base += 64 * PER_LANE) {  // uniform in the wave
+    uint32_t x[PER_LANE];
 #pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) n += __builtin_popcount(lane + 64 * j == W - 1 ? x[j] & tail : x[j]);
-  n = lane63(wave_prefix_sum(n));
-  if (lane == 0) s_flag[wave] = n > kSparseMax ? 1u : 0u;
+    for (int j = 0; j < PER_LANE; ++j) x[j] = load_word(rm, (base + lane + 64 * j) * 4);
+    uint32_t n = 0;
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) n += __builtin_popcount(base + lane + 64 * j == W - 1 ? x[j] & tail : x[j]);
+    total += lane63(wave_prefix_sum(n));
+  }
+  if (lane == 0) s_flag[wave] = total > kSparseMax ? 1u : 0u;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t bits = 0;

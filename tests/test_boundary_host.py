@@ -337,15 +337,16 @@ def test_sample_workspace_bytes():
     assert lib.mi_sample_workspace_bytes(2, 1, 128000) == per_row
     assert lib.mi_sample_workspace_bytes(1, 32, 8192) == 32 * per_row
     assert lib.mi_sample_workspace_bytes(1, 33, 8192) == 0       # more rows than the split takes
-    # more rows than compute units, rows longer than a block holds in registers:
-    # one bit per row (rounded up to 256 bytes) orders them heavy first
+    # more rows than compute units, rows longer than a 512-thread block holds in
+    # registers: one bit per row (rounded up to 256 bytes) orders them heavy first
     assert lib.mi_sample_workspace_bytes(1, 256, 32000) == 0
     assert lib.mi_sample_workspace_bytes(1, 257, 16385) == 256
     assert lib.mi_sample_workspace_bytes(1, 1024, 16384) == 0    # rows held in registers are not ordered
     assert lib.mi_sample_workspace_bytes(2, 1024, 32000) == 256
     assert lib.mi_sample_workspace_bytes(2, 8192, 65536) == 1024
     assert lib.mi_sample_workspace_bytes(2, 8193, 65536) == 0    # beyond the ordered rows
-    assert lib.mi_sample_workspace_bytes(2, 1024, 65537) == 0    # rows of the 16-bit-counter search
+    assert lib.mi_sample_workspace_bytes(2, 1024, 65537) == 256  # rows of the 16-bit-counter search too
+    assert lib.mi_sample_workspace_bytes(1, 300, 1 << 20) == 256
     assert lib.mi_sample_workspace_bytes(0, 1024, 32000) == 0    # fp32 rows
     assert lib.mi_sample_workspace_bytes(2, 16, 8191) == 0       # rows too short to split
     assert lib.mi_sample_workspace_bytes(0, 16, 128000) == 0     # fp32 rows are not split

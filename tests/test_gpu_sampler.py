@@ -1138,7 +1138,8 @@ def mixed_density_mask(rng, R, cols, V, pad_words=0):
 
 @pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
 def test_heavy_rows_first_tokens_do_not_depend_on_the_order(dtype):
-    """Filtered batches of 257 to 8192 rows of more than 16 384 tokens,
+    """Filtered batches of 257 to 8192 rows of more than 16 384 tokens
+    (512-thread blocks up to 65 536 tokens, 1024-thread blocks beyond),
     given a workspace, hand out their dense rows first (a pass marks each
     row dense or sparse from its mask; every wave then finds its block's row
     by rank), so a row's block depends on the whole batch.  Its token must
@@ -1152,7 +1153,7 @@ def test_heavy_rows_first_tokens_do_not_depend_on_the_order(dtype):
     modes = (dict(top_p=0.9), dict(min_p=0.05, top_p=0.95), dict(top_k=50, top_p=0.9, min_p=0.05), dict(top_k=50),
              dict(top_p=0.5, temperature=0.7))
     for R, cols, V, prefixes in ((1024, 32000, None, (1000, 600, 256)), (600, 50257, 50000, (257, 200)),
-                                 (2048, 20000, 19999, (1500, 256))):
+                                 (2048, 20000, 19999, (1500, 256)), (300, 70001, 70000, (257, 256))):
         bits = random_logits(rng, dtype, R, cols, sigma=float(rng.choice([1.0, 3.0])), ties=R == 600)
         mask = mixed_density_mask(rng, R, cols, V or cols, pad_words=3 if R == 2048 else 0)
         dl = dev_logits(bits, dtype)
@@ -1199,13 +1200,19 @@ def test_heavy_rows_first_largest_batch():
 
 def test_heavy_rows_first_against_the_oracle():
     """The ordered path against the oracle directly: 300 fp16 rows of 17 000
-    tokens of mixed density, top-p with min-p, and per-row parameters."""
+    tokens of mixed density, top-p with min-p, and per-row parameters; 260
+    bf16 rows of 66 000 tokens (1024-thread blocks), top-k alone."""
     rng = np.random.default_rng(233)
     R, cols = 300, 17000
     bits = random_logits(rng, "float16", R, cols)
     mask = mixed_density_mask(rng, R, cols, cols)
     say("[gpu] heavy rows first against the oracle, top-p 0.9 min-p 0.05")
     check_rows(bits, "float16", mask, None, 1.0, 0, 0.9, 0.05, seed=3, offset=4)
+    lb = random_logits(rng, "bfloat16", 260, 66000)
+    lm = mixed_density_mask(rng, 260, 66000, 66000)
+    assert mb.sample_workspace_bytes(torch.bfloat16, 260, 66000) > 0
+    say("[gpu] heavy rows first against the oracle, 260 bf16 rows of 66000, top-k 40")
+    check_rows(lb, "bfloat16", lm, None, 1.0, 40, 1.0, 0.0, seed=6, offset=2)
     T = rng.choice([0.0, 0.7, 1.3], R).astype(np.float32)
     p = rng.choice([1.0, 0.8, 0.3], R).astype(np.float32)
     say("[gpu] heavy rows first against the oracle, per-row parameters")
